@@ -1,0 +1,81 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle checks.
+
+This module holds no pruning, compression or matmul arithmetic: it only draws
+normal samples with numpy's PCG64 generator, rounds them to fp32 and then to
+bf16 (round to nearest even on the fp32 bit pattern), and hands out raw bit
+arrays.  Both sides of every parity check read the same bytes.
+
+Workloads (feed-forward-network shapes, N(mu, sigma) entries):
+  * 2:4 fp32 weight [256 x 512] with a [512 x 128] dense operand,
+  * 2:4 bf16 up-projection weight [8192 x 2048], activations [2048 x 4096],
+  * V:N:M (V=64, M=8) bf16 down-projection weight [2048 x 8192], activations
+    [8192 x 4096],
+  * one 2:4 training step with d_model 4096, d_ff 16384, 8192 tokens,
+  * ReLU activations [8192 x 16384] ~ N(-0.5, 1) pruned V:N:M (V=128, M=8)
+    times a dense down-projection weight [16384 x 4096].
+Seeds: workload c draws tensor t from PCG64(1000*c + t), t = 0 for the sparse
+operand, 1 for the dense operand, 2 for the backward gradient.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even) and return the uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 values (exact)."""
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal(shape, seed: int, mean: float = 0.0, std: float = 1.0, dtype: str = "bf16") -> np.ndarray:
+    """N(mean, std) samples: raw uint16 bf16 bits (dtype 'bf16') or float32 ('f32')."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = (rng.standard_normal(size=shape, dtype=np.float64) * std + mean).astype(np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def small_ints(shape, seed: int, lo: int = -8, hi: int = 8, dtype: str = "bf16") -> np.ndarray:
+    """Uniform integers in [lo, hi] (exact in bf16 and fp32): raw bits or float32."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def tie_rich(shape, seed: int, dtype: str = "bf16") -> np.ndarray:
+    """Values from {-2, -1, -0.0, +0.0, 1, 2, 3}: many equal magnitudes and signed zeros."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    alphabet = np.array([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0, 3.0], np.float32)
+    x = alphabet[rng.integers(0, len(alphabet), size=shape)]
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+# name -> dict of shapes, distributions and seeds
+WORKLOADS = {
+    "nm24_fp32_256x512x128": dict(
+        kind="spmm_nm", dtype="f32", R=256, K=512, Nc=128,
+        A=dict(seed=1000, mean=0.0, std=1.0), B=dict(seed=1001, mean=0.0, std=1.0)),
+    "ffn_up_nm24_8192x2048x4096": dict(
+        kind="spmm_nm", dtype="bf16", R=8192, K=2048, Nc=4096,
+        A=dict(seed=2000, mean=0.0, std=0.02), B=dict(seed=2001, mean=0.0, std=1.0)),
+    "ffn_down_vnm64_2_8_2048x8192x4096": dict(
+        kind="spmm_venom", dtype="bf16", R=2048, K=8192, Nc=4096, V=64, M=8,
+        A=dict(seed=3000, mean=0.0, std=0.02), B=dict(seed=3001, mean=0.0, std=1.0)),
+    "train_step_nm24_dmodel4096_dff16384_tok8192": dict(
+        kind="train_step", dtype="bf16", d_model=4096, d_ff=16384, tokens=8192,
+        W=dict(seed=4000, mean=0.0, std=0.02), X=dict(seed=4001, mean=0.0, std=1.0),
+        dY=dict(seed=4002, mean=0.0, std=1.0)),
+    "relu_act_vnm128_2_8_8192x16384x4096": dict(
+        kind="act_venom", dtype="bf16", R=8192, K=16384, Nc=4096, V=128, M=8,
+        Z=dict(seed=5000, mean=-0.5, std=1.0), W=dict(seed=5001, mean=0.0, std=0.02)),
+}

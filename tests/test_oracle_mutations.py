@@ -1,0 +1,130 @@
+"""The pins are sharp: plausible mistakes planted in the oracle (on the CPU,
+through monkeypatching) make at least one pin fail."""
+
+import numpy as np
+import pytest
+
+from oracle import nm_oracle as O
+from tests import test_oracle_pins as P
+
+
+def _select_tie_high(keys, N, M):
+    R, K = keys.shape
+    g = keys.reshape(R, K // M, M)
+    rank = np.zeros(g.shape, np.int64)
+    for p in range(M):
+        for q in range(M):
+            if q != p:
+                rank[:, :, p] += g[:, :, q] > g[:, :, p]
+                if q > p:                                   # mistake: higher index wins ties
+                    rank[:, :, p] += g[:, :, q] == g[:, :, p]
+    return (rank < N).astype(np.uint8).reshape(R, K)
+
+
+def _select_no_ties(keys, N, M):
+    R, K = keys.shape
+    g = keys.reshape(R, K // M, M)
+    rank = np.zeros(g.shape, np.int64)
+    for p in range(M):
+        for q in range(M):
+            if q != p:
+                rank[:, :, p] += g[:, :, q] > g[:, :, p]   # mistake: equality term dropped
+    return (rank < N).astype(np.uint8).reshape(R, K)
+
+
+_orig_pack = O.pack_positions
+_orig_unpack = O.unpack_positions_flat
+_orig_l1 = O.venom_column_l1
+_orig_relu = O.relu_raw
+_orig_decompress = O.decompress_nm
+_orig_reprune = O.reprune_t
+_orig_prune = O.prune_nm
+
+
+def _pack_msb_first(pos, M, nbytes):
+    b = O.meta_bits(M)
+    swapped = np.zeros_like(pos)
+    for t in range(b):                                      # mistake: bits of a field reversed
+        swapped |= ((pos >> t) & 1) << (b - 1 - t)
+    return _orig_pack(swapped, M, nbytes)
+
+
+def _unpack_msb_first(meta, F, M):
+    pos = _orig_unpack(meta, F, M)
+    b = O.meta_bits(M)
+    out = np.zeros_like(pos)
+    for t in range(b):
+        out |= ((pos >> t) & 1) << (b - 1 - t)
+    return out
+
+
+def _l1_max(x, V, M):
+    R, K = x.shape
+    return np.abs(x).reshape(R // V, V, K).max(axis=1)     # mistake: max instead of sum
+
+
+def _l1_signed(x, V, M):
+    R, K = x.shape
+    return x.reshape(R // V, V, K).sum(axis=1)             # mistake: |.| dropped
+
+
+def _relu_keeps_negzero(raw, dtype):
+    x = O.decode(raw, dtype)
+    out = raw.copy()
+    out[x < 0] = 0                                          # mistake: -0.0 survives
+    return out
+
+
+def _decompress_negzero(values, meta, R, K, N, M):
+    out = _orig_decompress(values, meta, R, K, N, M)
+    fill = np.float32(-0.0) if out.dtype == np.float32 else np.uint16(0x8000)
+    pos = O.unpack_positions(meta, R, K, N, M)
+    keep = np.zeros((R, K // M, M), bool)
+    np.put_along_axis(keep, pos, True, axis=2)
+    out = out.copy()
+    out[~keep.reshape(R, K)] = fill                         # mistake: -0.0 fill
+    return out
+
+
+def _reprune_no_transpose(values, meta, R, K, dtype):
+    ws = _orig_decompress(values, meta, R, K, 2, 4)
+    vt, mt, _ = O.compress_nm(ws, _orig_prune(ws, dtype, 2, 4), 2, 4)   # mistake: no transpose
+    return vt, mt
+
+
+def _prune_signed(raw, dtype, N, M):
+    return O.nm_select(O.decode(raw, dtype), N, M)          # mistake: signed key, not magnitude
+
+
+MUTATIONS = [
+    ("nm_select", _select_tie_high, [lambda: P.test_nm_select_exhaustive_m4(2, "f32")]),
+    ("nm_select", _select_no_ties, [lambda: P.test_prune_compress_invariants(2, 4, "bf16")]),
+    ("prune_nm", _prune_signed, [lambda: P.test_golden_nm24()]),
+    ("pack_positions", _pack_msb_first, [lambda: P.test_golden_nm28_bit_stream()]),
+    ("unpack_positions_flat", _unpack_msb_first, [lambda: P.test_golden_reprune_t()]),
+    ("venom_column_l1", _l1_max, [lambda: P.test_venom_brute(2, 8)]),
+    ("venom_column_l1", _l1_signed, [lambda: P.test_venom_brute(3, 8)]),
+    ("relu_raw", _relu_keeps_negzero, [lambda: P.test_relu_venom()]),
+    ("decompress_nm", _decompress_negzero, [lambda: P.test_prune_compress_invariants(2, 4, "f32")]),
+    ("reprune_t", _reprune_no_transpose, [lambda: P.test_golden_reprune_t()]),
+]
+
+
+@pytest.mark.parametrize("name,fn,pins", MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, fn, pins):
+    monkeypatch.setattr(O, name, fn)
+    for pin in pins:
+        with pytest.raises(AssertionError):
+            pin()
+
+
+def test_spmm_transposed_operand_is_caught(monkeypatch):
+    def spmm_bt(values, meta, R, K, B_raw, dtype):
+        A = O.decode(_orig_decompress(values, meta, R, K, 2, 4), dtype)
+        B = O.decode(B_raw, dtype)
+        return A @ B[::-1]                                  # mistake: B rows reversed
+    monkeypatch.setattr(O, "spmm_nm", spmm_bt)
+    with pytest.raises(AssertionError):
+        P.test_spmm_gather_loop_equals_dgemm("f32")
+    with pytest.raises(AssertionError):
+        P.test_golden_nm24()

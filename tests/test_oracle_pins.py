@@ -1,0 +1,341 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+* brute-force enumeration with exact rationals (oracle/brute.py) over
+  tie-rich alphabets, exhaustively where the alphabet is small;
+* hand-derived examples (tests/golden/hand_examples.json);
+* invariants and special cases that reduce to a simpler rule;
+* closed forms for the products (an explicit gather loop, exact rational
+  products, B = I, linearity).
+"""
+
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import brute
+from oracle import nm_oracle as O
+from sparse_matmul_ffns_amd import synth
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")))
+
+
+def f32(a):
+    return np.array(a, np.float32)
+
+
+# ---------------------------------------------------------------------------
+# N:M selection against brute force
+# ---------------------------------------------------------------------------
+
+ALPHA7 = [-2.0, -1.0, -0.0, 0.0, 1.0, 2.0, 3.0]
+
+
+@pytest.mark.parametrize("N", [1, 2, 3])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nm_select_exhaustive_m4(N, dtype):
+    groups = np.array(list(itertools.product(ALPHA7, repeat=4)), np.float32)  # 2401 groups
+    raw = groups if dtype == "f32" else synth.f32_to_bf16_bits(groups)
+    got = O.prune_nm(raw, dtype, N, 4)
+    want = brute.nm_mask(groups.astype(np.float64), N, 4)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("N", [2, 3])
+def test_nm_select_exhaustive_m8(N):
+    groups = np.array(list(itertools.product([0.0, 1.0, 2.0], repeat=8)), np.float32)  # 6561
+    got = O.prune_nm(groups, "f32", N, 8)
+    want = brute.nm_mask(groups.astype(np.float64), N, 8)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("N,rows", [(2, 40), (4, 20), (8, 2)])
+def test_nm_select_random_m16(N, rows):
+    raw = synth.tie_rich((rows, 16 * 6), seed=7 + N, dtype="f32")
+    got = O.prune_nm(raw, "f32", N, 16)
+    want = brute.nm_mask(raw.astype(np.float64), N, 16)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# hand-derived examples
+# ---------------------------------------------------------------------------
+
+def test_golden_nm24():
+    g = GOLDEN["nm24_fp32"]
+    A = f32(g["A"])
+    mask = O.prune_nm(A, "f32", 2, 4)
+    assert mask.tolist() == g["mask"]
+    vals, meta, bad = O.compress_nm(A, mask, 2, 4)
+    assert bad == 0
+    assert vals.tobytes() == f32(g["values"]).tobytes()      # bitwise, signed zeros included
+    assert meta.tolist() == g["meta"]
+    C = O.spmm_nm(vals, meta, 2, 8, f32(g["B"]), "f32")
+    assert C.tolist() == g["C"]
+
+
+def test_golden_nm28_bit_stream():
+    g = GOLDEN["nm28_fp32"]
+    A = f32(g["A"])
+    mask = O.prune_nm(A, "f32", 2, 8)
+    assert mask.tolist() == g["mask"]
+    vals, meta, _ = O.compress_nm(A, mask, 2, 8)
+    assert vals.tolist() == g["values"]
+    assert meta.tolist() == g["meta"]
+    back = O.decompress_nm(vals, meta, 1, 16, 2, 8)
+    assert np.array_equal(back, np.where(mask == 1, A, 0))
+
+
+def test_golden_venom():
+    g = GOLDEN["vnm_v2_m8_fp32"]
+    A = f32(g["A"])
+    vals, meta, colsel, mask, _ = O.prune_venom(A, "f32", g["V"], g["M"], apply_relu=False)
+    assert colsel.tolist() == g["colsel"]
+    assert vals.tolist() == g["values"]
+    assert meta.tolist() == g["meta"]
+    assert mask.tolist() == g["mask"]
+
+
+def test_golden_reprune_t():
+    g = GOLDEN["reprune_t_fp32"]
+    Ws = f32(g["Ws_dense"])
+    mask = O.prune_nm(Ws, "f32", 2, 4)
+    vals, meta, _ = O.compress_nm(Ws, mask, 2, 4)
+    assert vals.tolist() == g["Ws_values"] and meta.tolist() == g["Ws_meta"]
+    vt, mt = O.reprune_t(vals, meta, 4, 4, "f32")
+    assert vt.tolist() == g["Wt_values"]
+    assert mt.tolist() == g["Wt_meta"]
+
+
+# ---------------------------------------------------------------------------
+# invariants of prune + compress
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,M", [(2, 4), (1, 4), (2, 8), (4, 8), (4, 16)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prune_compress_invariants(N, M, dtype):
+    raw = synth.tie_rich((24, M * 10), seed=N * 100 + M, dtype=dtype)
+    raw[:, :M] = synth.normal((24, M), seed=3, dtype=dtype)   # some untied groups too
+    x = O.decode(raw, dtype)
+    mask = O.prune_nm(raw, dtype, N, M)
+    mg = mask.reshape(24, -1, M)
+    assert np.all(mg.sum(axis=2) == N)                       # exactly N per group
+    keys = np.abs(x).reshape(24, -1, M)
+    kept_min = np.where(mg == 1, keys, np.inf).min(axis=2)
+    drop_max = np.where(mg == 0, keys, -np.inf).max(axis=2)
+    assert np.all(kept_min >= drop_max)                      # kept keys dominate
+    vals, meta, bad = O.compress_nm(raw, mask, N, M)
+    assert bad == 0
+    pos = O.unpack_positions(meta, 24, M * 10, N, M)
+    assert np.all(np.diff(pos, axis=2) > 0)                  # ascending positions
+    kept_raw = raw.reshape(24, -1, M)[mg == 1].reshape(24, -1)
+    assert kept_raw.tobytes() == vals.tobytes()              # raw bits at kept positions
+    back = O.decompress_nm(vals, meta, 24, M * 10, N, M)
+    want = np.where(mask == 1, raw, O.zeros_raw(raw.shape, dtype))
+    assert back.tobytes() == want.tobytes()                  # round trip, +0.0 fill
+
+
+def test_already_24_is_fixed_point():
+    rng = np.random.default_rng(5)
+    A = rng.standard_normal((16, 64)).astype(np.float32)
+    A = A + np.sign(A) * 0.5                                 # keep away from zero
+    sel = O.nm_select(rng.random((16, 64)), 2, 4)            # arbitrary 2:4 pattern
+    A = np.where(sel == 1, A, np.float32(0))
+    mask = O.prune_nm(A, "f32", 2, 4)
+    assert np.array_equal(mask, sel)
+    vals, meta, _ = O.compress_nm(A, mask, 2, 4)
+    assert O.decompress_nm(vals, meta, 16, 64, 2, 4).tobytes() == A.tobytes()
+
+
+def test_compress_counts_bad_groups():
+    raw = synth.normal((4, 16), seed=1, dtype="bf16")
+    mask = O.prune_nm(raw, "bf16", 2, 4)
+    mask[0, 0:4] = [1, 1, 1, 0]
+    mask[3, 12:16] = [0, 0, 0, 0]
+    vals, meta, bad = O.compress_nm(raw, mask, 2, 4)
+    assert bad == 2
+    assert np.all(vals[0, 0:2] == 0) and np.all(vals[3, 6:8] == 0)
+    pos = O.unpack_positions(meta, 4, 16, 2, 4)
+    assert pos[0, 0].tolist() == [0, 1] and pos[3, 3].tolist() == [0, 1]
+
+
+# ---------------------------------------------------------------------------
+# V:N:M against brute force and its special cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("V,M", [(1, 8), (2, 8), (3, 8), (2, 16), (4, 4)])
+def test_venom_brute(V, M):
+    raw = synth.tie_rich((V * 4, M * 5), seed=V * 31 + M, dtype="f32")
+    vals, meta, colsel, mask, _ = O.prune_venom(raw, "f32", V, M, apply_relu=False)
+    cs, mk = brute.venom_select(raw.astype(np.float64), V, M)
+    assert np.array_equal(colsel, cs)
+    assert np.array_equal(mask, mk)
+    back = O.decompress_venom(vals, meta, colsel, V * 4, M * 5, V, M)
+    assert back.tobytes() == np.where(mask == 1, raw, np.float32(0)).tobytes()
+
+
+def test_venom_m4_is_24():
+    raw = synth.normal((32, 64), seed=11, dtype="bf16")
+    vals, meta, colsel, mask, _ = O.prune_venom(raw, "bf16", 8, 4, apply_relu=False)
+    assert np.all(colsel == np.arange(4))
+    m24 = O.prune_nm(raw, "bf16", 2, 4)
+    v24, meta24, _ = O.compress_nm(raw, m24, 2, 4)
+    assert np.array_equal(mask, m24) and np.array_equal(meta, meta24) and np.array_equal(vals, v24)
+
+
+def test_venom_v1_is_row_top2_of_8():
+    raw = synth.tie_rich((16, 64), seed=12, dtype="bf16")
+    _, _, _, mask, _ = O.prune_venom(raw, "bf16", 1, 8, apply_relu=False)
+    assert np.array_equal(mask, O.prune_nm(raw, "bf16", 2, 8))
+
+
+def test_venom_colsel_shared_and_survivors_inside():
+    raw = synth.normal((64, 128), seed=13, dtype="bf16")
+    V, M = 16, 8
+    _, _, colsel, mask, _ = O.prune_venom(raw, "bf16", V, M, apply_relu=False)
+    G = 128 // M
+    for r in range(64):
+        for g in range(G):
+            kept = np.nonzero(mask[r, g * M:(g + 1) * M])[0]
+            assert len(kept) == 2 and set(kept) <= set(colsel[r // V, g].tolist())
+    assert np.all(np.diff(colsel.astype(int), axis=2) > 0)
+
+
+def test_relu_venom():
+    raw = synth.normal((32, 64), seed=14, mean=-0.5, std=1.0, dtype="bf16")
+    raw[0, :] = synth.f32_to_bf16_bits(np.full(64, -1.0, np.float32))  # a row with no positives
+    raw[1, :8] = synth.f32_to_bf16_bits(np.float32([-0.0] * 8))
+    vals, meta, colsel, mask, h = O.prune_venom(raw, "bf16", 8, 8, apply_relu=True)
+    hx = O.decode(h, "bf16")
+    assert np.all(hx >= 0) and not np.any(np.signbit(hx))   # +0.0 only, no -0.0
+    assert np.array_equal(h == 0, ~(O.decode(raw, "bf16") > 0))
+    pos = O.unpack_positions(meta, 32, 64 // 8 * 4, 2, 4)
+    assert np.all(pos[0] == [0, 1])                          # all-zero row keeps j = 0, 1
+    assert np.all(vals[0] == 0)
+    cs, mk = brute.venom_select(hx, 8, 8)
+    assert np.array_equal(cs, colsel) and np.array_equal(mk, mask)
+
+
+def test_venom_l1_is_sequential_fp64():
+    # Column sums whose fp64 value depends on the order of addition: the rows
+    # must be added top to bottom.
+    x = np.zeros((4, 8))
+    x[:, 0] = [2.0 ** 53, 1.0, 1.0, 0.0]
+    l1 = O.venom_column_l1(x, 4, 8)
+    assert l1[0, 0] == 2.0 ** 53                              # (2^53 + 1) + 1 rounds twice
+    x[:, 0] = [1.0, 1.0, 2.0 ** 53, 0.0]
+    assert O.venom_column_l1(x, 4, 8)[0, 0] == 2.0 ** 53 + 2
+
+
+# ---------------------------------------------------------------------------
+# double pruning
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_reprune_t_brute(seed):
+    R, K = 12, 16
+    raw = synth.tie_rich((R, K), seed=40 + seed, dtype="f32")
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, "f32", 2, 4), 2, 4)
+    vt, mt = O.reprune_t(vals, meta, R, K, "f32")
+    ws = np.where(brute.nm_mask(raw.astype(np.float64), 2, 4) == 1, raw, np.float32(0))
+    mt_want = brute.nm_mask(ws.T.astype(np.float64), 2, 4)
+    back = O.decompress_nm(vt, mt, K, R, 2, 4)
+    assert back.tobytes() == np.where(mt_want == 1, ws.T, np.float32(0)).tobytes()
+
+
+def test_reprune_t_idempotent_on_checkerboard():
+    # 2x2 blocks in a checkerboard are 2:4 along rows and along columns.
+    i, j = np.indices((16, 16))
+    pat = (((i // 2) + (j // 2)) % 2 == 0).astype(np.float64)
+    rng = np.random.default_rng(3)
+    mag = rng.integers(1, 9, pat.shape) * rng.choice([-1, 1], pat.shape)
+    A = np.where(pat == 1, mag, 0.0).astype(np.float32)        # +0.0 off the pattern
+    vals, meta, _ = O.compress_nm(A, O.prune_nm(A, "f32", 2, 4), 2, 4)
+    assert O.decompress_nm(vals, meta, 16, 16, 2, 4).tobytes() == A.tobytes()
+    vt, mt = O.reprune_t(vals, meta, 16, 16, "f32")
+    assert O.decompress_nm(vt, mt, 16, 16, 2, 4).tobytes() == np.ascontiguousarray(A.T).tobytes()
+
+
+# ---------------------------------------------------------------------------
+# products: closed forms
+# ---------------------------------------------------------------------------
+
+def _compressed(R, K, seed, dtype, ints=False):
+    raw = synth.small_ints((R, K), seed, dtype=dtype) if ints else synth.normal((R, K), seed, dtype=dtype)
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, dtype, 2, 4), 2, 4)
+    return raw, vals, meta
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_spmm_gather_loop_equals_dgemm(dtype):
+    R, K, Nc = 6, 24, 5
+    _, vals, meta = _compressed(R, K, 50, dtype)
+    B = synth.normal((K, Nc), 51, dtype=dtype)
+    a = O.spmm_nm(vals, meta, R, K, B, dtype)
+    b = O.spmm_nm_loop(vals, meta, R, K, B, dtype)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+def test_spmm_exact_rational():
+    R, K, Nc = 5, 16, 4
+    _, vals, meta = _compressed(R, K, 52, "f32")
+    B = synth.normal((K, Nc), 53, dtype="f32")
+    A64 = O.decode(O.decompress_nm(vals, meta, R, K, 2, 4), "f32")
+    exact = brute.dense_product(A64, B.astype(np.float64))
+    assert np.allclose(O.spmm_nm(vals, meta, R, K, B, "f32"), exact, rtol=1e-14, atol=1e-14)
+
+
+def test_spmm_identity_and_linearity():
+    R, K = 8, 32
+    raw, vals, meta = _compressed(R, K, 54, "bf16", ints=True)
+    eye = synth.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    C = O.spmm_nm(vals, meta, R, K, eye, "bf16")
+    assert np.array_equal(C, O.decode(O.decompress_nm(vals, meta, R, K, 2, 4), "bf16"))
+    B1 = synth.small_ints((K, 3), 55, dtype="bf16")
+    B2 = synth.small_ints((K, 3), 56, dtype="bf16")
+    Bs = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(B1) + synth.bf16_bits_to_f32(B2))
+    assert np.array_equal(O.spmm_nm(vals, meta, R, K, Bs, "bf16"),
+                          O.spmm_nm(vals, meta, R, K, B1, "bf16") + O.spmm_nm(vals, meta, R, K, B2, "bf16"))
+
+
+def test_spmm_venom_gather_loop_equals_dgemm():
+    R, K, V, M, Nc = 8, 32, 4, 8, 5
+    raw = synth.normal((R, K), 60, dtype="bf16")
+    vals, meta, colsel, _, _ = O.prune_venom(raw, "bf16", V, M, apply_relu=False)
+    B = synth.normal((K, Nc), 61, dtype="bf16")
+    a = O.spmm_venom(vals, meta, colsel, R, K, V, M, B, "bf16")
+    b = O.spmm_venom_loop(vals, meta, colsel, R, K, V, M, B, "bf16")
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+def test_sddmm_exact_rational():
+    R, Kc, T = 4, 8, 6
+    D = synth.small_ints((R, T), 70, dtype="bf16")
+    X = synth.small_ints((Kc, T), 71, dtype="bf16")
+    W = synth.normal((R, Kc), 72, dtype="bf16")
+    _, meta, _ = O.compress_nm(W, O.prune_nm(W, "bf16", 2, 4), 2, 4)
+    got = O.sddmm_nm(D, X, meta, R, Kc, "bf16")
+    full = brute.dense_product(O.decode(D, "bf16"), O.decode(X, "bf16").T)
+    pos = O.unpack_positions(meta, R, Kc, 2, 4)
+    for r in range(R):
+        for g in range(Kc // 4):
+            for s in range(2):
+                assert got[r, 2 * g + s] == full[r, 4 * g + pos[r, g, s]]
+    rows = np.array([3, 1])
+    assert np.array_equal(O.sddmm_nm_rows(D, X, meta, rows, Kc, "bf16"), got[rows])
+
+
+def test_tolerance_check():
+    ref = np.array([[1.0, -2.0]])
+    bound = np.array([[1.0, 2.0]])
+    assert O.within_tolerance(ref + 1e-4, ref, bound)[0]
+    assert not O.within_tolerance(ref + np.array([[0.0, 0.05]]), ref, bound)[0]
+
+
+def test_decode_bf16():
+    bits = np.array([0x3F80, 0xBF80, 0x8000, 0x0000, 0x4049, 0x0001], np.uint16)
+    got = O.decode(bits, "bf16")
+    assert got[:4].tolist() == [1.0, -1.0, 0.0, 0.0] and np.signbit(got[2])
+    assert got[4] == 3.140625 and got[5] == 2.0 ** -133
