@@ -1,0 +1,198 @@
+/*
+ * nmsparse.h -- C ABI of the MI355X (gfx950) library for semi-structured
+ * sparse feed-forward matmuls: magnitude N:M and V:N:M pruning, compression
+ * to values plus packed position metadata, and the sparse x dense products of
+ * the FFN forward pass and of the double-pruned backward pass.
+ *
+ * Sources (page title, section):
+ *   "Success story: ESPLAG" (inno4scale) -- Highlights, Research Topic,
+ *       Solution: semi-structured N:M magnitude pruning, a compressed storage
+ *       format (VENOM) and an SpMM kernel library; figures 1-3 (the formats)
+ *       are missing from the page.
+ *   "To 2:4 Sparsity and Beyond: Neuron-level Activation Function to
+ *       Accelerate LLM Pre-Training" -- abstract: 2:4 weights and v:n:m
+ *       (Venom) activations in every FFN matmul.
+ *   NSF PAR award 2340011 listing -- SLOPE abstract: the backward pass uses
+ *       the transposed weight re-pruned with N:M ("double pruned").
+ *   "Sparser, Faster, Lighter Transformer Language Models" -- Methodologie:
+ *       ReLU activations, the FFN as the dominant cost.
+ *
+ * Conventions shared by every call
+ *   - Matrices are row-major.  Leading dimensions (lda, ldb, ...) count
+ *     elements, not bytes, and must be >= the row width.
+ *   - Groups are M consecutive elements along the reduction dimension K of the
+ *     left (sparse) operand, starting at column 0.  K must be a multiple of M.
+ *   - Selection keeps the N largest magnitudes of a group; on equal magnitude
+ *     the lower position wins.  A group always keeps exactly N elements, zeros
+ *     included.  +0.0 and -0.0 have equal magnitude.
+ *   - Compressed form of an R x K matrix, N:M:
+ *       values [R][(K/M)*N]  kept elements in ascending position, raw bits of
+ *                            the input dtype (signed zeros preserved);
+ *       meta   [R][ceil((K/M)*N*b/8)] bytes, b = ceil(log2 M): per row one
+ *                            LSB-first bit stream of b-bit positions, survivor
+ *                            s of group g at bit (g*N + s)*b.  For 2:4 this is
+ *                            one nibble p0 | p1 << 2 per group, even groups in
+ *                            the low nibble (ceil(K/8) bytes per row).
+ *   - V:N:M form (N = 2): per V-row block and M-column group the 4 columns with
+ *     the largest block L1 norm (fp64, rows summed top to bottom) are kept,
+ *     then 2 of those 4 per row by magnitude:
+ *       colsel [R/V][K/M][4] u8  the 4 kept columns of each group, ascending;
+ *       values [R][(K/M)*2]       kept elements;
+ *       meta   [R][ceil(K/M/2)]   2:4 nibbles j0 | j1 << 2 over j = 0..3,
+ *                                 j indexing the group's colsel entries.
+ *   - Device pointers: every array argument is device memory owned by the
+ *     caller, naturally aligned for its element type.  Outputs are fully
+ *     overwritten and must not overlap inputs.  The library allocates nothing
+ *     and keeps no state: calls are reentrant and thread-safe.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Every call
+ *     is asynchronous on that stream; argument errors are returned before
+ *     anything is launched.
+ *   - Floating point: products accumulate in fp32 and are written as fp32.
+ *   - Errors: NM_ERR_NULL for a NULL required pointer, NM_ERR_SHAPE for
+ *     non-positive sizes, sizes that are not multiples of the group/block, or
+ *     a leading dimension below the row width, NM_ERR_UNSUPPORTED for a dtype
+ *     or (N, M, V) the call does not implement, NM_ERR_ALIGN for a pointer
+ *     that is not aligned to its element size, NM_ERR_HIP when the launch
+ *     fails (nm_last_hip_error() names the HIP error).
+ */
+#ifndef NMSPARSE_H
+#define NMSPARSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NM_OK = 0,
+  NM_ERR_NULL = 1,
+  NM_ERR_SHAPE = 2,
+  NM_ERR_UNSUPPORTED = 3,
+  NM_ERR_ALIGN = 4,
+  NM_ERR_HIP = 5
+} nm_status;
+
+typedef enum { NM_F32 = 0, NM_BF16 = 1 } nm_dtype;
+
+/* A hipStream_t, passed as an opaque pointer (NULL = the null stream). */
+typedef void* nm_stream;
+
+/*
+ * nm_prune -- magnitude N:M pruning along K ("Success story: ESPLAG",
+ * Highlights and Solution; "To 2:4 Sparsity and Beyond", abstract).
+ *   A     [R][lda]    fp32 or bf16 input (dt)
+ *   mask  [R][ldmask] u8 output: 1 where kept, 0 elsewhere (columns 0..K-1)
+ * N:M: M in {4, 8, 16}, 1 <= N < M.
+ */
+nm_status nm_prune(nm_dtype dt, const void* A, int64_t lda, int64_t R, int64_t K, int N, int M,
+                   uint8_t* mask, int64_t ldmask, nm_stream stream);
+
+/*
+ * nm_compress -- gather the kept elements of each group in ascending position
+ * and pack their positions ("Success story: ESPLAG", Solution: compressed
+ * storage format).
+ *   A          [R][lda] input; mask [R][ldmask] u8 (nonzero = kept)
+ *   values     [R][(K/M)*N] output, dtype dt
+ *   meta       [R][ceil((K/M)*N*b/8)] u8 output
+ *   bad_groups nullable device int32: incremented (never reset) by the number
+ *              of groups whose mask keeps a count other than N.  Such a group
+ *              is stored as +0.0 values at positions 0..N-1.
+ */
+nm_status nm_compress(nm_dtype dt, const void* A, int64_t lda, const uint8_t* mask, int64_t ldmask,
+                      int64_t R, int64_t K, int N, int M, void* values, uint8_t* meta,
+                      int32_t* bad_groups, nm_stream stream);
+
+/*
+ * nm_decompress -- inverse of nm_compress: dense A_out [R][lda] with +0.0 at
+ * every position that is not kept.
+ */
+nm_status nm_decompress(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                        int N, int M, void* A_out, int64_t lda, nm_stream stream);
+
+/*
+ * spmm_nm -- C = decompress(values, meta) * B for a 2:4 left operand
+ * ("Success story: ESPLAG", Research Topic: the SpMM; "To 2:4 Sparsity and
+ * Beyond", abstract: 2:4 weights in every FFN matmul).
+ *   values [R][K/2], meta [R][ceil(K/8)] (2:4 form of an R x K matrix), dtype dt
+ *   B      [K][ldb] dense, dtype dt
+ *   C      [R][ldc] fp32 output, C[r][n] for n < Nc
+ * K must be a multiple of 4.
+ */
+nm_status spmm_nm(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                  const void* B, int64_t ldb, int64_t Nc, float* C, int64_t ldc, nm_stream stream);
+
+/*
+ * prune_act_venom -- V:N:M prune (N = 2) and compress in one pass, optionally
+ * after ReLU ("To 2:4 Sparsity and Beyond", abstract: v:n:m activations;
+ * "Sparser, Faster, Lighter Transformer Language Models", Methodologie: ReLU;
+ * "Success story: ESPLAG", Solution: VENOM format).
+ *   Z       [R][ldz] input, dtype dt
+ *   apply_relu  nonzero: select on h = ReLU(Z) (every z <= 0, and -0.0,
+ *               becomes +0.0) and store h's values
+ *   values  [R][(K/M)*2], meta [R][ceil(K/M/2)], colsel [R/V][K/M][4] outputs
+ *   mask    nullable [R][ldmask] u8 output: 1 at the 2 kept columns per group
+ * M in {4, 8, 16}; 1 <= V <= 256; R % V == 0; K % M == 0.
+ */
+nm_status prune_act_venom(nm_dtype dt, const void* Z, int64_t ldz, int64_t R, int64_t K, int V,
+                          int M, int apply_relu, void* values, uint8_t* meta, uint8_t* colsel,
+                          uint8_t* mask, int64_t ldmask, nm_stream stream);
+
+/*
+ * spmm_venom -- C = decompress_venom(values, meta, colsel) * B:
+ * C[r][n] = sum_g sum_s values[r][2g+s] * B[g*M + colsel[r/V][g][j_s]][n]
+ * ("To 2:4 Sparsity and Beyond", abstract; "Success story: ESPLAG",
+ * Solution: VENOM format and its SpMM).
+ *   B [K][ldb] dense, dtype dt; C [R][ldc] fp32 output.
+ * M in {4, 8, 16}; 1 <= V <= 256; R % V == 0; K % M == 0.
+ */
+nm_status spmm_venom(nm_dtype dt, const void* values, const uint8_t* meta, const uint8_t* colsel,
+                     int64_t R, int64_t K, int V, int M, const void* B, int64_t ldb, int64_t Nc,
+                     float* C, int64_t ldc, nm_stream stream);
+
+/*
+ * nm_reprune_t -- double pruning (NSF PAR award 2340011, SLOPE abstract): the
+ * 2:4-compressed W_s [R x K] is decompressed with +0.0 fill, transposed to
+ * [K x R], pruned 2:4 by magnitude along R and compressed.
+ *   values [R][K/2], meta [R][ceil(K/8)]      input (2:4 along K)
+ *   values_t [K][R/2], meta_t [K][ceil(R/8)]  output (2:4 along R)
+ * R and K must be multiples of 4.
+ */
+nm_status nm_reprune_t(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                       void* values_t, uint8_t* meta_t, nm_stream stream);
+
+/*
+ * sddmm_nm -- the weight gradient of a 2:4 layer, sampled at the weight's
+ * survivors ("Success story: ESPLAG", Research Topic: kernels for the full
+ * sparse training step):
+ *   values_out[r][2g+s] = sum_t D[r][t] * X[4g + p_s(r, g)][t]
+ * with p_s from meta (the 2:4 metadata of the R x Kc weight).
+ *   D [R][ldd] (the output gradient), X [Kc][ldx] (the layer input, one row
+ *   per input feature), dtype dt; values_out [R][Kc/2] fp32.
+ * Kc must be a multiple of 4.
+ */
+nm_status sddmm_nm(nm_dtype dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R,
+                   int64_t Kc, int64_t T, const uint8_t* meta, float* values_out, nm_stream stream);
+
+/*
+ * nm_sizes -- host-only helper: element count of values, bytes of meta and of
+ * colsel for an R x K matrix in N:M form (V > 0: V:N:M form with N = 2, where
+ * N is ignored).  NULL outputs are skipped.
+ */
+void nm_sizes(int64_t R, int64_t K, int N, int M, int V, int64_t* n_values, int64_t* meta_bytes,
+              int64_t* colsel_bytes);
+
+/* Static description of a status code. */
+const char* nm_status_str(nm_status status);
+
+/* The HIP error string behind the last NM_ERR_HIP on this thread ("" if none). */
+const char* nm_last_hip_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int nm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NMSPARSE_H */

@@ -1,0 +1,21 @@
+"""MI355X (gfx950) semi-structured sparse FFN matmuls: N:M and V:N:M pruning,
+compression and sparse x dense products behind the libnmsparse C ABI.
+
+The binding functions live in `sparse_matmul_ffns_amd.nmsparse`; the library
+is loaded on first use and must have been built with
+`python -m sparse_matmul_ffns_amd.build`.
+"""
+
+from .nmsparse import (  # noqa: F401
+    NmError,
+    lib,
+    nm_compress,
+    nm_decompress,
+    nm_prune,
+    nm_reprune_t,
+    prune_act_venom,
+    sddmm_nm,
+    sizes,
+    spmm_nm,
+    spmm_venom,
+)

@@ -1,0 +1,143 @@
+// C ABI of libnmsparse: argument validation and dispatch to the gfx950 kernels.
+// Every check runs on the host before anything is launched; a call that
+// returns an error has touched no device memory.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/nmsparse.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+nm_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return NM_OK;
+  const char* s = hipGetErrorString(e);
+  strncpy(g_last_hip_error, s ? s : "unknown HIP error", sizeof(g_last_hip_error) - 1);
+  g_last_hip_error[sizeof(g_last_hip_error) - 1] = '\0';
+  return NM_ERR_HIP;
+}
+
+bool dtype_ok(nm_dtype dt) { return dt == NM_F32 || dt == NM_BF16; }
+int esize(nm_dtype dt) { return dt == NM_BF16 ? 2 : 4; }
+bool aligned(const void* p, int a) { return ((uintptr_t)p % (uintptr_t)a) == 0; }
+bool m_ok(int M) { return M == 4 || M == 8 || M == 16; }
+bool nm_ok(int N, int M) { return m_ok(M) && N >= 1 && N < M; }
+bool v_ok(int V) { return V >= 1 && V <= 256; }
+hipStream_t hs(nm_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+nm_status nm_prune(nm_dtype dt, const void* A, int64_t lda, int64_t R, int64_t K, int N, int M, uint8_t* mask,
+                   int64_t ldmask, nm_stream stream) {
+  if (!A || !mask) return NM_ERR_NULL;
+  if (!dtype_ok(dt) || !nm_ok(N, M)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || K % M != 0 || lda < K || ldmask < K) return NM_ERR_SHAPE;
+  if (!aligned(A, esize(dt))) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_nm_prune(dt, A, lda, R, K, N, M, mask, ldmask, hs(stream)));
+}
+
+nm_status nm_compress(nm_dtype dt, const void* A, int64_t lda, const uint8_t* mask, int64_t ldmask, int64_t R,
+                      int64_t K, int N, int M, void* values, uint8_t* meta, int32_t* bad_groups,
+                      nm_stream stream) {
+  if (!A || !mask || !values || !meta) return NM_ERR_NULL;
+  if (!dtype_ok(dt) || !nm_ok(N, M)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || K % M != 0 || lda < K || ldmask < K) return NM_ERR_SHAPE;
+  if (!aligned(A, esize(dt)) || !aligned(values, esize(dt)) || !aligned(bad_groups, 4)) return NM_ERR_ALIGN;
+  return hip_status(
+      nms::launch_nm_compress(dt, A, lda, mask, ldmask, R, K, N, M, values, meta, bad_groups, hs(stream)));
+}
+
+nm_status nm_decompress(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, int N, int M,
+                        void* A_out, int64_t lda, nm_stream stream) {
+  if (!values || !meta || !A_out) return NM_ERR_NULL;
+  if (!dtype_ok(dt) || !nm_ok(N, M)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || K % M != 0 || lda < K) return NM_ERR_SHAPE;
+  if (!aligned(values, esize(dt)) || !aligned(A_out, esize(dt))) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_nm_decompress(dt, values, meta, R, K, N, M, A_out, lda, hs(stream)));
+}
+
+nm_status spmm_nm(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* B,
+                  int64_t ldb, int64_t Nc, float* C, int64_t ldc, nm_stream stream) {
+  if (!values || !meta || !B || !C) return NM_ERR_NULL;
+  if (!dtype_ok(dt)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || Nc <= 0 || K % 4 != 0 || ldb < Nc || ldc < Nc) return NM_ERR_SHAPE;
+  if (!aligned(values, esize(dt)) || !aligned(B, esize(dt)) || !aligned(C, 4)) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_spmm_nm(dt, values, meta, R, K, B, ldb, Nc, C, ldc, hs(stream)));
+}
+
+nm_status prune_act_venom(nm_dtype dt, const void* Z, int64_t ldz, int64_t R, int64_t K, int V, int M,
+                          int apply_relu, void* values, uint8_t* meta, uint8_t* colsel, uint8_t* mask,
+                          int64_t ldmask, nm_stream stream) {
+  if (!Z || !values || !meta || !colsel) return NM_ERR_NULL;
+  if (!dtype_ok(dt) || !m_ok(M) || !v_ok(V)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || R % V != 0 || K % M != 0 || ldz < K || (mask && ldmask < K)) return NM_ERR_SHAPE;
+  if (!aligned(Z, esize(dt)) || !aligned(values, esize(dt))) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_prune_act_venom(dt, Z, ldz, R, K, V, M, apply_relu != 0, values, meta, colsel,
+                                                mask, ldmask, hs(stream)));
+}
+
+nm_status spmm_venom(nm_dtype dt, const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R,
+                     int64_t K, int V, int M, const void* B, int64_t ldb, int64_t Nc, float* C, int64_t ldc,
+                     nm_stream stream) {
+  if (!values || !meta || !colsel || !B || !C) return NM_ERR_NULL;
+  if (!dtype_ok(dt) || !m_ok(M) || !v_ok(V)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || Nc <= 0 || R % V != 0 || K % M != 0 || ldb < Nc || ldc < Nc) return NM_ERR_SHAPE;
+  if (!aligned(values, esize(dt)) || !aligned(B, esize(dt)) || !aligned(C, 4)) return NM_ERR_ALIGN;
+  return hip_status(
+      nms::launch_spmm_venom(dt, values, meta, colsel, R, K, V, M, B, ldb, Nc, C, ldc, hs(stream)));
+}
+
+nm_status nm_reprune_t(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, void* values_t,
+                       uint8_t* meta_t, nm_stream stream) {
+  if (!values || !meta || !values_t || !meta_t) return NM_ERR_NULL;
+  if (!dtype_ok(dt)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || R % 4 != 0 || K % 4 != 0) return NM_ERR_SHAPE;
+  if (!aligned(values, esize(dt)) || !aligned(values_t, esize(dt))) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_nm_reprune_t(dt, values, meta, R, K, values_t, meta_t, hs(stream)));
+}
+
+nm_status sddmm_nm(nm_dtype dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
+                   int64_t T, const uint8_t* meta, float* values_out, nm_stream stream) {
+  if (!D || !X || !meta || !values_out) return NM_ERR_NULL;
+  if (!dtype_ok(dt)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || Kc <= 0 || T <= 0 || Kc % 4 != 0 || ldd < T || ldx < T) return NM_ERR_SHAPE;
+  if (!aligned(D, esize(dt)) || !aligned(X, esize(dt)) || !aligned(values_out, 4)) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_sddmm_nm(dt, D, ldd, X, ldx, R, Kc, T, meta, values_out, hs(stream)));
+}
+
+void nm_sizes(int64_t R, int64_t K, int N, int M, int V, int64_t* n_values, int64_t* meta_bytes,
+              int64_t* colsel_bytes) {
+  if (M <= 0) M = 4;
+  const int64_t G = K / M;
+  if (V > 0) {
+    if (n_values) *n_values = R * G * 2;
+    if (meta_bytes) *meta_bytes = R * ((G + 1) / 2);
+    if (colsel_bytes) *colsel_bytes = (R / V) * G * 4;
+  } else {
+    if (n_values) *n_values = R * G * N;
+    if (meta_bytes) *meta_bytes = R * nms::meta_row_bytes(K, N, M);
+    if (colsel_bytes) *colsel_bytes = 0;
+  }
+}
+
+const char* nm_status_str(nm_status status) {
+  switch (status) {
+    case NM_OK: return "ok";
+    case NM_ERR_NULL: return "a required pointer is NULL";
+    case NM_ERR_SHAPE: return "invalid shape or leading dimension";
+    case NM_ERR_UNSUPPORTED: return "unsupported dtype, N:M pattern or block size";
+    case NM_ERR_ALIGN: return "pointer not aligned to its element size";
+    case NM_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* nm_last_hip_error(void) { return g_last_hip_error; }
+
+int nm_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Host-side launchers of the gfx950 kernels (internal to libnmsparse).
+// Arguments are validated by api.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nms {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+inline int64_t meta_row_bytes(int64_t K, int N, int M) {
+  int b = 1;
+  while ((1 << b) < M) ++b;
+  return ((K / M) * N * b + 7) / 8;
+}
+
+hipError_t launch_nm_prune(int dt, const void* A, int64_t lda, int64_t R, int64_t K, int N, int M,
+                           uint8_t* mask, int64_t ldmask, hipStream_t s);
+hipError_t launch_nm_compress(int dt, const void* A, int64_t lda, const uint8_t* mask, int64_t ldmask,
+                              int64_t R, int64_t K, int N, int M, void* values, uint8_t* meta, int32_t* bad,
+                              hipStream_t s);
+hipError_t launch_nm_decompress(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, int N,
+                                int M, void* out, int64_t lda, hipStream_t s);
+hipError_t launch_prune_act_venom(int dt, const void* Z, int64_t ldz, int64_t R, int64_t K, int V, int M,
+                                  int relu, void* values, uint8_t* meta, uint8_t* colsel, uint8_t* mask,
+                                  int64_t ldmask, hipStream_t s);
+hipError_t launch_nm_reprune_t(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                               void* values_t, uint8_t* meta_t, hipStream_t s);
+hipError_t launch_spmm_nm(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* B,
+                          int64_t ldb, int64_t Nc, float* C, int64_t ldc, hipStream_t s);
+hipError_t launch_spmm_venom(int dt, const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R,
+                             int64_t K, int V, int M, const void* B, int64_t ldb, int64_t Nc, float* C,
+                             int64_t ldc, hipStream_t s);
+hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R,
+                           int64_t Kc, int64_t T, const uint8_t* meta, float* out, hipStream_t s);
+
+}  // namespace nms

@@ -1,0 +1,142 @@
+// Double pruning of the transposed weight (gfx950).
+//
+// The SLOPE abstract (NSF PAR award 2340011) runs the backward pass on the
+// transposed weight re-pruned with N:M.  Here the already 2:4-pruned weight
+// W_s [R x K] (compressed along K) is decompressed with +0.0 fill, transposed
+// and pruned 2:4 along R, giving W_ds^T [K x R] compressed along R.
+//
+// One workgroup owns a 128-row x 64-column tile of W_s:
+//   1. each lane decompresses 4 groups (16 columns of one row) into LDS;
+//   2. each lane takes 16 consecutive rows of one column (4 output groups),
+//      keeps 2 of every 4 by magnitude (lower row on ties) and writes 8 values
+//      and 2 bytes of nibbles; the 8 lanes of one column write 128 contiguous
+//      bytes of the output row.
+// HBM traffic is one read of W_s's values and metadata and one write of the
+// result, the bound of this pass.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nms {
+
+constexpr int RP_ROWS = 128;  // rows of W_s per tile
+constexpr int RP_COLS = 64;   // columns of W_s per tile
+constexpr int RP_PITCH = RP_COLS + 2;
+
+template <typename T>
+__global__ __launch_bounds__(256) void reprune_t_kernel(const T* __restrict__ values, const uint8_t* __restrict__ meta,
+                                                        int64_t R, int64_t K, T* __restrict__ values_t,
+                                                        uint8_t* __restrict__ meta_t, int vec_in, int vec_out) {
+  __shared__ T tile[RP_ROWS * RP_PITCH];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * RP_ROWS;
+  const int64_t k0 = (int64_t)blockIdx.y * RP_COLS;
+  const int64_t kvalid = (K - k0) < RP_COLS ? (K - k0) : RP_COLS;   // multiple of 4
+  const int64_t rvalid = (R - r0) < RP_ROWS ? (R - r0) : RP_ROWS;   // multiple of 4
+
+  // 1. decompress: unit = (row, quad of 4 groups); 128 rows x 4 quads
+  for (int u = tid; u < RP_ROWS * 4; u += 256) {
+    const int r = u >> 2, q = u & 3;
+    const int c = q * 16;
+    T dense[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dense[e] = (T)0;
+    if (r < rvalid && c < kvalid) {
+      const int64_t row = r0 + r;
+      const T* v = values + row * (K / 2) + (k0 + c) / 2;
+      const uint8_t* m = meta + row * ((K + 7) / 8) + (k0 + c) / 8;
+      const int ng = (int)((kvalid - c) < 16 ? (kvalid - c) : 16) / 4;
+      T vv[8];
+      uint32_t nibs = 0;
+      if (vec_in && ng == 4) {
+        if constexpr (sizeof(T) == 2) {
+          u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v));
+          __builtin_memcpy(vv, &t, 16);
+        } else {
+          u32x4 t0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v));
+          u32x4 t1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v) + 1);
+          __builtin_memcpy(vv, &t0, 16);
+          __builtin_memcpy(vv + 4, &t1, 16);
+        }
+        nibs = (uint32_t)m[0] | ((uint32_t)m[1] << 8);
+      } else {
+        // groups of this unit start at column k0 + c; the first one may sit in
+        // the high nibble when (k0 + c) / 4 is odd (never here: c and k0 are
+        // multiples of 16)
+        for (int g = 0; g < ng; ++g) {
+          vv[2 * g] = v[2 * g];
+          vv[2 * g + 1] = v[2 * g + 1];
+          nibs |= (uint32_t)((m[g >> 1] >> (4 * (g & 1))) & 0xF) << (4 * g);
+        }
+      }
+      for (int g = 0; g < ng; ++g) {
+        const uint32_t nib = (nibs >> (4 * g)) & 0xF;
+        dense[4 * g + (nib & 3)] = vv[2 * g];
+        dense[4 * g + ((nib >> 2) & 3)] = vv[2 * g + 1];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tile[r * RP_PITCH + c + e] = dense[e];
+  }
+  __syncthreads();
+
+  // 2. re-prune along rows: unit = (column, 16-row chunk); chunk index fastest
+  for (int u = tid; u < RP_COLS * 8; u += 256) {
+    const int col = u >> 3, ch = u & 7;
+    const int rr = ch * 16;
+    if (col >= kvalid || rr >= rvalid) continue;
+    const int ng = (int)((rvalid - rr) < 16 ? (rvalid - rr) : 16) / 4;
+    T out[8];
+    uint32_t nibs = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      T x[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) x[p] = tile[(rr + 4 * g + p) * RP_PITCH + col];
+      const uint32_t nib = select24(Elem<T>::key(x[0]), Elem<T>::key(x[1]), Elem<T>::key(x[2]), Elem<T>::key(x[3]));
+      out[2 * g] = x[nib & 3];
+      out[2 * g + 1] = x[(nib >> 2) & 3];
+      nibs |= nib << (4 * g);
+    }
+    const int64_t orow = k0 + col;
+    T* vd = values_t + orow * (R / 2) + (r0 + rr) / 2;
+    uint8_t* md = meta_t + orow * ((R + 7) / 8) + (r0 + rr) / 8;
+    if (vec_out && ng == 4) {
+      if constexpr (sizeof(T) == 2) {
+        u32x4 t; __builtin_memcpy(&t, out, 16); *reinterpret_cast<u32x4*>(vd) = t;
+      } else {
+        u32x4 t0, t1; __builtin_memcpy(&t0, out, 16); __builtin_memcpy(&t1, out + 4, 16);
+        reinterpret_cast<u32x4*>(vd)[0] = t0; reinterpret_cast<u32x4*>(vd)[1] = t1;
+      }
+      md[0] = (uint8_t)(nibs & 0xFF);
+      md[1] = (uint8_t)(nibs >> 8);
+    } else {
+      for (int e = 0; e < 2 * ng; ++e) vd[e] = out[e];
+      // (r0 + rr) / 4 is even, so group g of this unit is nibble g of md
+      for (int g = 0; g < ng; g += 2) {
+        const uint32_t lo = (nibs >> (4 * g)) & 0xF;
+        const uint32_t hi = (g + 1 < ng) ? ((nibs >> (4 * (g + 1))) & 0xF) : 0u;
+        md[g >> 1] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}
+
+template <typename T>
+static hipError_t reprune_dispatch(const void* values, const uint8_t* meta, int64_t R, int64_t K, void* values_t,
+                                   uint8_t* meta_t, hipStream_t s) {
+  const int esz = sizeof(T);
+  const int vec_in = ((uintptr_t)values % 16 == 0) && (((K / 2) * esz) % 16 == 0);
+  const int vec_out = ((uintptr_t)values_t % 16 == 0) && (((R / 2) * esz) % 16 == 0);
+  dim3 grid((unsigned)((R + RP_ROWS - 1) / RP_ROWS), (unsigned)((K + RP_COLS - 1) / RP_COLS));
+  hipLaunchKernelGGL(reprune_t_kernel<T>, grid, dim3(256), 0, s, (const T*)values, meta, R, K, (T*)values_t, meta_t,
+                     vec_in, vec_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_nm_reprune_t(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                               void* values_t, uint8_t* meta_t, hipStream_t s) {
+  return dt == DT_BF16 ? reprune_dispatch<uint16_t>(values, meta, R, K, values_t, meta_t, s)
+                       : reprune_dispatch<uint32_t>(values, meta, R, K, values_t, meta_t, s);
+}
+
+}  // namespace nms

@@ -1,0 +1,245 @@
+// Weight gradient of a 2:4 layer sampled at the weight's survivors (gfx950).
+//
+// "Success story: ESPLAG" (Research Topic) needed kernels beyond the SpMM for
+// the complete sparse training step.  For Y = W_s X the weight gradient is
+// dY X^T, and only the entries W_s keeps are needed:
+//   out[r][2g+s] = sum_t D[r][t] * X[4g + p_s(r, g)][t],   D = dY.
+// Which two of each four outputs survive varies per row, so the matrix
+// instruction cannot skip work: the kernel is a dense bf16 "NT" GEMM (both
+// operands contiguous along the reduction index t, so no transposes), with the
+// selection done in the epilogue.
+//
+// v_mfma_f32_16x16x32_bf16 on gfx950: lane l holds row l%16 of A and column
+// l%16 of B, k = 8*(l/16)..+7; the result holds column l%16, rows
+// 4*(l/16)..+3.  Fragment j of each 64-column group maps lane c to output
+// column 4c + j, so every lane ends up holding all four columns of one 2:4
+// group of the weight: the selection is lane-local (two of the lane's four
+// accumulators, chosen by the group's nibble), and the 16 lanes of a row write
+// 16 consecutive float2 pairs -- 128 contiguous bytes.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nms {
+
+// ---------------------------------------------------------------------------
+// generic path: any dtype / alignment.  64 x 64 dense tile over (r, c).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void sddmm_generic_kernel(const T* __restrict__ D, int64_t ldd, const T* __restrict__ X,
+                                                            int64_t ldx, int64_t R, int64_t Kc, int64_t Tn,
+                                                            const uint8_t* __restrict__ meta, float* __restrict__ out) {
+  constexpr int TM = 64, TN = 64, KC = 32;
+  __shared__ float Ds[KC][TM + 4];
+  __shared__ float Xs[KC][TN + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  const int64_t m0 = (int64_t)blockIdx.y * TM, n0 = (int64_t)blockIdx.x * TN;
+  float acc[4][4] = {};
+  for (int64_t t0 = 0; t0 < Tn; t0 += KC) {
+    for (int i = tid; i < KC * TM; i += 256) {
+      const int r = i / KC, kk = i % KC;
+      const int64_t row = m0 + r, t = t0 + kk;
+      Ds[kk][r] = (row < R && t < Tn) ? Elem<T>::to_f32(D[row * ldd + t]) : 0.f;
+      const int64_t col = n0 + r;
+      Xs[kk][r] = (col < Kc && t < Tn) ? Elem<T>::to_f32(X[col * ldx + t]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < KC; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = Ds[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Xs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  // lane (ty, tx) holds columns n0 + 4tx .. +3: one whole 2:4 group
+  const int64_t gq = n0 / 4 + tx;
+  if (gq >= Kc / 4) return;
+  const int64_t mrow = (Kc + 7) / 8;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = m0 + ty * 4 + i;
+    if (row >= R) continue;
+    const uint32_t nib = (meta[row * mrow + gq / 2] >> (4 * (gq & 1))) & 0xF;
+    out[row * (Kc / 2) + 2 * gq] = acc[i][nib & 3];
+    out[row * (Kc / 2) + 2 * gq + 1] = acc[i][(nib >> 2) & 3];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fast path: bf16 v_mfma_f32_16x16x32_bf16
+// ---------------------------------------------------------------------------
+constexpr int DK = 64;        // t per k-step
+constexpr int D_PITCH = 72;   // u16 per LDS row (64 + 8 pad)
+
+__device__ inline int sd_lds_row(int n) { return (n & ~63) | ((n & 3) << 4) | ((n & 63) >> 2); }
+
+template <int BM, int BN, int WM, int WN>
+struct SddmmCfg {
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int FM = WM / 16, FN = WN / 16;
+  static constexpr int A_CH = BM * 8 / NT;     // 16-byte chunks of D per lane per k-step
+  static constexpr int B_CH = BN * 8 / NT;     // 16-byte chunks of X per lane per k-step
+  static constexpr int LDS_A = BM * D_PITCH * 2;
+  static constexpr int LDS_B = BN * D_PITCH * 2;
+  static constexpr int STAGE = LDS_A + LDS_B;
+  static_assert(WN % 64 == 0, "whole 64-column groups per wave");
+  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "chunking");
+  static_assert(NT == 256, "kernels are compiled for 256-lane workgroups");
+};
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256) void sddmm_mfma_kernel(
+    const uint16_t* __restrict__ D, int64_t ldd, const uint16_t* __restrict__ X, int64_t ldx, int64_t R, int64_t Kc,
+    int64_t Tn, const uint8_t* __restrict__ meta, float* __restrict__ out) {
+  using Cfg = SddmmCfg<BM, BN, WM, WN>;
+  constexpr int NT = Cfg::NT, FM = Cfg::FM, FN = Cfg::FN;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+
+  const int ntm = (int)((R + BM - 1) / BM), ntn = (int)((Kc + BN - 1) / BN);
+  const int nwg = ntm * ntn;
+  const int wg = xcd_remap(blockIdx.x, nwg);
+  constexpr int GM = 8;
+  const int grp = wg / (GM * ntn);
+  const int first_m = grp * GM;
+  const int gsz = (ntm - first_m) < GM ? (ntm - first_m) : GM;
+  const int within = wg - grp * GM * ntn;
+  const int tm = first_m + within % gsz, tn = within / gsz;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int KT = (int)((Tn + DK - 1) / DK);
+
+  u32x4 ra[Cfg::A_CH], rb[Cfg::B_CH];
+  auto load_global = [&](int kt) {
+    const int64_t t0 = (int64_t)kt * DK;
+#pragma unroll
+    for (int i = 0; i < Cfg::A_CH; ++i) {
+      const int c = tid + i * NT;
+      const int r = c >> 3, part = c & 7;
+      const int64_t row = m0 + r, t = t0 + part * 8;
+      ra[i] = (row < R && t < Tn) ? *reinterpret_cast<const u32x4*>(D + row * ldd + t) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::B_CH; ++i) {
+      const int c = tid + i * NT;
+      const int r = c >> 3, part = c & 7;
+      const int64_t col = n0 + r, t = t0 + part * 8;
+      rb[i] = (col < Kc && t < Tn) ? *reinterpret_cast<const u32x4*>(X + col * ldx + t) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_lds = [&](int buf) {
+    unsigned char* st = smem + buf * Cfg::STAGE;
+    uint16_t* As = reinterpret_cast<uint16_t*>(st);
+    uint16_t* Bs = reinterpret_cast<uint16_t*>(st + Cfg::LDS_A);
+#pragma unroll
+    for (int i = 0; i < Cfg::A_CH; ++i) {
+      const int c = tid + i * NT;
+      *reinterpret_cast<u32x4*>(As + (c >> 3) * D_PITCH + (c & 7) * 8) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::B_CH; ++i) {
+      const int c = tid + i * NT;
+      *reinterpret_cast<u32x4*>(Bs + sd_lds_row(c >> 3) * D_PITCH + (c & 7) * 8) = rb[i];
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int lr16 = lane & 15, lg = lane >> 4;
+
+  auto compute = [&](int buf) {
+    const unsigned char* st = smem + buf * Cfg::STAGE;
+    const uint16_t* As = reinterpret_cast<const uint16_t*>(st);
+    const uint16_t* Bs = reinterpret_cast<const uint16_t*>(st + Cfg::LDS_A);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      bf16x8 a[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(As + (wm * WM + i * 16 + lr16) * D_PITCH + kh * 32 + lg * 8);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        const int lrow = wn * WN + (f >> 2) * 64 + (f & 3) * 16 + lr16;
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bs + lrow * D_PITCH + kh * 32 + lg * 8);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][f], 0, 0, 0);
+      }
+    }
+  };
+
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) load_global(kt + 1);
+    compute(cur);
+    if (kt + 1 < KT) store_lds(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds the 4 columns of group gq for rows 16i + 4lg + e
+  const int64_t mrow = (Kc + 7) / 8;
+  const int64_t G = Kc / 4;
+#pragma unroll
+  for (int grp4 = 0; grp4 < FN / 4; ++grp4) {
+    const int64_t gq = (n0 + wn * WN + grp4 * 64) / 4 + lr16;
+    if (gq >= G) continue;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + wm * WM + i * 16 + lg * 4 + e;
+        if (row >= R) continue;
+        const uint32_t nib = (meta[row * mrow + gq / 2] >> (4 * (gq & 1))) & 0xF;
+        float v[4] = {acc[i][grp4 * 4 + 0][e], acc[i][grp4 * 4 + 1][e], acc[i][grp4 * 4 + 2][e],
+                      acc[i][grp4 * 4 + 3][e]};
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        f32x2 o = {v[nib & 3], v[(nib >> 2) & 3]};
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x2*>(out + row * (Kc / 2) + 2 * gq));
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t run_sddmm_mfma(const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
+                                 int64_t Tn, const uint8_t* meta, float* out, hipStream_t s) {
+  using Cfg = SddmmCfg<BM, BN, WM, WN>;
+  const size_t lds = 2 * (size_t)Cfg::STAGE;
+  auto kern = sddmm_mfma_kernel<BM, BN, WM, WN>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const int64_t ntiles = ((R + BM - 1) / BM) * ((Kc + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg::NT), lds, s, (const uint16_t*)D, ldd, (const uint16_t*)X,
+                     ldx, R, Kc, Tn, meta, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
+                           int64_t Tn, const uint8_t* meta, float* out, hipStream_t s) {
+  const char* e = getenv("NMSPARSE_FORCE_GENERIC");
+  const bool force = e && e[0] == '1';
+  if (dt == DT_BF16 && !force && Tn % 8 == 0 && ldd % 8 == 0 && ldx % 8 == 0 && (uintptr_t)D % 16 == 0 &&
+      (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0)
+    return run_sddmm_mfma<256, 128, 128, 64>(D, ldd, X, ldx, R, Kc, Tn, meta, out, s);
+  dim3 grid((unsigned)((Kc + 63) / 64), (unsigned)((R + 63) / 64));
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(sddmm_generic_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)D, ldd,
+                       (const uint16_t*)X, ldx, R, Kc, Tn, meta, out);
+  else
+    hipLaunchKernelGGL(sddmm_generic_kernel<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)D, ldd,
+                       (const uint32_t*)X, ldx, R, Kc, Tn, meta, out);
+  return hipGetLastError();
+}
+
+}  // namespace nms

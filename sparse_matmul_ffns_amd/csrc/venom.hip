@@ -1,0 +1,208 @@
+// V:N:M (VENOM-style) pruning and compression in one HBM pass (gfx950).
+//
+// "To 2:4 Sparsity and Beyond" (abstract) prunes FFN activations to v:n:m;
+// "Success story: ESPLAG" (Solution) stores them in the VENOM format; ReLU as
+// the activation comes from "Sparser, Faster, Lighter Transformer Language
+// Models" (Methodologie).  The rule implemented: per V-row block and M-column
+// group keep the 4 columns with the largest block L1 norm, then per row the
+// 2 largest magnitudes among those 4.
+//
+// One workgroup owns one V-row block and CW columns.  It stages the tile in
+// LDS once (ReLU applied on the way in), so HBM is read exactly once:
+//   1. coalesced 16-byte loads of the V x CW tile into LDS;
+//   2. one lane per column adds |h| over the V rows in fp64, top to bottom
+//      (the same sequence of additions as a sequential loop, so the sums are
+//      bit-identical to any other implementation that adds in row order);
+//   3. one lane per group ranks the M sums (lower column wins ties) and
+//      writes the group's 4 column indices;
+//   4. one lane per (row, 4 groups) picks 2 of the 4 selected values and
+//      writes 4 x 2 values (16 bytes for bf16) and 16 bits of nibbles.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nms {
+
+template <int M>
+__device__ inline int rank_f64(const double (&k)[M], int p) {
+  int r = 0;
+#pragma unroll
+  for (int q = 0; q < M; ++q) {
+    r += (k[q] > k[p]) ? 1 : 0;
+    r += (q < p && k[q] == k[p]) ? 1 : 0;
+  }
+  return r;
+}
+
+template <typename T, int M>
+__global__ __launch_bounds__(256) void venom_prune_kernel(const T* __restrict__ Z, int64_t ldz, int64_t K, int V,
+                                                          int relu, int CW, T* __restrict__ values,
+                                                          uint8_t* __restrict__ meta, uint8_t* __restrict__ colsel,
+                                                          uint8_t* __restrict__ mask, int64_t ldmask, int vec_in,
+                                                          int vec_out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int EPC = 16 / sizeof(T);       // elements per 16-byte chunk
+  const int tid = threadIdx.x;
+  const int64_t blk = blockIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.y * CW;
+  const int64_t G = K / M;
+  const int cols = (int)((K - c0) < CW ? (K - c0) : CW);  // valid columns in this tile (multiple of M)
+  const int ngr = cols / M;                                // valid groups
+  const int pitch = CW;                                    // elements per LDS row
+
+  T* tile = reinterpret_cast<T*>(smem);
+  double* l1 = reinterpret_cast<double*>(smem + (size_t)V * CW * sizeof(T));
+  uint8_t* csel = reinterpret_cast<uint8_t*>(l1 + CW);
+
+  // 1. stage the tile (ReLU'd) in LDS
+  const int cpr = CW / EPC;
+  const T* zb = Z + blk * V * ldz + c0;
+  for (int i = tid; i < V * cpr; i += 256) {
+    const int r = i / cpr, ch = i - r * cpr;
+    const int c = ch * EPC;
+    T x[EPC];
+    if (vec_in && c + EPC <= cols) {
+      u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(zb + (int64_t)r * ldz + c));
+      __builtin_memcpy(x, &t, 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) x[e] = (c + e < cols) ? zb[(int64_t)r * ldz + c + e] : (T)0;
+    }
+    if (relu) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) x[e] = Elem<T>::positive(x[e]) ? x[e] : (T)0;
+    }
+    u32x4 t;
+    __builtin_memcpy(&t, x, 16);
+    *reinterpret_cast<u32x4*>(tile + r * pitch + c) = t;
+  }
+  __syncthreads();
+
+  // 2. block column L1 norms, fp64, rows in ascending order
+  for (int c = tid; c < cols; c += 256) {
+    double acc = 0.0;
+    for (int r = 0; r < V; ++r) acc += (double)fabsf(Elem<T>::to_f32(tile[r * pitch + c]));
+    l1[c] = acc;
+  }
+  __syncthreads();
+
+  // 3. keep the 4 columns of each group with the largest L1 (lower column on ties)
+  for (int g = tid; g < ngr; g += 256) {
+    double k[M];
+#pragma unroll
+    for (int p = 0; p < M; ++p) k[p] = l1[g * M + p];
+    uint32_t packed = 0;
+    int j = 0;
+#pragma unroll
+    for (int p = 0; p < M; ++p) {
+      if (rank_f64<M>(k, p) < 4) {
+        packed |= (uint32_t)p << (8 * j);
+        ++j;
+      }
+    }
+    *reinterpret_cast<uint32_t*>(csel + 4 * g) = packed;
+    const int64_t gg = c0 / M + g;
+    uint8_t* dst = colsel + (blk * G + gg) * 4;
+    if (((uintptr_t)dst & 3) == 0) {
+      *reinterpret_cast<uint32_t*>(dst) = packed;
+    } else {
+      for (int e = 0; e < 4; ++e) dst[e] = (uint8_t)(packed >> (8 * e));
+    }
+  }
+  __syncthreads();
+
+  // 4. per row, 2 of the 4 selected columns of each group
+  const int nq = (ngr + 3) / 4;
+  const int64_t meta_row = (G + 1) / 2;
+  for (int u = tid; u < V * nq; u += 256) {
+    const int r = u / nq, q = u - r * nq;
+    const int64_t row = blk * V + r;
+    T v[8];
+    uint32_t nibs = 0;
+    const int gq = (ngr - 4 * q) < 4 ? (ngr - 4 * q) : 4;
+    uint8_t msk[4][M];
+    for (int gi = 0; gi < 4; ++gi) {
+      const int g = 4 * q + gi;
+      if (gi < gq) {
+        const uint32_t cs = *reinterpret_cast<const uint32_t*>(csel + 4 * g);
+        T x[4];
+        uint32_t k[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = tile[r * pitch + g * M + ((cs >> (8 * j)) & 0xFF)];
+          k[j] = Elem<T>::key(x[j]);
+        }
+        const uint32_t nib = select24(k[0], k[1], k[2], k[3]);
+        const int j0 = nib & 3, j1 = (nib >> 2) & 3;
+        v[2 * gi] = x[j0];
+        v[2 * gi + 1] = x[j1];
+        nibs |= nib << (4 * gi);
+        if (mask) {
+#pragma unroll
+          for (int p = 0; p < M; ++p) msk[gi][p] = 0;
+          msk[gi][(cs >> (8 * j0)) & 0xFF] = 1;
+          msk[gi][(cs >> (8 * j1)) & 0xFF] = 1;
+        }
+      } else {
+        v[2 * gi] = (T)0;
+        v[2 * gi + 1] = (T)0;
+      }
+    }
+    const int64_t gglob = c0 / M + 4 * q;  // first group of this unit, even
+    T* vd = values + row * (G * 2) + gglob * 2;
+    if (vec_out && gq == 4) {
+      if constexpr (sizeof(T) == 2) {
+        u32x4 t; __builtin_memcpy(&t, v, 16); *reinterpret_cast<u32x4*>(vd) = t;
+      } else {
+        u32x4 t0, t1; __builtin_memcpy(&t0, v, 16); __builtin_memcpy(&t1, v + 4, 16);
+        reinterpret_cast<u32x4*>(vd)[0] = t0; reinterpret_cast<u32x4*>(vd)[1] = t1;
+      }
+    } else {
+      for (int e = 0; e < 2 * gq; ++e) vd[e] = v[e];
+    }
+    uint8_t* md = meta + row * meta_row + gglob / 2;
+    md[0] = (uint8_t)(nibs & 0xFF);
+    if (gq > 2) md[1] = (uint8_t)((nibs >> 8) & 0xFF);
+    if (mask) {
+      uint8_t* mk = mask + row * ldmask + c0 + 4 * q * M;
+      for (int gi = 0; gi < gq; ++gi)
+#pragma unroll
+        for (int p = 0; p < M; ++p) mk[gi * M + p] = msk[gi][p];
+    }
+  }
+}
+
+template <typename T>
+static hipError_t venom_dispatch(const void* Z, int64_t ldz, int64_t R, int64_t K, int V, int M, int relu,
+                                 void* values, uint8_t* meta, uint8_t* colsel, uint8_t* mask, int64_t ldmask,
+                                 hipStream_t s) {
+  const int esz = sizeof(T);
+  int CW = (int)(65536 / ((int64_t)V * esz));
+  CW = (CW / 64) * 64;
+  if (CW > 512) CW = 512;
+  if (CW < 64) CW = 64;
+  const size_t lds = (size_t)V * CW * esz + (size_t)CW * sizeof(double) + (size_t)(CW / 4) * 4 + 64;
+  const int vec_in = ((uintptr_t)Z % 16 == 0) && ((ldz * esz) % 16 == 0);
+  const int vec_out = ((uintptr_t)values % 16 == 0) && (((K / M) * 2 * esz) % 16 == 0);
+  dim3 grid((unsigned)(R / V), (unsigned)((K + CW - 1) / CW));
+  auto run = [&](auto kern) {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, (const T*)Z, ldz, K, V, relu, CW, (T*)values, meta, colsel,
+                       mask, ldmask, vec_in, vec_out);
+    return hipGetLastError();
+  };
+  switch (M) {
+    case 4: return run(venom_prune_kernel<T, 4>);
+    case 8: return run(venom_prune_kernel<T, 8>);
+    default: return run(venom_prune_kernel<T, 16>);
+  }
+}
+
+hipError_t launch_prune_act_venom(int dt, const void* Z, int64_t ldz, int64_t R, int64_t K, int V, int M,
+                                  int relu, void* values, uint8_t* meta, uint8_t* colsel, uint8_t* mask,
+                                  int64_t ldmask, hipStream_t s) {
+  return dt == DT_BF16
+             ? venom_dispatch<uint16_t>(Z, ldz, R, K, V, M, relu, values, meta, colsel, mask, ldmask, s)
+             : venom_dispatch<uint32_t>(Z, ldz, R, K, V, M, relu, values, meta, colsel, mask, ldmask, s);
+}
+
+}  // namespace nms

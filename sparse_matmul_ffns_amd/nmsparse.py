@@ -1,0 +1,247 @@
+"""Thin Python binding of libnmsparse (ctypes).
+
+Argument marshalling only: every function checks device, dtype and layout of
+its torch tensors, allocates outputs with torch when none are given, and calls
+the C ABI on torch's current HIP stream.  Every step of the computation runs
+in the library's gfx950 kernels; nothing here computes, and there is no CPU
+fallback -- a missing library or a CPU tensor is an error.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnmsparse.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "nmsparse.h")
+
+NM_OK, NM_ERR_NULL, NM_ERR_SHAPE, NM_ERR_UNSUPPORTED, NM_ERR_ALIGN, NM_ERR_HIP = range(6)
+NM_F32, NM_BF16 = 0, 1
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_vp = ctypes.c_void_p
+
+# name -> argument types, in header order
+_SIGNATURES = {
+    "nm_prune": [_int, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp],
+    "nm_compress": [_int, _vp, _i64, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp],
+    "nm_decompress": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _vp],
+    "spmm_nm": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
+    "prune_act_venom": [_int, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _i64, _vp],
+    "spmm_venom": [_int, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
+    "nm_reprune_t": [_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp],
+    "sddmm_nm": [_int, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp],
+}
+
+_lib = None
+
+
+class NmError(RuntimeError):
+    """A non-OK status returned by libnmsparse."""
+
+    def __init__(self, status: int, call: str):
+        self.status = status
+        msg = lib().nm_status_str(status).decode()
+        if status == NM_ERR_HIP:
+            msg += ": " + lib().nm_last_hip_error().decode()
+        super().__init__(f"{call}: {msg} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sparse_matmul_ffns_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.nm_sizes.argtypes = [_i64, _i64, _int, _int, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                               ctypes.POINTER(_i64)]
+        L.nm_sizes.restype = None
+        L.nm_status_str.argtypes = [_int]
+        L.nm_status_str.restype = ctypes.c_char_p
+        L.nm_last_hip_error.argtypes = []
+        L.nm_last_hip_error.restype = ctypes.c_char_p
+        L.nm_version.argtypes = []
+        L.nm_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/nmsparse.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:nm_status|void|const char\*|int)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def _check(status: int, call: str) -> None:
+    if status != NM_OK:
+        raise NmError(status, call)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return NM_BF16
+    if t.dtype == torch.float32:
+        return NM_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: bfloat16 or float32")
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libnmsparse works on GPU tensors only (no CPU fallback)")
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Row stride of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with contiguous rows")
+    return t.stride(0)
+
+
+def _flat(t: torch.Tensor, name: str) -> None:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def sizes(R: int, K: int, N: int = 2, M: int = 4, V: int = 0):
+    """(n_values, meta_bytes, colsel_bytes) of the compressed form (host-only)."""
+    a, b, c = _i64(), _i64(), _i64()
+    lib().nm_sizes(R, K, N, M, V, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return a.value, b.value, c.value
+
+
+def nm_prune(A: torch.Tensor, N: int = 2, M: int = 4, mask: torch.Tensor | None = None) -> torch.Tensor:
+    _dev(A, mask)
+    R, K = A.shape
+    lda = _rows(A, "A")
+    if mask is None:
+        mask = torch.empty((R, K), dtype=torch.uint8, device=A.device)
+    _check(lib().nm_prune(_dt(A), _p(A), lda, R, K, N, M, _p(mask), _rows(mask, "mask"), _stream()), "nm_prune")
+    return mask
+
+
+def nm_compress(A: torch.Tensor, mask: torch.Tensor, N: int = 2, M: int = 4,
+                bad_groups: torch.Tensor | None = None, values=None, meta=None):
+    _dev(A, mask, bad_groups, values, meta)
+    R, K = A.shape
+    nv, mb, _ = sizes(R, K, N, M)
+    if values is None:
+        values = torch.empty((R, nv // R), dtype=A.dtype, device=A.device)
+    if meta is None:
+        meta = torch.empty((R, mb // R), dtype=torch.uint8, device=A.device)
+    _flat(values, "values"), _flat(meta, "meta")
+    _check(lib().nm_compress(_dt(A), _p(A), _rows(A, "A"), _p(mask), _rows(mask, "mask"), R, K, N, M,
+                             _p(values), _p(meta), _p(bad_groups), _stream()), "nm_compress")
+    return values, meta
+
+
+def nm_decompress(values: torch.Tensor, meta: torch.Tensor, K: int, N: int = 2, M: int = 4, out=None):
+    _dev(values, meta, out)
+    _flat(values, "values"), _flat(meta, "meta")
+    R = values.shape[0]
+    if out is None:
+        out = torch.empty((R, K), dtype=values.dtype, device=values.device)
+    _check(lib().nm_decompress(_dt(values), _p(values), _p(meta), R, K, N, M, _p(out), _rows(out, "out"),
+                               _stream()), "nm_decompress")
+    return out
+
+
+def spmm_nm(values: torch.Tensor, meta: torch.Tensor, K: int, B: torch.Tensor, out=None) -> torch.Tensor:
+    _dev(values, meta, B, out)
+    _flat(values, "values"), _flat(meta, "meta")
+    if B.dtype != values.dtype:
+        raise TypeError("values and B must share a dtype")
+    R = values.shape[0]
+    Nc = B.shape[1]
+    if B.shape[0] != K:
+        raise ValueError("B must have K rows")
+    if out is None:
+        out = torch.empty((R, Nc), dtype=torch.float32, device=B.device)
+    _check(lib().spmm_nm(_dt(B), _p(values), _p(meta), R, K, _p(B), _rows(B, "B"), Nc, _p(out),
+                         _rows(out, "out"), _stream()), "spmm_nm")
+    return out
+
+
+def prune_act_venom(Z: torch.Tensor, V: int, M: int = 8, apply_relu: bool = False, want_mask: bool = False,
+                    values=None, meta=None, colsel=None, mask=None):
+    _dev(Z, values, meta, colsel, mask)
+    R, K = Z.shape
+    nv, mb, cb = sizes(R, K, 2, M, V)
+    if values is None:
+        values = torch.empty((R, nv // R), dtype=Z.dtype, device=Z.device)
+    if meta is None:
+        meta = torch.empty((R, mb // R), dtype=torch.uint8, device=Z.device)
+    if colsel is None:
+        colsel = torch.empty((R // V, K // M, 4), dtype=torch.uint8, device=Z.device)
+    if want_mask and mask is None:
+        mask = torch.empty((R, K), dtype=torch.uint8, device=Z.device)
+    _flat(values, "values"), _flat(meta, "meta"), _flat(colsel, "colsel")
+    ldm = _rows(mask, "mask") if mask is not None else 0
+    _check(lib().prune_act_venom(_dt(Z), _p(Z), _rows(Z, "Z"), R, K, V, M, int(bool(apply_relu)), _p(values),
+                                 _p(meta), _p(colsel), _p(mask), ldm, _stream()), "prune_act_venom")
+    return (values, meta, colsel, mask) if mask is not None else (values, meta, colsel)
+
+
+def spmm_venom(values: torch.Tensor, meta: torch.Tensor, colsel: torch.Tensor, K: int, V: int, M: int,
+               B: torch.Tensor, out=None) -> torch.Tensor:
+    _dev(values, meta, colsel, B, out)
+    _flat(values, "values"), _flat(meta, "meta"), _flat(colsel, "colsel")
+    if B.dtype != values.dtype:
+        raise TypeError("values and B must share a dtype")
+    R = values.shape[0]
+    Nc = B.shape[1]
+    if B.shape[0] != K:
+        raise ValueError("B must have K rows")
+    if out is None:
+        out = torch.empty((R, Nc), dtype=torch.float32, device=B.device)
+    _check(lib().spmm_venom(_dt(B), _p(values), _p(meta), _p(colsel), R, K, V, M, _p(B), _rows(B, "B"), Nc,
+                            _p(out), _rows(out, "out"), _stream()), "spmm_venom")
+    return out
+
+
+def nm_reprune_t(values: torch.Tensor, meta: torch.Tensor, R: int, K: int, values_t=None, meta_t=None):
+    _dev(values, meta, values_t, meta_t)
+    _flat(values, "values"), _flat(meta, "meta")
+    if values_t is None:
+        values_t = torch.empty((K, R // 2), dtype=values.dtype, device=values.device)
+    if meta_t is None:
+        meta_t = torch.empty((K, (R + 7) // 8), dtype=torch.uint8, device=values.device)
+    _check(lib().nm_reprune_t(_dt(values), _p(values), _p(meta), R, K, _p(values_t), _p(meta_t), _stream()),
+           "nm_reprune_t")
+    return values_t, meta_t
+
+
+def sddmm_nm(D: torch.Tensor, X: torch.Tensor, meta: torch.Tensor, out=None) -> torch.Tensor:
+    _dev(D, X, meta, out)
+    _flat(meta, "meta")
+    if D.dtype != X.dtype:
+        raise TypeError("D and X must share a dtype")
+    R, T = D.shape
+    Kc = X.shape[0]
+    if X.shape[1] != T:
+        raise ValueError("D and X must have the same number of columns")
+    if out is None:
+        out = torch.empty((R, Kc // 2), dtype=torch.float32, device=D.device)
+    _flat(out, "out")
+    _check(lib().sddmm_nm(_dt(D), _p(D), _rows(D, "D"), _p(X), _rows(X, "X"), R, Kc, T, _p(meta), _p(out),
+                          _stream()), "sddmm_nm")
+    return out

@@ -23,10 +23,14 @@ import numpy as np
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round fp32 to bf16 (nearest, ties to even) and return the uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    """Round fp32 to bf16 (nearest, ties to even) and return the uint16 bit patterns.
+
+    Finite inputs only: adding 0x7FFF plus the lowest kept bit cannot carry
+    out of 32 bits for any finite fp32 pattern.
+    """
+    u = np.array(x, dtype=np.float32, copy=True).reshape(-1).view(np.uint32)
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (u >> np.uint32(16)).astype(np.uint16).reshape(np.shape(x))
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -35,14 +39,25 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def normal(shape, seed: int, mean: float = 0.0, std: float = 1.0, dtype: str = "bf16") -> np.ndarray:
-    """N(mean, std) samples: raw uint16 bf16 bits (dtype 'bf16') or float32 ('f32')."""
+    """N(mean, std) samples: raw uint16 bf16 bits (dtype 'bf16') or float32 ('f32').
+
+    float64 standard normals from PCG64(seed), scaled, rounded to fp32 and (for
+    bf16) to bf16; drawn in chunks, which yields the same stream as one draw.
+    """
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(dtype)
     rng = np.random.Generator(np.random.PCG64(seed))
-    x = (rng.standard_normal(size=shape, dtype=np.float64) * std + mean).astype(np.float32)
-    if dtype == "f32":
-        return x
-    if dtype == "bf16":
-        return f32_to_bf16_bits(x)
-    raise ValueError(dtype)
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint16 if dtype == "bf16" else np.float32)
+    chunk = 1 << 22
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        x = rng.standard_normal(size=e - s, dtype=np.float64)
+        x *= std
+        x += mean
+        y = x.astype(np.float32)
+        out[s:e] = f32_to_bf16_bits(y) if dtype == "bf16" else y
+    return out.reshape(shape)
 
 
 def small_ints(shape, seed: int, lo: int = -8, hi: int = 8, dtype: str = "bf16") -> np.ndarray:

@@ -1,0 +1,110 @@
+"""The C ABI loads, exports every declared symbol and rejects bad arguments
+before launching anything (CPU only: no call here reaches a kernel)."""
+
+import ctypes
+
+import pytest
+
+from sparse_matmul_ffns_amd import nmsparse as nm
+
+FAKE = 4096  # a non-NULL address that is never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    return nm.lib()
+
+
+def test_exports_every_header_function(L):
+    names = nm.header_functions()
+    assert set(names) >= {"nm_prune", "nm_compress", "spmm_nm", "spmm_venom", "prune_act_venom",
+                          "nm_decompress", "nm_reprune_t", "sddmm_nm", "nm_sizes", "nm_status_str"}
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_binding_covers_header():
+    assert set(nm._SIGNATURES) | {"nm_sizes", "nm_status_str", "nm_last_hip_error", "nm_version"} == \
+        set(nm.header_functions())
+
+
+def test_status_strings(L):
+    for s in range(6):
+        assert L.nm_status_str(s)
+    assert L.nm_version() >= 100
+    assert L.nm_last_hip_error() == b""
+
+
+def test_sizes():
+    assert nm.sizes(8192, 2048, 2, 4) == (8192 * 1024, 8192 * 256, 0)
+    assert nm.sizes(3, 12, 2, 4) == (18, 3 * 2, 0)                  # ceil(12/8) = 2 bytes per row
+    assert nm.sizes(2, 16, 2, 8) == (8, 2 * 2, 0)                   # 4 fields x 3 bits -> 2 bytes
+    assert nm.sizes(8192, 16384, 2, 8, 128) == (8192 * 4096, 8192 * 1024, 64 * 2048 * 4)
+    assert nm.sizes(4, 24, 2, 8, 2) == (4 * 6, 4 * 2, 2 * 3 * 4)    # 3 groups -> 2 bytes of nibbles
+
+
+def test_prune_errors(L):
+    s = None
+    assert L.nm_prune(1, None, 8, 4, 8, 2, 4, FAKE, 8, s) == nm.NM_ERR_NULL
+    assert L.nm_prune(1, FAKE, 8, 4, 8, 2, 4, None, 8, s) == nm.NM_ERR_NULL
+    assert L.nm_prune(7, FAKE, 8, 4, 8, 2, 4, FAKE, 8, s) == nm.NM_ERR_UNSUPPORTED
+    assert L.nm_prune(1, FAKE, 8, 4, 8, 2, 5, FAKE, 8, s) == nm.NM_ERR_UNSUPPORTED
+    assert L.nm_prune(1, FAKE, 8, 4, 8, 4, 4, FAKE, 8, s) == nm.NM_ERR_UNSUPPORTED
+    assert L.nm_prune(1, FAKE, 8, 4, 8, 0, 4, FAKE, 8, s) == nm.NM_ERR_UNSUPPORTED
+    assert L.nm_prune(1, FAKE, 8, 0, 8, 2, 4, FAKE, 8, s) == nm.NM_ERR_SHAPE
+    assert L.nm_prune(1, FAKE, 8, 4, 10, 2, 4, FAKE, 10, s) == nm.NM_ERR_SHAPE   # K % M
+    assert L.nm_prune(1, FAKE, 4, 4, 8, 2, 4, FAKE, 8, s) == nm.NM_ERR_SHAPE     # lda < K
+    assert L.nm_prune(1, FAKE, 8, 4, 8, 2, 4, FAKE, 7, s) == nm.NM_ERR_SHAPE     # ldmask < K
+    assert L.nm_prune(1, FAKE + 1, 8, 4, 8, 2, 4, FAKE, 8, s) == nm.NM_ERR_ALIGN
+    assert L.nm_prune(0, FAKE + 2, 8, 4, 8, 2, 4, FAKE, 8, s) == nm.NM_ERR_ALIGN
+
+
+def test_compress_decompress_errors(L):
+    s = None
+    assert L.nm_compress(1, FAKE, 8, FAKE, 8, 4, 8, 2, 4, None, FAKE, None, s) == nm.NM_ERR_NULL
+    assert L.nm_compress(1, FAKE, 8, FAKE, 8, 4, 8, 2, 16, FAKE, FAKE, None, s) == nm.NM_ERR_SHAPE
+    assert L.nm_compress(1, FAKE, 8, FAKE, 8, 4, 8, 2, 4, FAKE + 1, FAKE, None, s) == nm.NM_ERR_ALIGN
+    assert L.nm_compress(1, FAKE, 8, FAKE, 8, 4, 8, 2, 4, FAKE, FAKE, FAKE + 2, s) == nm.NM_ERR_ALIGN
+    assert L.nm_decompress(1, FAKE, None, 4, 8, 2, 4, FAKE, 8, s) == nm.NM_ERR_NULL
+    assert L.nm_decompress(1, FAKE, FAKE, 4, 8, 2, 4, FAKE, 6, s) == nm.NM_ERR_SHAPE
+    assert L.nm_decompress(1, FAKE, FAKE, 4, 8, 3, 3, FAKE, 8, s) == nm.NM_ERR_UNSUPPORTED
+
+
+def test_spmm_errors(L):
+    s = None
+    assert L.spmm_nm(1, FAKE, FAKE, 4, 8, None, 8, 8, FAKE, 8, s) == nm.NM_ERR_NULL
+    assert L.spmm_nm(1, FAKE, FAKE, 4, 6, FAKE, 8, 8, FAKE, 8, s) == nm.NM_ERR_SHAPE       # K % 4
+    assert L.spmm_nm(1, FAKE, FAKE, 4, 8, FAKE, 4, 8, FAKE, 8, s) == nm.NM_ERR_SHAPE       # ldb < Nc
+    assert L.spmm_nm(1, FAKE, FAKE, 4, 8, FAKE, 8, 8, FAKE, 7, s) == nm.NM_ERR_SHAPE       # ldc < Nc
+    assert L.spmm_nm(1, FAKE, FAKE, 4, 8, FAKE, 8, 0, FAKE, 8, s) == nm.NM_ERR_SHAPE
+    assert L.spmm_nm(3, FAKE, FAKE, 4, 8, FAKE, 8, 8, FAKE, 8, s) == nm.NM_ERR_UNSUPPORTED
+    assert L.spmm_nm(1, FAKE, FAKE, 4, 8, FAKE, 8, 8, FAKE + 2, 8, s) == nm.NM_ERR_ALIGN
+    assert L.spmm_venom(1, FAKE, FAKE, None, 4, 16, 2, 8, FAKE, 8, 8, FAKE, 8, s) == nm.NM_ERR_NULL
+    assert L.spmm_venom(1, FAKE, FAKE, FAKE, 4, 16, 3, 8, FAKE, 8, 8, FAKE, 8, s) == nm.NM_ERR_SHAPE  # R % V
+    assert L.spmm_venom(1, FAKE, FAKE, FAKE, 4, 16, 2, 6, FAKE, 8, 8, FAKE, 8, s) == nm.NM_ERR_UNSUPPORTED
+    assert L.spmm_venom(1, FAKE, FAKE, FAKE, 4, 16, 0, 8, FAKE, 8, 8, FAKE, 8, s) == nm.NM_ERR_UNSUPPORTED
+    assert L.spmm_venom(1, FAKE, FAKE, FAKE, 512, 16, 512, 8, FAKE, 8, 8, FAKE, 8, s) == nm.NM_ERR_UNSUPPORTED
+
+
+def test_venom_reprune_sddmm_errors(L):
+    s = None
+    assert L.prune_act_venom(1, FAKE, 16, 4, 16, 2, 8, 1, FAKE, FAKE, None, None, 0, s) == nm.NM_ERR_NULL
+    assert L.prune_act_venom(1, FAKE, 16, 4, 12, 2, 8, 1, FAKE, FAKE, FAKE, None, 0, s) == nm.NM_ERR_SHAPE
+    assert L.prune_act_venom(1, FAKE, 16, 4, 16, 2, 8, 1, FAKE, FAKE, FAKE, FAKE, 8, s) == nm.NM_ERR_SHAPE
+    assert L.prune_act_venom(1, FAKE, 16, 4, 16, 257, 8, 1, FAKE, FAKE, FAKE, None, 0, s) == nm.NM_ERR_UNSUPPORTED
+    assert L.nm_reprune_t(1, FAKE, FAKE, 6, 8, FAKE, FAKE, s) == nm.NM_ERR_SHAPE
+    assert L.nm_reprune_t(1, FAKE, FAKE, 8, 8, FAKE, None, s) == nm.NM_ERR_NULL
+    assert L.nm_reprune_t(1, FAKE, FAKE, 8, 8, FAKE + 1, FAKE, s) == nm.NM_ERR_ALIGN
+    assert L.sddmm_nm(1, FAKE, 8, FAKE, 8, 4, 6, 8, FAKE, FAKE, s) == nm.NM_ERR_SHAPE
+    assert L.sddmm_nm(1, FAKE, 4, FAKE, 8, 4, 8, 8, FAKE, FAKE, s) == nm.NM_ERR_SHAPE
+    assert L.sddmm_nm(1, FAKE, 8, FAKE, 8, 4, 8, 8, None, FAKE, s) == nm.NM_ERR_NULL
+    assert L.sddmm_nm(1, FAKE, 8, FAKE, 8, 4, 8, 8, FAKE, FAKE + 2, s) == nm.NM_ERR_ALIGN
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        nm.nm_prune(torch.zeros(4, 8, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        nm.spmm_nm(torch.zeros(4, 4, dtype=torch.bfloat16), torch.zeros(4, 1, dtype=torch.uint8), 8,
+                   torch.zeros(8, 8, dtype=torch.bfloat16))

@@ -1,0 +1,226 @@
+"""GPU parity at oracle-sized shapes: every call of the C ABI (through the thin
+binding) against the fp64 oracle on the same seeded bytes.
+
+Masks, metadata, column selections and compressed values must be bit-exact;
+matmul outputs must meet relative Frobenius error <= 1e-3 and elementwise
+|C - C*| <= 1e-2 (|A| |B|) against fp64, and be bit-exact where every partial
+sum is an integer below 2^24 (small-integer inputs).  Shapes span several
+tiles of each kernel and end in ragged tails; padded leading dimensions
+exercise the strided paths, and shapes that miss the vector-path conditions
+exercise the generic kernels.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_matmul_ffns_amd as nm
+from oracle import nm_oracle as O
+from sparse_matmul_ffns_amd import synth
+from tests.gpu_util import check_close, dev, host, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _inputs(kind, shape, seed, dtype):
+    if kind == "ties":
+        return synth.tie_rich(shape, seed, dtype=dtype)
+    if kind == "ints":
+        return synth.small_ints(shape, seed, dtype=dtype)
+    return synth.normal(shape, seed, dtype=dtype)
+
+
+# ---------------------------------------------------------------------------
+# nm_prune / nm_compress / nm_decompress: bit-exact
+# ---------------------------------------------------------------------------
+
+PRUNE_CASES = [(2, 4, 37, 44), (1, 4, 20, 64), (2, 8, 33, 88), (4, 8, 9, 64), (4, 16, 17, 96), (8, 16, 5, 48),
+               (2, 4, 300, 1024), (3, 4, 7, 12)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["ties", "normal"])
+@pytest.mark.parametrize("N,M,R,K", PRUNE_CASES, ids=[f"{n}of{m}_{r}x{k}" for n, m, r, k in PRUNE_CASES])
+@pytest.mark.parametrize("pad", [0, 8])
+def test_prune_compress_decompress(N, M, R, K, dtype, kind, pad):
+    raw = _inputs(kind, (R, K), seed=R * 7 + K + N, dtype=dtype)
+    A = dev(raw, dtype, pad=pad)
+    mask_t = torch.full((R, K + pad), 7, dtype=torch.uint8, device="cuda")[:, :K]
+    mask = host(nm.nm_prune(A, N, M, mask=mask_t))
+    want = O.prune_nm(raw, dtype, N, M)
+    assert np.array_equal(mask, want)
+    vals, meta = nm.nm_compress(A, dev(want, "u8"), N, M)
+    wv, wm, bad = O.compress_nm(raw, want, N, M)
+    assert bad == 0
+    assert host(vals).tobytes() == wv.tobytes()
+    assert np.array_equal(host(meta), wm)
+    out = nm.nm_decompress(dev(wv, dtype), dev(wm, "u8"), K, N, M)
+    assert host(out).tobytes() == O.decompress_nm(wv, wm, R, K, N, M).tobytes()
+
+
+def test_compress_bad_groups():
+    raw = synth.normal((64, 64), 5, dtype="bf16")
+    mask = O.prune_nm(raw, "bf16", 2, 4)
+    mask[0, 0:4] = [1, 1, 1, 0]
+    mask[13, 8:12] = [0, 0, 0, 0]
+    mask[63, 60:64] = [1, 0, 0, 0]
+    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+    vals, meta = nm.nm_compress(dev(raw, "bf16"), dev(mask, "u8"), 2, 4, bad_groups=counter)
+    wv, wm, bad = O.compress_nm(raw, mask, 2, 4)
+    assert int(counter.item()) == bad == 3
+    assert host(vals).tobytes() == wv.tobytes() and np.array_equal(host(meta), wm)
+
+
+# ---------------------------------------------------------------------------
+# spmm_nm
+# ---------------------------------------------------------------------------
+
+SPMM_CASES = [
+    # (R, K, Nc, pad_b, pad_c)  -- fast path needs K % 16 == 0, Nc % 8 == 0
+    (300, 208, 136, 0, 0),
+    (256, 512, 128, 8, 4),
+    (513, 1024, 264, 0, 0),
+    (64, 64, 64, 0, 0),
+    (17, 132, 40, 0, 0),      # K % 16 != 0: generic kernel
+    (40, 96, 13, 3, 1),       # Nc % 8 != 0: generic kernel
+]
+
+
+@pytest.mark.parametrize("R,K,Nc,pb,pc", SPMM_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SPMM_CASES])
+@pytest.mark.parametrize("kind", ["normal", "ints"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_spmm_nm(R, K, Nc, pb, pc, kind, dtype):
+    raw = _inputs(kind, (R, K), seed=R + K, dtype=dtype)
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, dtype, 2, 4), 2, 4)
+    Braw = _inputs(kind, (K, Nc), seed=Nc + 1, dtype=dtype)
+    Cbuf = torch.full((R, Nc + pc), float("nan"), dtype=torch.float32, device="cuda")
+    C = host(nm.spmm_nm(dev(vals, dtype), dev(meta, "u8"), K, dev(Braw, dtype, pad=pb), out=Cbuf[:, :Nc]))
+    Cref = O.spmm_nm(vals, meta, R, K, Braw, dtype)
+    if kind == "ints" and K <= 1024:
+        assert np.array_equal(C, Cref)     # every partial sum is an exact fp32 integer
+    A64 = O.decode(O.decompress_nm(vals, meta, R, K, 2, 4), dtype)
+    check_close(C, Cref, O.abs_bound(A64, O.decode(Braw, dtype)), f"spmm_nm {R}x{K}x{Nc}")
+    if pc:
+        assert torch.isnan(Cbuf[:, Nc:]).all()   # the padding columns are untouched
+
+
+def test_spmm_nm_identity():
+    R, K = 128, 256
+    raw = synth.normal((R, K), 3, dtype="bf16")
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, "bf16", 2, 4), 2, 4)
+    eye = synth.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    C = host(nm.spmm_nm(dev(vals, "bf16"), dev(meta, "u8"), K, dev(eye, "bf16")))
+    assert np.array_equal(C, O.decode(O.decompress_nm(vals, meta, R, K, 2, 4), "bf16").astype(np.float32))
+
+
+def test_spmm_nm_config1_fp32():
+    w = synth.WORKLOADS["nm24_fp32_256x512x128"]
+    A = synth.normal((256, 512), w["A"]["seed"], dtype="f32")
+    B = synth.normal((512, 128), w["B"]["seed"], dtype="f32")
+    mask = host(nm.nm_prune(dev(A, "f32")))
+    assert np.array_equal(mask, O.prune_nm(A, "f32", 2, 4))
+    vals, meta, _ = O.compress_nm(A, mask, 2, 4)
+    gv, gm = nm.nm_compress(dev(A, "f32"), dev(mask, "u8"))
+    assert host(gv).tobytes() == vals.tobytes() and np.array_equal(host(gm), meta)
+    C = host(nm.spmm_nm(dev(vals, "f32"), dev(meta, "u8"), 512, dev(B, "f32")))
+    A64 = O.decode(O.decompress_nm(vals, meta, 256, 512, 2, 4), "f32")
+    check_close(C, O.spmm_nm(vals, meta, 256, 512, B, "f32"), O.abs_bound(A64, B.astype(np.float64)), "cfg1")
+
+
+def test_spmm_nm_deterministic():
+    R, K, Nc = 512, 512, 256
+    raw = synth.normal((R, K), 9, dtype="bf16")
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, "bf16", 2, 4), 2, 4)
+    B = dev(synth.normal((K, Nc), 10, dtype="bf16"), "bf16")
+    v, m = dev(vals, "bf16"), dev(meta, "u8")
+    c1 = nm.spmm_nm(v, m, K, B)
+    c2 = nm.spmm_nm(v, m, K, B)
+    assert torch.equal(c1, c2)
+
+
+# ---------------------------------------------------------------------------
+# prune_act_venom / spmm_venom
+# ---------------------------------------------------------------------------
+
+VENOM_CASES = [(256, 1024, 64, 8), (384, 512, 128, 8), (24, 96, 3, 16), (64, 64, 16, 4), (256, 2048, 256, 8),
+               (10, 40, 5, 8), (128, 136, 64, 8)]
+
+
+@pytest.mark.parametrize("R,K,V,M", VENOM_CASES, ids=[f"{c[0]}x{c[1]}_V{c[2]}_M{c[3]}" for c in VENOM_CASES])
+@pytest.mark.parametrize("relu", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prune_act_venom(R, K, V, M, relu, dtype):
+    mean = -0.5 if relu else 0.0
+    raw = synth.normal((R, K), R + K + V, mean=mean, dtype=dtype)
+    raw[: min(R, V), :M] = synth.tie_rich((min(R, V), M), 1, dtype=dtype)   # ties in one group
+    vals, meta, colsel, mask = nm.prune_act_venom(dev(raw, dtype), V, M, apply_relu=relu, want_mask=True)
+    wv, wm, wc, wmask, _ = O.prune_venom(raw, dtype, V, M, relu)
+    assert np.array_equal(host(colsel), wc)
+    assert host(vals).tobytes() == wv.tobytes()
+    assert np.array_equal(host(meta), wm)
+    assert np.array_equal(host(mask), wmask)
+
+
+SPMM_VENOM_CASES = [(256, 1024, 264, 64, 8), (384, 512, 136, 128, 8), (48, 96, 40, 3, 16), (128, 136, 64, 64, 8),
+                    (512, 2048, 512, 128, 8), (128, 256, 72, 64, 4), (64, 512, 256, 64, 16)]
+
+
+@pytest.mark.parametrize("R,K,Nc,V,M", SPMM_VENOM_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}_V{c[3]}_M{c[4]}" for c in SPMM_VENOM_CASES])
+@pytest.mark.parametrize("kind", ["normal", "ints"])
+def test_spmm_venom(R, K, Nc, V, M, kind):
+    dtype = "bf16"
+    raw = _inputs(kind, (R, K), R * 3 + K, dtype)
+    vals, meta, colsel, _, _ = O.prune_venom(raw, dtype, V, M, False)
+    B = _inputs(kind, (K, Nc), Nc + 5, dtype)
+    C = host(nm.spmm_venom(dev(vals, dtype), dev(meta, "u8"), dev(colsel, "u8"), K, V, M, dev(B, dtype)))
+    Cref = O.spmm_venom(vals, meta, colsel, R, K, V, M, B, dtype)
+    if kind == "ints":
+        assert np.array_equal(C, Cref)
+    A64 = O.decode(O.decompress_venom(vals, meta, colsel, R, K, V, M), dtype)
+    check_close(C, Cref, O.abs_bound(A64, O.decode(B, dtype)), f"spmm_venom {R}x{K}x{Nc}")
+
+
+# ---------------------------------------------------------------------------
+# nm_reprune_t / sddmm_nm
+# ---------------------------------------------------------------------------
+
+REPRUNE_CASES = [(132, 68), (256, 512), (16, 16), (300, 200), (4, 4), (1024, 128)]
+
+
+@pytest.mark.parametrize("R,K", REPRUNE_CASES, ids=[f"{r}x{k}" for r, k in REPRUNE_CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_reprune_t(R, K, dtype, kind):
+    raw = _inputs(kind, (R, K), R + 2 * K, dtype)
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, dtype, 2, 4), 2, 4)
+    vt, mt = nm.nm_reprune_t(dev(vals, dtype), dev(meta, "u8"), R, K)
+    wvt, wmt = O.reprune_t(vals, meta, R, K, dtype)
+    assert host(vt).tobytes() == wvt.tobytes()
+    assert np.array_equal(host(mt), wmt)
+
+
+SDDMM_CASES = [(300, 136, 200), (256, 256, 512), (37, 20, 13), (64, 64, 64), (129, 68, 96)]
+
+
+@pytest.mark.parametrize("R,Kc,T", SDDMM_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SDDMM_CASES])
+@pytest.mark.parametrize("kind", ["normal", "ints"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sddmm_nm(R, Kc, T, kind, dtype):
+    D = _inputs(kind, (R, T), R + T, dtype)
+    X = _inputs(kind, (Kc, T), Kc + T + 1, dtype)
+    W = synth.normal((R, Kc), 77, dtype=dtype)
+    _, meta, _ = O.compress_nm(W, O.prune_nm(W, dtype, 2, 4), 2, 4)
+    out = host(nm.sddmm_nm(dev(D, dtype), dev(X, dtype), dev(meta, "u8")))
+    ref = O.sddmm_nm(D, X, meta, R, Kc, dtype)
+    if kind == "ints":
+        assert np.array_equal(out, ref)
+    full_bound = np.abs(O.decode(D, dtype)) @ np.abs(O.decode(X, dtype)).T
+    pos = O.unpack_positions(meta, R, Kc, 2, 4)
+    cols = (np.arange(Kc // 4)[None, :, None] * 4 + pos).reshape(R, Kc // 2)
+    check_close(out, ref, np.take_along_axis(full_bound, cols, axis=1), f"sddmm {R}x{Kc}x{T}")
