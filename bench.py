@@ -1,0 +1,298 @@
+"""Throughput of the sparse FFN hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one pass of the hot path over the workload's synthetic inputs
+(already resident in HBM when the timed region starts):
+  ffn_up_nm24_8192x2048x4096 (default): nm_prune -> nm_compress -> spmm_nm of
+      a bf16 2:4 weight [8192 x 2048] ~ N(0, 0.02) with activations
+      [2048 x 4096] ~ N(0, 1);
+  ffn_down_vnm64_2_8_2048x8192x4096: prune_act_venom (V=64, M=8) -> spmm_venom;
+  train_step_nm24_dmodel4096_dff16384_tok8192: nm_reprune_t -> spmm_nm (Y) ->
+      spmm_nm (dX) -> sddmm_nm (dW) (the weight's own prune and compress run
+      once before timing);
+  relu_act_vnm128_2_8_8192x16384x4096: prune_act_venom (ReLU, V=128, M=8) ->
+      spmm_venom;
+  nm24_fp32_256x512x128: the small fp32 case.
+`value` is dense-equivalent TFLOP/s of the whole step (2 R K Nc per product,
+pruned zeros counted as if dense).  The JSON line also carries the roofline
+of the step's dominant kernel, timed with HIP events on the stream it runs on,
+and the fp64 CPU oracle timed on the host (rank 0, N = 1 only).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "dense-equivalent TFLOP/s of 2:4 & V:N:M SpMM at FFN shapes; % of bf16 MFMA peak"
+
+
+def _parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="ffn_up_nm24_8192x2048x4096")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return p.parse_args()
+
+
+def _dev(raw):
+    import torch
+    if raw.dtype == np.uint16:
+        return torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(raw).cuda()
+
+
+# ---------------------------------------------------------------------------
+# workloads: each returns (setup dict, list of (kernel name, callable), flops)
+# ---------------------------------------------------------------------------
+
+def _w_nm(w, dtype):
+    import torch
+    import sparse_matmul_ffns_amd as nm
+    from sparse_matmul_ffns_amd import synth
+    R, K, Nc = w["R"], w["K"], w["Nc"]
+    A = _dev(synth.normal((R, K), w["A"]["seed"], w["A"]["mean"], w["A"]["std"], dtype))
+    B = _dev(synth.normal((K, Nc), w["B"]["seed"], w["B"]["mean"], w["B"]["std"], dtype))
+    mask = torch.empty((R, K), dtype=torch.uint8, device="cuda")
+    nv, mb, _ = nm.sizes(R, K, 2, 4)
+    vals = torch.empty((R, nv // R), dtype=A.dtype, device="cuda")
+    meta = torch.empty((R, mb // R), dtype=torch.uint8, device="cuda")
+    C = torch.empty((R, Nc), dtype=torch.float32, device="cuda")
+    steps = [
+        ("nm_prune", lambda: nm.nm_prune(A, 2, 4, mask=mask)),
+        ("nm_compress", lambda: nm.nm_compress(A, mask, 2, 4, values=vals, meta=meta)),
+        ("spmm_nm", lambda: nm.spmm_nm(vals, meta, K, B, out=C)),
+    ]
+    flops = {"spmm_nm": 2.0 * R * K * Nc}
+    algo = {"spmm_nm": ("mfma", R * (K // 2) * Nc * 2.0)}
+    return steps, flops, algo, "spmm_nm"
+
+
+def _w_venom(w, relu):
+    import torch
+    import sparse_matmul_ffns_amd as nm
+    from sparse_matmul_ffns_amd import synth
+    R, K, Nc, V, M = w["R"], w["K"], w["Nc"], w["V"], w["M"]
+    a = w["Z"] if relu else w["A"]
+    b = w["W"] if relu else w["B"]
+    Z = _dev(synth.normal((R, K), a["seed"], a["mean"], a["std"]))
+    B = _dev(synth.normal((K, Nc), b["seed"], b["mean"], b["std"]))
+    nv, mb, cb = nm.sizes(R, K, 2, M, V)
+    vals = torch.empty((R, nv // R), dtype=Z.dtype, device="cuda")
+    meta = torch.empty((R, mb // R), dtype=torch.uint8, device="cuda")
+    colsel = torch.empty((R // V, K // M, 4), dtype=torch.uint8, device="cuda")
+    C = torch.empty((R, Nc), dtype=torch.float32, device="cuda")
+    steps = [
+        ("prune_act_venom", lambda: nm.prune_act_venom(Z, V, M, apply_relu=relu, values=vals, meta=meta,
+                                                       colsel=colsel)),
+        ("spmm_venom", lambda: nm.spmm_venom(vals, meta, colsel, K, V, M, B, out=C)),
+    ]
+    flops = {"spmm_venom": 2.0 * R * K * Nc}
+    algo = {"spmm_venom": ("mfma", R * (K // M * 2) * Nc * 2.0),
+            "prune_act_venom": ("hbm", R * K * 2 + nv * 2 + mb + cb)}
+    return steps, flops, algo, "spmm_venom"
+
+
+def _w_train(w):
+    import torch
+    import sparse_matmul_ffns_amd as nm
+    from sparse_matmul_ffns_amd import synth
+    dm, dff, T = w["d_model"], w["d_ff"], w["tokens"]
+    W = _dev(synth.normal((dff, dm), w["W"]["seed"], w["W"]["mean"], w["W"]["std"]))
+    X = _dev(synth.normal((dm, T), w["X"]["seed"], w["X"]["mean"], w["X"]["std"]))
+    dY = _dev(synth.normal((dff, T), w["dY"]["seed"], w["dY"]["mean"], w["dY"]["std"]))
+    mask = nm.nm_prune(W)
+    vals, meta = nm.nm_compress(W, mask)
+    del mask
+    vt = torch.empty((dm, dff // 2), dtype=W.dtype, device="cuda")
+    mt = torch.empty((dm, dff // 8), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((dff, T), dtype=torch.float32, device="cuda")
+    dX = torch.empty((dm, T), dtype=torch.float32, device="cuda")
+    dW = torch.empty((dff, dm // 2), dtype=torch.float32, device="cuda")
+    steps = [
+        ("nm_reprune_t", lambda: nm.nm_reprune_t(vals, meta, dff, dm, values_t=vt, meta_t=mt)),
+        ("spmm_nm_fwd", lambda: nm.spmm_nm(vals, meta, dm, X, out=Y)),
+        ("spmm_nm_dx", lambda: nm.spmm_nm(vt, mt, dff, dY, out=dX)),
+        ("sddmm_nm", lambda: nm.sddmm_nm(dY, X, meta, out=dW)),
+    ]
+    g = 2.0 * dff * dm * T
+    flops = {"spmm_nm_fwd": g, "spmm_nm_dx": g, "sddmm_nm": g}
+    algo = {"spmm_nm_fwd": ("mfma", g / 2), "spmm_nm_dx": ("mfma", g / 2), "sddmm_nm": ("mfma", g),
+            "nm_reprune_t": ("hbm", 2 * (dff * dm // 2 * 2 + dff * dm // 8))}
+    return steps, flops, algo, "sddmm_nm"
+
+
+def build_workload(name):
+    from sparse_matmul_ffns_amd import synth
+    w = synth.WORKLOADS[name]
+    if w["kind"] == "spmm_nm":
+        return _w_nm(w, w["dtype"])
+    if w["kind"] == "spmm_venom":
+        return _w_venom(w, relu=False)
+    if w["kind"] == "act_venom":
+        return _w_venom(w, relu=True)
+    return _w_train(w)
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample, host cores)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(name):
+    from oracle import nm_oracle as O
+    from sparse_matmul_ffns_amd import synth
+    w = synth.WORKLOADS[name]
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    if w["kind"] in ("spmm_nm",):
+        R, K, Nc = w["R"], w["K"], w["Nc"]
+        rows = R
+        A = synth.normal((rows, K), w["A"]["seed"], w["A"]["mean"], w["A"]["std"], w["dtype"])
+        B = synth.normal((K, Nc), w["B"]["seed"], w["B"]["mean"], w["B"]["std"], w["dtype"])
+        t0 = time.perf_counter()
+        mask = O.prune_nm(A, w["dtype"], 2, 4)
+        v, m, _ = O.compress_nm(A, mask, 2, 4)
+        O.spmm_nm(v, m, rows, K, B, w["dtype"])
+        dt = time.perf_counter() - t0
+        fl = 2.0 * rows * K * Nc
+        sample = f"whole workload, one step: prune + compress of the [{R}x{K}] weight, fp64 decompress-and-dgemm with the [{K}x{Nc}] operand"
+    else:
+        R, K, Nc, V, M = w["R"], w["K"], w["Nc"], w["V"], w["M"]
+        rows = min(R, 4 * V)
+        a = w.get("Z") or w.get("A")
+        b = w.get("W") or w.get("B")
+        A = synth.normal((rows, K), a["seed"], a["mean"], a["std"])
+        B = synth.normal((K, Nc), b["seed"], b["mean"], b["std"])
+        t0 = time.perf_counter()
+        v, m, c, _, _ = O.prune_venom(A, "bf16", V, M, w["kind"] == "act_venom")
+        O.spmm_venom(v, m, c, rows, K, V, M, B, "bf16")
+        dt = time.perf_counter() - t0
+        fl = 2.0 * rows * K * Nc
+        sample = f"{rows} of {R} rows: V:N:M prune + fp64 decompress-and-dgemm with the full [{K}x{Nc}] operand"
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+# ---------------------------------------------------------------------------
+# counters recorded with rocprofv3 (profiles/), valid while the kernel source is unchanged
+# ---------------------------------------------------------------------------
+
+def _src_hash(kernel):
+    src = {"spmm_nm": "spmm.hip", "spmm_venom": "spmm.hip", "sddmm_nm": "sddmm.hip"}.get(kernel)
+    if src is None:
+        return None
+    with open(os.path.join(ROOT, "sparse_matmul_ffns_amd", "csrc", src), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256_16") != _src_hash(kernel):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU "
+              "component in this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    steps, flops, algo, dominant = build_workload(args.workload)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for _, fn in steps:
+            fn()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    names = [n for n, _ in steps]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, (_, fn) in enumerate(steps):
+            fn()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per_kernel_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+                     for i, n in enumerate(names)}
+    ms_per_step = elapsed * 1e3 / args.steps
+    total_flops = sum(flops.values())
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    bound, per_launch = algo[dominant]
+    t_dom = per_kernel_ms[dominant] * 1e-3
+    if bound == "mfma":
+        achieved, peak, unit = per_launch / t_dom / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = per_launch / t_dom / 1e9, PEAK_HBM_GBS, "GB/s"
+    from sparse_matmul_ffns_amd import synth
+    w = synth.WORKLOADS[args.workload]
+    if w["dtype"] == "f32":
+        peak = PEAK_FP32_MFMA_TFLOPS
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w["dtype"] == "bf16" else "f32",
+        "data": "synthetic (seeded normal inputs of the workload's shapes; no dataset or trained weights)",
+        "config": {"workload": args.workload, "kernels": names,
+                   "pct_of_bf16_peak_dense_equivalent": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "per_kernel_us": {n: round(v * 1e3, 2) for n, v in per_kernel_ms.items()},
+        "roofline": {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": recorded_traffic(args.workload, dominant)},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

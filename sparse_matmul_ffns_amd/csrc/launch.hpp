@@ -32,6 +32,12 @@ hipError_t launch_spmm_nm(int dt, const void* values, const uint8_t* meta, int64
 hipError_t launch_spmm_venom(int dt, const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R,
                              int64_t K, int V, int M, const void* B, int64_t ldb, int64_t Nc, float* C,
                              int64_t ldc, hipStream_t s);
+bool spmm_dma_ok(const void* values, const uint8_t* meta, const void* B, int64_t ldb, int64_t Nc, int64_t Kd);
+hipError_t launch_spmm_nm_dma(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* B,
+                              int64_t ldb, int64_t Nc, float* C, int64_t ldc, hipStream_t s);
+hipError_t launch_spmm_venom_dma(const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R,
+                                 int64_t Kd, int V, int M, int64_t G, const void* B, int64_t ldb, int64_t Nc,
+                                 float* C, int64_t ldc, hipStream_t s);
 hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R,
                            int64_t Kc, int64_t T, const uint8_t* meta, float* out, hipStream_t s);
 

@@ -346,17 +346,20 @@ static bool fast_ok(const void* values, const uint8_t* meta, const void* B, int6
          (uintptr_t)meta % 2 == 0 && (uintptr_t)B % 16 == 0 && (uintptr_t)C % 16 == 0;
 }
 
-static int g_force_generic = -1;
-static bool force_generic() {
-  if (g_force_generic < 0) {
-    const char* e = getenv("NMSPARSE_FORCE_GENERIC");
-    g_force_generic = (e && e[0] == '1') ? 1 : 0;
-  }
-  return g_force_generic == 1;
+// Kernel selection knobs, read on every call (for A/B tests of the tiers):
+// NMSPARSE_SPMM_TIER=1 skips the pipelined DMA kernel (register-staged SMFMAC
+// kernel instead); NMSPARSE_FORCE_GENERIC=1 uses the SIMT kernel everywhere.
+static bool env_is_one(const char* name) {
+  const char* e = getenv(name);
+  return e && e[0] == '1';
 }
+static int kernel_tier() { return env_is_one("NMSPARSE_SPMM_TIER") ? 1 : 0; }
+static bool force_generic() { return env_is_one("NMSPARSE_FORCE_GENERIC"); }
 
 hipError_t launch_spmm_nm(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* B,
                           int64_t ldb, int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
+  if (dt == DT_BF16 && !force_generic() && kernel_tier() == 0 && spmm_dma_ok(values, meta, B, ldb, Nc, K))
+    return launch_spmm_nm_dma(values, meta, R, K, B, ldb, Nc, C, ldc, s);
   if (dt == DT_BF16 && !force_generic() && fast_ok(values, meta, B, ldb, Nc, C, ldc, K))
     return run_smfmac<256, 128, 128, 64, false>(values, meta, nullptr, R, K, 4, 4, K / 4, B, ldb, Nc, C, ldc, s);
   return dt == DT_BF16 ? run_generic<uint16_t, false>(values, meta, nullptr, R, K, 4, 4, B, ldb, Nc, C, ldc, s)
@@ -368,6 +371,9 @@ hipError_t launch_spmm_venom(int dt, const void* values, const uint8_t* meta, co
                              hipStream_t s) {
   const int64_t G = K / M;
   const int64_t Kd = G * 4;  // the 2:4 domain: 4 selected columns per group
+  if (dt == DT_BF16 && !force_generic() && kernel_tier() == 0 && spmm_dma_ok(values, meta, B, ldb, Nc, Kd) &&
+      (uintptr_t)colsel % 4 == 0 && V % 64 == 0)
+    return launch_spmm_venom_dma(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
   if (dt == DT_BF16 && !force_generic() && fast_ok(values, meta, B, ldb, Nc, C, ldc, Kd) &&
       (uintptr_t)colsel % 4 == 0) {
     if (V % 128 == 0)

@@ -81,8 +81,10 @@ def test_compress_bad_groups():
 # ---------------------------------------------------------------------------
 
 SPMM_CASES = [
-    # (R, K, Nc, pad_b, pad_c)  -- fast path needs K % 16 == 0, Nc % 8 == 0
+    # (R, K, Nc, pad_b, pad_c): the pipelined kernel needs K % 64 == 0 and Nc % 8 == 0,
+    # the register-staged one K % 16 == 0 and Nc % 8 == 0; the rest runs the SIMT kernel
     (300, 208, 136, 0, 0),
+    (1000, 2048, 520, 8, 0),
     (256, 512, 128, 8, 4),
     (513, 1024, 264, 0, 0),
     (64, 64, 64, 0, 0),
@@ -91,10 +93,21 @@ SPMM_CASES = [
 ]
 
 
+TIERS = {"dma": {}, "staged": {"NMSPARSE_SPMM_TIER": "1"}, "generic": {"NMSPARSE_FORCE_GENERIC": "1"}}
+
+
+@pytest.fixture(params=list(TIERS))
+def tier(request, monkeypatch):
+    """Kernel tier of the bf16 SpMM: pipelined DMA, register-staged SMFMAC, or SIMT."""
+    for k, v in TIERS[request.param].items():
+        monkeypatch.setenv(k, v)
+    return request.param
+
+
 @pytest.mark.parametrize("R,K,Nc,pb,pc", SPMM_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SPMM_CASES])
 @pytest.mark.parametrize("kind", ["normal", "ints"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_spmm_nm(R, K, Nc, pb, pc, kind, dtype):
+def test_spmm_nm(R, K, Nc, pb, pc, kind, dtype, tier):
     raw = _inputs(kind, (R, K), seed=R + K, dtype=dtype)
     vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, dtype, 2, 4), 2, 4)
     Braw = _inputs(kind, (K, Nc), seed=Nc + 1, dtype=dtype)
@@ -173,7 +186,7 @@ SPMM_VENOM_CASES = [(256, 1024, 264, 64, 8), (384, 512, 136, 128, 8), (48, 96, 4
 @pytest.mark.parametrize("R,K,Nc,V,M", SPMM_VENOM_CASES,
                          ids=[f"{c[0]}x{c[1]}x{c[2]}_V{c[3]}_M{c[4]}" for c in SPMM_VENOM_CASES])
 @pytest.mark.parametrize("kind", ["normal", "ints"])
-def test_spmm_venom(R, K, Nc, V, M, kind):
+def test_spmm_venom(R, K, Nc, V, M, kind, tier):
     dtype = "bf16"
     raw = _inputs(kind, (R, K), R * 3 + K, dtype)
     vals, meta, colsel, _, _ = O.prune_venom(raw, dtype, V, M, False)
