@@ -48,9 +48,6 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
 }
-__device__ __forceinline__ void dma2(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(lds) : "memory");
-}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -77,13 +74,11 @@ struct DmaCfg {
   static constexpr int B_BYTES = 64 * B_ROW;
   static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
   static constexpr int A_INSTR = A_BYTES / 1024 / NW;      // per wave and stage
-  static constexpr int MS = (M_BYTES / (NW * 64)) >= 4 ? 4 : (M_BYTES / (NW * 64));   // bytes per lane
-  static constexpr int M_INSTR = M_BYTES / (NW * 64 * MS);
+  static constexpr int M_LANES = M_BYTES / 4 / NW;          // one dword DMA per wave, M_LANES lanes active
   static constexpr int B_INSTR = B_BYTES / 1024 / NW;
-  static constexpr int LOADS = A_INSTR + M_INSTR + B_INSTR;   // vmcnt per stage per wave
+  static constexpr int LOADS = A_INSTR + 1 + B_INSTR;      // vmcnt per stage per wave
   static_assert(A_BYTES % (1024 * NW) == 0, "A blocks per wave");
-  static_assert(MS == 1 || MS == 2 || MS == 4, "metadata DMA width");
-  static_assert(M_BYTES % (NW * 64 * MS) == 0, "metadata blocks per wave");
+  static_assert(M_BYTES % (4 * NW) == 0 && M_LANES >= 1 && M_LANES <= 64, "metadata lanes per wave");
   static_assert(B_BYTES % (1024 * NW) == 0 && (B_ROW % 1024 == 0 || 1024 % B_ROW == 0), "B blocks per wave");
   static_assert(FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "fragments");
   static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
@@ -134,15 +129,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
     row = row < R ? row : R - 1;
     a_src[t] = values + row * vrow + 8 * (2 * (q & 1) + (lane >> 5));
   }
-  // metadata: byte offset o = (q*64 + lane)*MS in the [BM][8] tile
-  const uint8_t* m_src[Cfg::M_INSTR];
-#pragma unroll
-  for (int t = 0; t < Cfg::M_INSTR; ++t) {
-    const int q = wave * Cfg::M_INSTR + t;
-    const int o = (q * 64 + lane) * Cfg::MS;
+  // metadata: wave w, lane l < M_LANES loads the dword at byte (w*M_LANES + l)*4 of the [BM][8] tile
+  const uint8_t* m_src;
+  {
+    const int o = (wave * Cfg::M_LANES + (lane < Cfg::M_LANES ? lane : 0)) * 4;
     int64_t row = m0 + (o >> 3);
     row = row < R ? row : R - 1;
-    m_src[t] = meta + row * mrow + (o & 7);
+    m_src = meta + row * mrow + (o & 7);
   }
   // B: instruction q covers LDS bytes q*1024.. of the [64][BN] tile
   int b_row[Cfg::B_INSTR];
@@ -167,12 +160,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
 #pragma unroll
     for (int t = 0; t < Cfg::A_INSTR; ++t)
       dma16(a_src[t] + k0 / 2, uniform(st + (wave * Cfg::A_INSTR + t) * 1024));
-#pragma unroll
-    for (int t = 0; t < Cfg::M_INSTR; ++t) {
-      const uint32_t dst = uniform(st + Cfg::A_BYTES + (wave * Cfg::M_INSTR + t) * 64 * Cfg::MS);
-      if constexpr (Cfg::MS == 4) dma4(m_src[t] + k0 / 8, dst);
-      else if constexpr (Cfg::MS == 2) dma2(m_src[t] + k0 / 8, dst);
-      else asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ubyte %0, off" ::"v"(m_src[t] + k0 / 8), "s"(dst) : "memory");
+    {
+      // lanes >= M_LANES are masked off; the instruction still counts once in vmcnt
+      const uint32_t dst = uniform(st + Cfg::A_BYTES + wave * Cfg::M_LANES * 4);
+      if (Cfg::M_LANES == 64 || lane < Cfg::M_LANES) dma4(m_src + k0 / 8, dst);
     }
 #pragma unroll
     for (int t = 0; t < Cfg::B_INSTR; ++t) {
