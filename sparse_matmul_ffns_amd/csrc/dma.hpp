@@ -1,0 +1,35 @@
+// Direct global->LDS loads and explicit pipeline waits for gfx950 kernels.
+//
+// global_load_lds_dword(x4) writes each lane's data to LDS at M0 + size*lane,
+// so one wave fills a contiguous block from 64 arbitrary global addresses.
+// The loads are issued from inline assembly: the compiler then leaves their
+// completion to the kernel, which waits with an explicit vmcnt before the
+// barrier that publishes a stage (the compiler would otherwise wait for every
+// outstanding LDS DMA before any LDS read, serialising the pipeline).  The
+// kernels that use these helpers set M0 only here and never index register
+// arrays dynamically, so nothing else in them depends on M0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nms {
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace nms

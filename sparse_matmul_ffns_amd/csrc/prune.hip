@@ -179,6 +179,73 @@ __global__ __launch_bounds__(256) void nm_compress_kernel(const T* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// nm_compress, 2:4 with 16-byte aligned rows: one thread per 16 elements
+// (4 groups): 16-byte loads of A and mask, one 16- or 32-byte store of the 8
+// kept values and one 2-byte store of their 4 nibbles.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void nm_compress24_vec_kernel(const T* __restrict__ A, int64_t lda,
+                                                                const uint8_t* __restrict__ mask, int64_t ldmask,
+                                                                int64_t R, int64_t K, T* __restrict__ values,
+                                                                uint8_t* __restrict__ meta, int32_t* bad_groups) {
+  const int64_t per_row = K / 16;
+  const int64_t cid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int bad = 0;
+  if (cid < R * per_row) {
+    const int64_t r = cid / per_row;
+    const int64_t c0 = (cid - r * per_row) * 16;
+    T x[16];
+    uint8_t m[16];
+    const u32x4* a4 = reinterpret_cast<const u32x4*>(A + r * lda + c0);
+#pragma unroll
+    for (int i = 0; i < 16 * (int)sizeof(T) / 16; ++i) {
+      u32x4 t = __builtin_nontemporal_load(a4 + i);
+      __builtin_memcpy(&x[i * 16 / sizeof(T)], &t, 16);
+    }
+    {
+      u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(mask + r * ldmask + c0));
+      __builtin_memcpy(m, &t, 16);
+    }
+    T v[8];
+    uint32_t nibs = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      int cnt = 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) cnt += m[4 * g + p] ? 1 : 0;
+      uint32_t nib = 0;
+      T v0 = (T)0, v1 = (T)0;
+      if (cnt == 2) {
+        int s = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          if (m[4 * g + p]) {
+            if (s == 0) v0 = x[4 * g + p]; else v1 = x[4 * g + p];
+            nib |= (uint32_t)p << (2 * s);
+            ++s;
+          }
+        }
+      } else {
+        ++bad;
+        nib = 0x4;  // positions 0 and 1, values +0.0
+      }
+      v[2 * g] = v0;
+      v[2 * g + 1] = v1;
+      nibs |= nib << (4 * g);
+    }
+    T* vd = values + r * (K / 2) + c0 / 2;
+#pragma unroll
+    for (int i = 0; i < 8 * (int)sizeof(T) / 16; ++i) {
+      u32x4 t;
+      __builtin_memcpy(&t, &v[i * 16 / sizeof(T)], 16);
+      __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(vd) + i);
+    }
+    *reinterpret_cast<uint16_t*>(meta + r * (K / 8) + c0 / 8) = (uint16_t)nibs;
+  }
+  if (bad_groups != nullptr && bad > 0) atomicAdd(bad_groups, bad);
+}
+
+// ---------------------------------------------------------------------------
 // nm_decompress: one thread per chunk of CG groups of one row.
 // ---------------------------------------------------------------------------
 template <typename T, int M>
@@ -245,6 +312,14 @@ template <typename T>
 static hipError_t compress_dispatch(const void* A, int64_t lda, const uint8_t* mask, int64_t ldmask,
                                     int64_t R, int64_t K, int N, int M, void* values, uint8_t* meta,
                                     int32_t* bad, hipStream_t s) {
+  const int esz = sizeof(T);
+  if (N == 2 && M == 4 && K % 16 == 0 && (uintptr_t)A % 16 == 0 && (lda * esz) % 16 == 0 &&
+      (uintptr_t)mask % 16 == 0 && ldmask % 16 == 0 && (uintptr_t)values % 16 == 0 && (uintptr_t)meta % 2 == 0) {
+    const int64_t n = R * (K / 16);
+    hipLaunchKernelGGL(nm_compress24_vec_kernel<T>, dim3(nblocks(n, 256)), dim3(256), 0, s, (const T*)A, lda, mask,
+                       ldmask, R, K, (T*)values, meta, bad);
+    return hipGetLastError();
+  }
   const int64_t G = K / M;
   const int CG = compress_chunk_groups(N, M);
   const int64_t meta_row = meta_row_bytes(K, N, M);

@@ -17,6 +17,7 @@
 // accumulators, chosen by the group's nibble), and the 16 lanes of a row write
 // 16 consecutive float2 pairs -- 128 contiguous bytes.
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 
 namespace nms {
@@ -212,6 +213,184 @@ __global__ __launch_bounds__(256) void sddmm_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// pipelined path: direct-to-LDS loads, v_mfma_f32_32x32x16_bf16.
+//
+// v_mfma_f32_32x32x16_bf16 on gfx950: lane l holds A row l%32 and B column
+// l%32, k = 8*(l/32)..+7; the result holds column l%32 and, in element e, row
+// 8*(e/4) + 4*(l/32) + e%4.  A wave owns 64 rows x 128 output columns; its
+// four B fragments j = 0..3 map lane c to output column 4c + j, so lane c holds
+// every column of 2:4 group c and selects two of them by the group's nibble.
+// Tiles are staged per 32 t: D rows and X rows of 64 bytes, loaded with
+// direct-to-LDS dwordx4 loads; X rows are placed so that fragment j's 32 rows
+// are consecutive in LDS, and the 16-byte chunks of LDS row r are XOR-swizzled
+// by (r >> 1) & 3, which makes every ds_read_b128 of an operand conflict-free.
+// ---------------------------------------------------------------------------
+constexpr int TK = 32;   // t per stage
+
+__device__ __forceinline__ int sd_swz(int r) { return (r >> 1) & 3; }
+// LDS row of output column n (within a 128-column wave group): fragment j = n%4, lane c = n/4
+__device__ __forceinline__ int sd_xrow(int n) { return (n & ~127) | ((n & 3) << 5) | ((n & 127) >> 2); }
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+struct SdCfg {
+  static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int FM = WM / 32;
+  static constexpr int A_BYTES = BM * TK * 2, B_BYTES = BN * TK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_INSTR = A_BYTES / 1024 / NW, B_INSTR = B_BYTES / 1024 / NW;
+  static constexpr int LOADS = A_INSTR + B_INSTR;
+  static_assert(WN == 128, "a wave owns 128 output columns (32 whole 2:4 groups)");
+  static_assert(WM % 32 == 0 && A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "tiling");
+  static_assert(LOADS * (STAGES - 2) <= 63 && STAGE * STAGES <= 160 * 1024, "pipeline");
+};
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
+    const uint16_t* __restrict__ D, int64_t ldd, const uint16_t* __restrict__ X, int64_t ldx, int64_t R, int64_t Kc,
+    int64_t Tn, const uint8_t* __restrict__ meta, float* __restrict__ out) {
+  using Cfg = SdCfg<BM, BN, WAVES_M, WAVES_N, STAGES>;
+  constexpr int FM = Cfg::FM;
+  extern __shared__ __align__(1024) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+  const int ntm = (int)((R + BM - 1) / BM), ntn = (int)((Kc + BN - 1) / BN);
+  const int nwg = ntm * ntn;
+  const int wg = xcd_remap(blockIdx.x, nwg);
+  constexpr int GM = 4;
+  const int grp = wg / (GM * ntn);
+  const int first_m = grp * GM;
+  const int gsz = (ntm - first_m) < GM ? (ntm - first_m) : GM;
+  const int within = wg - grp * GM * ntn;
+  const int tm = first_m + within % gsz, tn = within / gsz;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int KT = (int)(Tn / TK);
+  const uint32_t smem_base = lds_addr(smem);
+
+  // DMA sources: instruction q covers LDS bytes q*1024.. = 16 rows of 64 bytes;
+  // lane -> LDS row 16q + lane/4, chunk position lane%4 (holding chunk pos ^ swz)
+  const uint16_t* a_src[Cfg::A_INSTR];
+#pragma unroll
+  for (int t = 0; t < Cfg::A_INSTR; ++t) {
+    const int r = 16 * (wave * Cfg::A_INSTR + t) + (lane >> 2);
+    const int c = (lane & 3) ^ sd_swz(r);
+    int64_t row = m0 + r;
+    row = row < R ? row : R - 1;
+    a_src[t] = D + row * ldd + 8 * c;
+  }
+  const uint16_t* b_src[Cfg::B_INSTR];
+#pragma unroll
+  for (int t = 0; t < Cfg::B_INSTR; ++t) {
+    const int r = 16 * (wave * Cfg::B_INSTR + t) + (lane >> 2);     // LDS row
+    const int c = (lane & 3) ^ sd_swz(r);
+    const int n = (r & ~127) | ((r & 31) << 2) | ((r & 127) >> 5);   // inverse of sd_xrow
+    int64_t col = n0 + n;
+    col = col < Kc ? col : Kc - 1;
+    b_src[t] = X + col * ldx + 8 * c;
+  }
+  auto issue = [&](int kt) {
+    const uint32_t st = smem_base + (kt % STAGES) * Cfg::STAGE;
+    const int64_t t0 = (int64_t)kt * TK;
+#pragma unroll
+    for (int t = 0; t < Cfg::A_INSTR; ++t) dma16(a_src[t] + t0, uniform(st + (wave * Cfg::A_INSTR + t) * 1024));
+#pragma unroll
+    for (int t = 0; t < Cfg::B_INSTR; ++t)
+      dma16(b_src[t] + t0, uniform(st + Cfg::A_BYTES + (wave * Cfg::B_INSTR + t) * 1024));
+  };
+
+  f32x16 acc[FM][4];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int l32 = lane & 31, aa = lane >> 5;
+  int a_off[FM][2], b_off[4][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int c = 2 * kk + aa;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * Cfg::WM + 32 * i + l32;
+      a_off[i][kk] = r * (TK * 2) + ((c ^ sd_swz(r)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 128 + 32 * j + l32;   // = sd_xrow(wn*128 + 4*l32 + j)
+      b_off[j][kk] = Cfg::A_BYTES + r * (TK * 2) + ((c ^ sd_swz(r)) << 4);
+    }
+  }
+
+  auto compute = [&](int kt) {
+    const unsigned char* st = smem + (kt % STAGES) * Cfg::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 a[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i][kk]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(st + b_off[j][kk]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) issue(s);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + STAGES - 2 < KT) wait_vmcnt<Cfg::LOADS * (STAGES - 2)>();
+    else if (kt + 1 < KT) wait_vmcnt<Cfg::LOADS>();   // fewer stages left: at most one newer stage outstanding
+    else wait_vmcnt<0>();
+    barrier();
+    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+    compute(kt);
+  }
+
+  // epilogue: lane l32 holds columns 4*l32 .. +3 of the wave's 128 = 2:4 group gq
+  const int64_t G = Kc / 4, mrow = (Kc + 7) / 8;
+  const int64_t gq = (n0 + wn * 128) / 4 + l32;
+  if (gq < G) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * Cfg::WM + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
+        if (row < R) {
+          const uint32_t nib = (meta[row * mrow + gq / 2] >> (4 * (gq & 1))) & 0xF;
+          const float v0 = acc[i][0][e], v1 = acc[i][1][e], v2 = acc[i][2][e], v3 = acc[i][3][e];
+          const uint32_t p0 = nib & 3, p1 = (nib >> 2) & 3;
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          f32x2 o;
+          o[0] = p0 == 0 ? v0 : p0 == 1 ? v1 : p0 == 2 ? v2 : v3;
+          o[1] = p1 == 0 ? v0 : p1 == 1 ? v1 : p1 == 2 ? v2 : v3;
+          __builtin_nontemporal_store(o, reinterpret_cast<f32x2*>(out + row * (Kc / 2) + 2 * gq));
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+static hipError_t run_sddmm_dma(const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
+                                int64_t Tn, const uint8_t* meta, float* out, hipStream_t s) {
+  using Cfg = SdCfg<BM, BN, WAVES_M, WAVES_N, STAGES>;
+  const size_t lds = (size_t)Cfg::STAGE * STAGES;
+  auto kern = sddmm_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const int64_t ntiles = ((R + BM - 1) / BM) * ((Kc + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg::NT), lds, s, (const uint16_t*)D, ldd, (const uint16_t*)X,
+                     ldx, R, Kc, Tn, meta, out);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN>
 static hipError_t run_sddmm_mfma(const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
                                  int64_t Tn, const uint8_t* meta, float* out, hipStream_t s) {
@@ -229,6 +408,11 @@ hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, in
                            int64_t Tn, const uint8_t* meta, float* out, hipStream_t s) {
   const char* e = getenv("NMSPARSE_FORCE_GENERIC");
   const bool force = e && e[0] == '1';
+  const char* tier = getenv("NMSPARSE_SPMM_TIER");
+  const bool staged = tier && tier[0] == '1';
+  if (dt == DT_BF16 && !force && !staged && Tn % TK == 0 && ldd % 8 == 0 && ldx % 8 == 0 && (uintptr_t)D % 16 == 0 &&
+      (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0)
+    return run_sddmm_dma<256, 256, 4, 2, 4>(D, ldd, X, ldx, R, Kc, Tn, meta, out, s);
   if (dt == DT_BF16 && !force && Tn % 8 == 0 && ldd % 8 == 0 && ldx % 8 == 0 && (uintptr_t)D % 16 == 0 &&
       (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0)
     return run_sddmm_mfma<256, 128, 128, 64>(D, ldd, X, ldx, R, Kc, Tn, meta, out, s);

@@ -36,28 +36,12 @@
 // Epilogue: each (fragment, element) store covers 128 contiguous bytes of a
 // row of C (non-temporal: C is written once).
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 
 namespace nms {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)p;
-}
-__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // swizzle of the 16-byte chunk index of B row r
 __device__ __forceinline__ int bswz(int r) { return (r & 3) << 1; }

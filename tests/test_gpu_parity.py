@@ -218,20 +218,20 @@ def test_reprune_t(R, K, dtype, kind):
     assert np.array_equal(host(mt), wmt)
 
 
-SDDMM_CASES = [(300, 136, 200), (256, 256, 512), (37, 20, 13), (64, 64, 64), (129, 68, 96)]
+SDDMM_CASES = [(300, 136, 200), (256, 256, 512), (37, 20, 13), (64, 64, 64), (129, 68, 96), (520, 1032, 1024)]
 
 
 @pytest.mark.parametrize("R,Kc,T", SDDMM_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SDDMM_CASES])
 @pytest.mark.parametrize("kind", ["normal", "ints"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_sddmm_nm(R, Kc, T, kind, dtype):
+def test_sddmm_nm(R, Kc, T, kind, dtype, tier):
     D = _inputs(kind, (R, T), R + T, dtype)
     X = _inputs(kind, (Kc, T), Kc + T + 1, dtype)
     W = synth.normal((R, Kc), 77, dtype=dtype)
     _, meta, _ = O.compress_nm(W, O.prune_nm(W, dtype, 2, 4), 2, 4)
     out = host(nm.sddmm_nm(dev(D, dtype), dev(X, dtype), dev(meta, "u8")))
     ref = O.sddmm_nm(D, X, meta, R, Kc, dtype)
-    if kind == "ints":
+    if kind == "ints" and T <= 1024:
         assert np.array_equal(out, ref)
     full_bound = np.abs(O.decode(D, dtype)) @ np.abs(O.decode(X, dtype)).T
     pos = O.unpack_positions(meta, R, Kc, 2, 4)
