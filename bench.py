@@ -47,7 +47,23 @@ def _parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="ffn_up_nm24_8192x2048x4096")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device copy of known size (to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return p.parse_args()
+
+
+def copy_calibration(steps):
+    """A plain 256 MiB device-to-device copy, `steps` times: the reference for the
+    HBM byte counters (each launch reads and writes exactly 256 MiB)."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": steps}))
 
 
 def _dev(raw):
@@ -232,6 +248,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     steps, flops, algo, dominant = build_workload(args.workload)
     torch.cuda.synchronize()
 

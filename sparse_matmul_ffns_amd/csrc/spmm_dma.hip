@@ -1,5 +1,5 @@
-// Pipelined SpMM for 2:4 and V:N:M operands on gfx950: direct-to-LDS loads,
-// transposing LDS reads and v_smfmac_f32_32x32x32_bf16.
+// Pipelined SpMM for 2:4 and V:N:M operands on gfx950 with
+// v_smfmac_f32_32x32x32_bf16.
 //
 // Product: C[r][n] = sum_k A[r][k] B[k][n], A in 2:4 form (values + nibbles),
 // or V:N:M form, which is 2:4 over the selected columns with the selected rows
@@ -13,70 +13,97 @@
 //    B column l%32 with k = 8*(l/32)..+7 in elements 0..7 and
 //    k = 16 + 8*(l/32)..+7 in elements 8..15; C column l%32, element e at
 //    row 8*(e/4) + 4*(l/32) + e%4.
-//  * global_load_lds_dwordx4 writes lane l's 16 bytes to M0 + 16*l: a wave
-//    fills 1 KB of LDS in lane order, from any 64 global addresses.
-//  * ds_read_b64_tr_b16, per 16-lane group: with lane i addressing the 4
-//    elements at row kb + i/4, columns c0 + 4*(i%4)..+3 of a row-major tile,
-//    lane j receives B[kb + t][c0 + j] for t = 0..3 -- four consecutive k of
-//    one column, i.e. the transposed operand.
+//  * global_load_lds_dwordx4 writes lane l's 16 bytes to M0 + 16*l.
+//  * LDS read throughput per CU: ds_read_b128 ~2.6x ds_read_b64_tr_b16, so
+//    the B operand is transposed in registers on its way into LDS and read
+//    back with ds_read_b128.
 //
 // Data flow per workgroup (BM x BN tile of C, 64 dense k per stage):
-//  * values: one 1 KB block per (32-row fragment, 32-k half), lanes in
-//    instruction order, so every A operand read is one conflict-free
+//  * values: direct-to-LDS, one 1 KB block per (32-row fragment, 32-k half)
+//    in instruction lane order: every A operand read is one conflict-free
 //    ds_read_b128 at block + 16*lane;
-//  * metadata: [BM][8 bytes] row-major; one ds_read_b64 per 32-row fragment
-//    yields the index operands of both k halves;
-//  * B: [64][BN] row-major as stored in HBM (rows gathered through colsel
-//    for V:N:M), 16-byte chunks XOR-swizzled per row so that the four rows a
-//    16-lane group reads in one transposing read fall in distinct banks;
-//  * STAGES-deep ring of LDS buffers; the loads of stage k+2 are in flight
-//    while stage k runs on the matrix cores.  Loads are issued with inline
-//    assembly and waited for with explicit vmcnt counts, so the compiler's
-//    conservative waits for LDS DMA never serialise the pipeline.
+//  * metadata: direct-to-LDS, [BM][8 bytes]; one ds_read_b32 per fragment
+//    and k half gives the index operand;
+//  * B: each lane loads 4 rows x 8 columns (16-byte row loads, coalesced along
+//    n; for V:N:M the 4 rows are one group's selected rows), transposes them
+//    in registers and writes 8-byte k-runs to LDS laid out n-major ([BN][64 k]),
+//    16-byte chunks XOR-swizzled by (n + n/8) & 7 so that both the writes and
+//    the ds_read_b128 operand reads are conflict-free;
+//  * three LDS stages and two register sets for B: the loads of stages k+1
+//    and k+2 are in flight while stage k runs on the matrix cores (one wave
+//    per SIMD, accumulators in AGPRs, 128 x 128 per wave); B of stage k+1 is
+//    written to LDS after stage k's instructions.  All loads are issued from
+//    inline assembly and waited for with explicit vmcnt counts.
 // Epilogue: each (fragment, element) store covers 128 contiguous bytes of a
 // row of C (non-temporal: C is written once).
+#include <type_traits>
+
 #include "common.hpp"
 #include "dma.hpp"
 #include "launch.hpp"
 
 namespace nms {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+// B rows are loaded with inline-assembly loads as well: their completion is
+// counted by the same explicit vmcnt waits as the direct loads, and the wait
+// takes the destination registers as in/out operands, so nothing reads them
+// before the data has arrived.
+__device__ __forceinline__ u32x4 load16_async(const void* g) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(g));
+  return r;
+}
+template <int N, int NJ>
+__device__ __forceinline__ void wait_vmcnt_regs(u32x4 (&rb)[NJ][4]) {
+  static_assert(NJ == 1 || NJ == 2, "B register sets");
+  if constexpr (NJ == 1) {
+    asm volatile("s_waitcnt vmcnt(%4)" : "+v"(rb[0][0]), "+v"(rb[0][1]), "+v"(rb[0][2]), "+v"(rb[0][3]) : "n"(N) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(%8)"
+                 : "+v"(rb[0][0]), "+v"(rb[0][1]), "+v"(rb[0][2]), "+v"(rb[0][3]), "+v"(rb[1][0]), "+v"(rb[1][1]),
+                   "+v"(rb[1][2]), "+v"(rb[1][3])
+                 : "n"(N)
+                 : "memory");
+  }
+}
 
-// swizzle of the 16-byte chunk index of B row r
-__device__ __forceinline__ int bswz(int r) { return (r & 3) << 1; }
+// swizzled 16-byte chunk position of B row n (column n of the tile)
+__device__ __forceinline__ int bpos(int n, int chunk) { return chunk ^ ((n + (n >> 3)) & 7); }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
-struct DmaCfg {
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+struct SpCfg {
+  static constexpr int STAGES = 3;
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int A_BYTES = BM * 64;                  // 32 kept bf16 per row and stage
+  static constexpr int A_BYTES = BM * 64;        // 32 kept bf16 per row and stage
   static constexpr int M_BYTES = BM * 8;
-  static constexpr int B_ROW = BN * 2;                     // bytes per B row in LDS
-  static constexpr int B_BYTES = 64 * B_ROW;
+  static constexpr int B_BYTES = BN * 128;       // 64 k x 2 bytes per column
   static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
-  static constexpr int A_INSTR = A_BYTES / 1024 / NW;      // per wave and stage
-  static constexpr int M_LANES = M_BYTES / 4 / NW;          // one dword DMA per wave, M_LANES lanes active
-  static constexpr int B_INSTR = B_BYTES / 1024 / NW;
-  static constexpr int LOADS = A_INSTR + 1 + B_INSTR;      // vmcnt per stage per wave
+  static constexpr int A_INSTR = A_BYTES / 1024 / NW;   // direct loads per wave and stage
+  static constexpr int M_DW = M_BYTES / 4 / NW;         // metadata dwords per wave and stage
+  static constexpr int M_INSTR = M_DW > 64 ? M_DW / 64 : 1;
+  static constexpr int M_LANES = M_DW > 64 ? 64 : M_DW; // active lanes of each metadata direct load
+  static constexpr int B_JOBS = 16 * BN / 8 / NT;       // (4-row, 8-column) blocks per lane
+  static constexpr int L_A = A_INSTR + M_INSTR;         // vmcnt of a stage's direct loads
+  static constexpr int L_B = 4 * B_JOBS;                // vmcnt of a stage's B row loads
   static_assert(A_BYTES % (1024 * NW) == 0, "A blocks per wave");
-  static_assert(M_BYTES % (4 * NW) == 0 && M_LANES >= 1 && M_LANES <= 64, "metadata lanes per wave");
-  static_assert(B_BYTES % (1024 * NW) == 0 && (B_ROW % 1024 == 0 || 1024 % B_ROW == 0), "B blocks per wave");
-  static_assert(FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "fragments");
-  static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
-  static_assert(1024 % B_ROW != 0 || 1024 / B_ROW <= 4, "rows of one B DMA instruction share a group of 4");
+  static_assert(M_BYTES % (4 * NW) == 0 && M_DW >= 1 && (M_DW <= 64 || M_DW % 64 == 0), "metadata lanes per wave");
+  static_assert((16 * BN / 8) % NT == 0 && B_JOBS >= 1, "B blocks per lane");
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && FM >= 1 && FN >= 1, "fragments");
+  static_assert(2 * (L_A + L_B) <= 63, "vmcnt range");
   static_assert(STAGE * STAGES <= 160 * 1024, "LDS budget");
+  static_assert(BN == 256 && NT % 64 == 0, "a wave's B blocks span exactly two groups (BN/8 = 32 lanes each)");
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool VENOM>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VENOM>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
     const uint16_t* __restrict__ values, const uint8_t* __restrict__ meta, const uint8_t* __restrict__ colsel,
     int64_t R, int64_t Kd, int V, int M, int64_t G, const uint16_t* __restrict__ B, int64_t ldb, int64_t Nc,
     float* __restrict__ C, int64_t ldc) {
-  using Cfg = DmaCfg<BM, BN, WAVES_M, WAVES_N, STAGES>;
-  constexpr int FM = Cfg::FM, FN = Cfg::FN;
+  using Cfg = SpCfg<BM, BN, WAVES_M, WAVES_N>;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, STAGES = Cfg::STAGES, NJ = Cfg::B_JOBS;
   extern __shared__ __align__(1024) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -102,66 +129,90 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
   const int64_t vblk = VENOM ? m0 / V : 0;
   const uint32_t smem_base = lds_addr(smem);
 
-  // ---- per-lane DMA sources that do not depend on the stage ----
-  // A block q (q = wave*A_INSTR + t): 32-row fragment q/2, k half q%2; lane -> row 32*(q/2) + lane%32,
-  // 16-byte chunk 2*(q%2) + lane/32 of the stage's 64 bytes
+  // ---- direct-load sources (values, metadata) ----
   const uint16_t* a_src[Cfg::A_INSTR];
 #pragma unroll
   for (int t = 0; t < Cfg::A_INSTR; ++t) {
-    const int q = wave * Cfg::A_INSTR + t;
+    const int q = wave * Cfg::A_INSTR + t;       // block: fragment q/2, k half q%2
     int64_t row = m0 + 32 * (q >> 1) + (lane & 31);
     row = row < R ? row : R - 1;
     a_src[t] = values + row * vrow + 8 * (2 * (q & 1) + (lane >> 5));
   }
-  // metadata: wave w, lane l < M_LANES loads the dword at byte (w*M_LANES + l)*4 of the [BM][8] tile
-  const uint8_t* m_src;
-  {
-    const int o = (wave * Cfg::M_LANES + (lane < Cfg::M_LANES ? lane : 0)) * 4;
+  // metadata: instruction t of wave w loads dwords (w*M_INSTR + t)*M_LANES + lane of the [BM][8] tile
+  const uint8_t* m_src[Cfg::M_INSTR];
+#pragma unroll
+  for (int t = 0; t < Cfg::M_INSTR; ++t) {
+    const int o = ((wave * Cfg::M_INSTR + t) * Cfg::M_LANES + (lane < Cfg::M_LANES ? lane : 0)) * 4;
     int64_t row = m0 + (o >> 3);
     row = row < R ? row : R - 1;
-    m_src = meta + row * mrow + (o & 7);
-  }
-  // B: instruction q covers LDS bytes q*1024.. of the [64][BN] tile
-  int b_row[Cfg::B_INSTR];
-  int64_t b_col[Cfg::B_INSTR];
-#pragma unroll
-  for (int t = 0; t < Cfg::B_INSTR; ++t) {
-    const int q = wave * Cfg::B_INSTR + t;
-    const int byte = q * 1024 + lane * 16;
-    const int r = byte / Cfg::B_ROW;
-    const int p = (byte % Cfg::B_ROW) / 16;          // chunk position in the LDS row
-    const int c = p ^ bswz(r);                         // global chunk held there
-    int64_t col = n0 + 8 * c;
-    col = col < Nc ? col : 0;                          // columns past Nc: any valid data, never stored
-    b_row[t] = r;
-    b_col[t] = col;
+    m_src[t] = meta + row * mrow + (o & 7);
   }
 
-  auto issue = [&](int kt) {
-    const int buf = kt % STAGES;
-    const uint32_t st = smem_base + buf * Cfg::STAGE;
+  // ---- B blocks: job u = tid + NT*jj covers k rows 4*(u / (BN/8)) .. +3 (one group of 4),
+  //      columns 8*(u % (BN/8)) .. +7 ----
+  int b_kq[NJ];           // first k row of the block within the stage (multiple of 4)
+  int b_nb[NJ];           // first column within the tile (multiple of 8)
+  int64_t b_col[NJ];      // global column (clamped into the matrix)
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int u = tid + Cfg::NT * jj;
+    b_kq[jj] = 4 * (u / (BN / 8));
+    b_nb[jj] = 8 * (u % (BN / 8));
+    const int64_t col = n0 + b_nb[jj];
+    b_col[jj] = col < Nc ? col : 0;          // columns past Nc: any valid data, never stored
+  }
+
+  // direct loads of k-step kdata into the LDS buffer of stage `stage`
+  auto issue_direct = [&](int stage, int kdata) {
+    const uint32_t st = smem_base + (stage % STAGES) * Cfg::STAGE;
+    const int64_t k0 = (int64_t)kdata * 64;
+#pragma unroll
+    for (int t = 0; t < Cfg::A_INSTR; ++t) dma16(a_src[t] + k0 / 2, uniform(st + (wave * Cfg::A_INSTR + t) * 1024));
+#pragma unroll
+    for (int t = 0; t < Cfg::M_INSTR; ++t) {
+      const uint32_t dst = uniform(st + Cfg::A_BYTES + (wave * Cfg::M_INSTR + t) * Cfg::M_LANES * 4);
+      if (Cfg::M_LANES == 64 || lane < Cfg::M_LANES) dma4(m_src[t] + k0 / 8, dst);
+    }
+  };
+
+  auto load_b = [&](int kt, u32x4 (&rb)[NJ][4]) {
     const int64_t k0 = (int64_t)kt * 64;
 #pragma unroll
-    for (int t = 0; t < Cfg::A_INSTR; ++t)
-      dma16(a_src[t] + k0 / 2, uniform(st + (wave * Cfg::A_INSTR + t) * 1024));
-    {
-      // lanes >= M_LANES are masked off; the instruction still counts once in vmcnt
-      const uint32_t dst = uniform(st + Cfg::A_BYTES + wave * Cfg::M_LANES * 4);
-      if (Cfg::M_LANES == 64 || lane < Cfg::M_LANES) dma4(m_src + k0 / 8, dst);
-    }
-#pragma unroll
-    for (int t = 0; t < Cfg::B_INSTR; ++t) {
-      int64_t krow = k0 + b_row[t];
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int64_t kd = k0 + b_kq[jj];
+      int64_t rows[4] = {kd, kd + 1, kd + 2, kd + 3};
       if constexpr (VENOM) {
-        // every row of one DMA instruction lies in the same group of 4 selected
-        // columns, so the group's 4 column bytes are one wave-uniform (scalar) load
-        const int q = wave * Cfg::B_INSTR + t;
-        const int64_t g = (k0 + (q * 1024) / Cfg::B_ROW) >> 2;
-        const uint32_t sel4 = reinterpret_cast<const uint32_t*>(colsel)[vblk * G + g];
-        const uint32_t sel = (sel4 >> (8 * (krow & 3))) & (uint32_t)(M - 1);
-        krow = g * M + sel;
+        // the wave's lanes cover two consecutive groups (lanes 0-31 and 32-63):
+        // one wave-uniform (scalar) load of their 8 column bytes
+        const int64_t g = kd >> 2;
+        const int64_t g_first = (int64_t)__builtin_amdgcn_readfirstlane((int)(g - (lane >> 5)));
+        const uint32_t* cs = reinterpret_cast<const uint32_t*>(colsel) + vblk * G + g_first;
+        const uint32_t s0 = cs[0];
+        const uint32_t s1 = (g_first + 1 < G) ? cs[1] : s0;
+        const uint32_t sel = (lane >> 5) ? s1 : s0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rows[q] = g * M + ((sel >> (8 * q)) & (uint32_t)(M - 1));
       }
-      dma16(B + krow * ldb + b_col[t], uniform(st + Cfg::A_BYTES + Cfg::M_BYTES + (wave * Cfg::B_INSTR + t) * 1024));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rb[jj][q] = load16_async(B + rows[q] * ldb + b_col[jj]);
+    }
+  };
+
+  auto store_b = [&](int kt, const u32x4 (&rb)[NJ][4]) {
+    unsigned char* Bs = smem + (kt % STAGES) * Cfg::STAGE + Cfg::A_BYTES + Cfg::M_BYTES;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int chunk = b_kq[jj] >> 3, half = (b_kq[jj] >> 2) & 1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // column e of the 4 rows: low half = even row, high half = odd row
+        const uint32_t x0 = rb[jj][0][e >> 1], x1 = rb[jj][1][e >> 1];
+        const uint32_t x2 = rb[jj][2][e >> 1], x3 = rb[jj][3][e >> 1];
+        const uint32_t w0 = (e & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
+        const uint32_t w1 = (e & 1) ? ((x2 >> 16) | (x3 & 0xFFFF0000u)) : ((x2 & 0xFFFFu) | (x3 << 16));
+        const int n = b_nb[jj] + e;
+        *reinterpret_cast<u32x2*>(Bs + n * 128 + (bpos(n, chunk) << 4) + half * 8) = u32x2{w0, w1};
+      }
     }
   };
 
@@ -173,74 +224,74 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // per-lane LDS read offsets that do not depend on the stage
   const int l32 = lane & 31, aa = lane >> 5;
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int bb = g16 >> 1, half16 = g16 & 1;
-  // B transposing read: lane addresses row (kbase + i16/4), columns cb + 16*half16 + 4*(i16%4)
-  int b_off[FN][2][4];
-  constexpr int KOFF[4] = {0, 4, 16, 20};
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int r = 32 * h + 8 * bb + KOFF[e4] + (i16 >> 2);
-        const int cel = wn * Cfg::WN + 32 * j + 16 * half16 + 4 * (i16 & 3);
-        const int c = cel >> 3;
-        b_off[j][h][e4] = r * Cfg::B_ROW + ((c ^ bswz(r)) << 4) + ((cel & 7) << 1);
-      }
-
   auto compute = [&](int kt) {
-    const int buf = kt % STAGES;
-    const unsigned char* st = smem + buf * Cfg::STAGE;
+    const unsigned char* st = smem + (kt % STAGES) * Cfg::STAGE;
     const unsigned char* As = st;
     const unsigned char* Ms = st + Cfg::A_BYTES;
     const unsigned char* Bs = st + Cfg::A_BYTES + Cfg::M_BYTES;
-    uint32_t idx[FM][2];
-    bf16x8 a[FM][2];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int rf = wm * FM + i;  // 32-row fragment index within the tile
-      const u32x2 mm = *reinterpret_cast<const u32x2*>(Ms + (rf * 32 + l32) * 8);
-      idx[i][0] = aa ? (mm[0] >> 16) : mm[0];
-      idx[i][1] = aa ? (mm[1] >> 16) : mm[1];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) a[i][h] = *reinterpret_cast<const bf16x8*>(As + (rf * 2 + h) * 1024 + lane * 16);
-    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      uint32_t idx[FM];
+      bf16x8 a[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int rf = wm * FM + i;
+        idx[i] = *reinterpret_cast<const uint32_t*>(Ms + (rf * 32 + l32) * 8 + 4 * h) >> (16 * aa);
+        a[i] = *reinterpret_cast<const bf16x8*>(As + (rf * 2 + h) * 1024 + lane * 16);
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Bs + b_off[j][h][0]));
-        s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Bs + b_off[j][h][1]));
-        s16x4 p2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Bs + b_off[j][h][2]));
-        s16x4 p3 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Bs + b_off[j][h][3]));
-        typedef short s16x16 __attribute__((ext_vector_type(16)));
-        s16x16 bv = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7),
-                                            __builtin_shufflevector(p2, p3, 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2, 3, 4, 5,
-                                            6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-        const bf16x16 b = __builtin_bit_cast(bf16x16, bv);
+        const int n = wn * Cfg::WN + 32 * j + l32;
+        const unsigned char* row = Bs + n * 128;
+        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(row + (bpos(n, 4 * h + aa) << 4));
+        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(row + (bpos(n, 4 * h + 2 + aa) << 4));
+        const bf16x16 b = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a[i][h], b, acc[i][j], (int)idx[i][h], 0, 0);
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a[i], b, acc[i][j], (int)idx[i], 0, 0);
       }
     }
   };
 
   // ---- pipeline ----
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s);
-  for (int kt = 0; kt < KT; ++kt) {
-    // own loads of stage kt have landed when at most (stages issued after it) remain
-    if (kt + STAGES - 2 < KT) wait_vmcnt<Cfg::LOADS * (STAGES - 2)>();
-    else wait_vmcnt<0>();
-    barrier();   // every wave's stage-kt data is in LDS; every wave is done with stage kt-1
-    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-    compute(kt);
+  // Step kt: the B rows of stage kt+2 are loaded into the register set that
+  // held stage kt, the direct loads of stage kt+2 are issued, stage kt runs
+  // on the matrix cores, and then the B rows of stage kt+1 (loaded one step
+  // earlier) are transposed into LDS.  Loads complete in issue order, so
+  // waiting until only this step's loads are outstanding covers everything
+  // older.  Past the last k-step the loads repeat the last k-step into buffers
+  // that are never read again, which keeps every step (and every wait count)
+  // alike; a trailing odd step only skips its matrix instructions.
+  const int klast = KT - 1;
+  auto kc = [&](int k) { return k < klast ? k : klast; };
+  u32x4 rb0[NJ][4], rb1[NJ][4];
+  load_b(0, rb0);
+  issue_direct(0, 0);
+  load_b(kc(1), rb1);
+  issue_direct(1, kc(1));
+  wait_vmcnt_regs<Cfg::L_B + Cfg::L_A>(rb0);
+  store_b(0, rb0);
+  auto step = [&](int kt, auto parity, bool run) {
+    constexpr int P = decltype(parity)::value;
+    u32x4(&cur)[NJ][4] = P == 0 ? rb0 : rb1;   // stage kt (in LDS) -> reloaded with stage kt+2
+    u32x4(&nxt)[NJ][4] = P == 0 ? rb1 : rb0;   // stage kt+1
+    barrier();   // stage kt is in LDS for every wave; every wave is done with stage kt-1
+    load_b(kc(kt + 2), cur);
+    issue_direct(kt + 2, kc(kt + 2));
+    if (run) compute(kt);
+    wait_vmcnt_regs<Cfg::L_B + Cfg::L_A>(nxt);
+    store_b(kt + 1, nxt);
+  };
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{}, true);
+    step(kt + 1, std::integral_constant<int, 1>{}, kt + 1 < KT);
   }
+  // Drain: no load may land in LDS or in a register after this point.  Both
+  // register sets are operands of the wait, so neither can be reused before
+  // its (redundant) loads have arrived.
+  wait_vmcnt_regs<0>(rb0);
+  wait_vmcnt_regs<0>(rb1);
 
   // ---- epilogue ----
 #pragma unroll
@@ -257,13 +308,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool VENOM>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VENOM>
 static hipError_t run_dma(const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R, int64_t Kd,
                           int V, int M, int64_t G, const void* B, int64_t ldb, int64_t Nc, float* C, int64_t ldc,
                           hipStream_t s) {
-  using Cfg = DmaCfg<BM, BN, WAVES_M, WAVES_N, STAGES>;
-  const size_t lds = (size_t)Cfg::STAGE * STAGES;
-  auto kern = spmm_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, VENOM>;
+  using Cfg = SpCfg<BM, BN, WAVES_M, WAVES_N>;
+  const size_t lds = (size_t)Cfg::STAGE * Cfg::STAGES;
+  auto kern = spmm_dma_kernel<BM, BN, WAVES_M, WAVES_N, VENOM>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int64_t ntiles = ((R + BM - 1) / BM) * ((Nc + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg::NT), lds, s, (const uint16_t*)values, meta, colsel, R,
@@ -280,15 +331,15 @@ bool spmm_dma_ok(const void* values, const uint8_t* meta, const void* B, int64_t
 
 hipError_t launch_spmm_nm_dma(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* B,
                               int64_t ldb, int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
-  return run_dma<256, 256, 2, 4, 3, false>(values, meta, nullptr, R, K, 4, 4, K / 4, B, ldb, Nc, C, ldc, s);
+  return run_dma<256, 256, 2, 2, false>(values, meta, nullptr, R, K, 4, 4, K / 4, B, ldb, Nc, C, ldc, s);
 }
 
 hipError_t launch_spmm_venom_dma(const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R,
                                  int64_t Kd, int V, int M, int64_t G, const void* B, int64_t ldb, int64_t Nc,
                                  float* C, int64_t ldc, hipStream_t s) {
   if (V % 128 == 0)
-    return run_dma<128, 256, 2, 4, 3, true>(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
-  return run_dma<64, 256, 1, 4, 3, true>(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
+    return run_dma<128, 256, 1, 4, true>(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
+  return run_dma<64, 256, 1, 4, true>(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
 }
 
 }  // namespace nms
