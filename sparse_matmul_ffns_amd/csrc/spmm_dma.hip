@@ -72,30 +72,32 @@ __device__ __forceinline__ int bpos(int n, int chunk) { return chunk ^ ((n + (n 
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 struct SpCfg {
-  static constexpr int STAGES = 3;
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int A_BYTES = BM * 64;        // 32 kept bf16 per row and stage
-  static constexpr int M_BYTES = BM * 8;
-  static constexpr int B_BYTES = BN * 128;       // 64 k x 2 bytes per column
-  static constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;
-  static constexpr int A_INSTR = A_BYTES / 1024 / NW;   // direct loads per wave and stage
-  static constexpr int M_DW = M_BYTES / 4 / NW;         // metadata dwords per wave and stage
-  static constexpr int M_INSTR = M_DW > 64 ? M_DW / 64 : 1;
-  static constexpr int M_LANES = M_DW > 64 ? 64 : M_DW; // active lanes of each metadata direct load
-  static constexpr int B_JOBS = 16 * BN / 8 / NT;       // (4-row, 8-column) blocks per lane
-  static constexpr int L_A = A_INSTR + M_INSTR;         // vmcnt of a stage's direct loads
-  static constexpr int L_B = 4 * B_JOBS;                // vmcnt of a stage's B row loads
-  static_assert(A_BYTES % (1024 * NW) == 0, "A blocks per wave");
-  static_assert(M_BYTES % (4 * NW) == 0 && M_DW >= 1 && (M_DW <= 64 || M_DW % 64 == 0), "metadata lanes per wave");
+  // A super-stage = two 64-k steps: 64 kept bf16 (128 bytes) and 16 metadata bytes per row
+  static constexpr int AV_BYTES = BM * 128;
+  static constexpr int AM_BYTES = BM * 16;
+  static constexpr int A_STAGE = AV_BYTES + AM_BYTES;
+  static constexpr int B_STAGE = BN * 128;          // 64 k x 2 bytes per column
+  static constexpr int LDS = 2 * A_STAGE + 2 * B_STAGE;
+  static constexpr int AV_INSTR = AV_BYTES / 1024 / NW;   // 1 KB (8 rows) per direct load
+  static constexpr int AM_LANES = BM / NW;               // one 16-byte metadata row per lane
+  static constexpr int B_JOBS = 16 * BN / 8 / NT;        // (4-row, 8-column) B blocks per lane and step
+  static constexpr int L_A = AV_INSTR + 1;               // vmcnt of a super-stage's direct loads
+  static constexpr int L_B = 4 * B_JOBS;                 // vmcnt of a step's B row loads
+  static_assert(AV_BYTES % (1024 * NW) == 0 && AV_INSTR >= 1, "A blocks per wave");
+  static_assert(AM_LANES >= 1 && AM_LANES <= 64 && BM % NW == 0, "metadata lanes per wave");
   static_assert((16 * BN / 8) % NT == 0 && B_JOBS >= 1, "B blocks per lane");
   static_assert(WM % 32 == 0 && WN % 32 == 0 && FM >= 1 && FN >= 1, "fragments");
-  static_assert(2 * (L_A + L_B) <= 63, "vmcnt range");
-  static_assert(STAGE * STAGES <= 160 * 1024, "LDS budget");
+  static_assert(L_A + L_B <= 63, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(BN == 256 && NT % 64 == 0, "a wave's B blocks span exactly two groups (BN/8 = 32 lanes each)");
 };
+
+// 16-byte chunk position of chunk c in A row r (rows are 128 bytes = 8 chunks)
+__device__ __forceinline__ int apos(int r, int c) { return c ^ (r & 7); }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool VENOM>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
     int64_t R, int64_t Kd, int V, int M, int64_t G, const uint16_t* __restrict__ B, int64_t ldb, int64_t Nc,
     float* __restrict__ C, int64_t ldc) {
   using Cfg = SpCfg<BM, BN, WAVES_M, WAVES_N>;
-  constexpr int FM = Cfg::FM, FN = Cfg::FN, STAGES = Cfg::STAGES, NJ = Cfg::B_JOBS;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN, NJ = Cfg::B_JOBS;
   extern __shared__ __align__(1024) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -124,33 +126,44 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
   const int64_t vrow = Kd / 2;     // values per row
-  const int64_t mrow = Kd / 8;     // metadata bytes per row (Kd % 64 == 0)
-  const int KT = (int)(Kd / 64);
+  const int64_t mrow = Kd / 8;     // metadata bytes per row
+  const int KT = (int)(Kd / 64);   // 64-k steps (even: Kd % 128 == 0)
   const int64_t vblk = VENOM ? m0 / V : 0;
   const uint32_t smem_base = lds_addr(smem);
+  unsigned char* const a_lds = smem;                          // 2 A super-stages
+  unsigned char* const b_lds = smem + 2 * Cfg::A_STAGE;       // 2 B steps
 
-  // ---- direct-load sources (values, metadata) ----
-  const uint16_t* a_src[Cfg::A_INSTR];
+  // ---- direct-load sources of a super-stage ----
+  // values: instruction q covers rows 8q..8q+7; lane -> row 8q + lane/8, LDS chunk lane%8 holding
+  // the row's 16-byte chunk (lane%8) ^ (row & 7)
+  const uint16_t* a_src[Cfg::AV_INSTR];
 #pragma unroll
-  for (int t = 0; t < Cfg::A_INSTR; ++t) {
-    const int q = wave * Cfg::A_INSTR + t;       // block: fragment q/2, k half q%2
-    int64_t row = m0 + 32 * (q >> 1) + (lane & 31);
+  for (int t = 0; t < Cfg::AV_INSTR; ++t) {
+    const int r = 8 * (wave * Cfg::AV_INSTR + t) + (lane >> 3);
+    int64_t row = m0 + r;
     row = row < R ? row : R - 1;
-    a_src[t] = values + row * vrow + 8 * (2 * (q & 1) + (lane >> 5));
+    a_src[t] = values + row * vrow + 8 * apos(r, lane & 7);
   }
-  // metadata: instruction t of wave w loads dwords (w*M_INSTR + t)*M_LANES + lane of the [BM][8] tile
-  const uint8_t* m_src[Cfg::M_INSTR];
+  // metadata: lane l < AM_LANES of wave w loads the 16 bytes of row w*AM_LANES + l
+  const uint8_t* m_src;
+  {
+    int64_t row = m0 + wave * Cfg::AM_LANES + (lane < Cfg::AM_LANES ? lane : 0);
+    row = row < R ? row : R - 1;
+    m_src = meta + row * mrow;
+  }
+  // super-stage j (k-steps 2j, 2j+1) into A buffer `buf`
+  auto issue_a = [&](int buf, int j) {
+    const uint32_t st = smem_base + buf * Cfg::A_STAGE;
 #pragma unroll
-  for (int t = 0; t < Cfg::M_INSTR; ++t) {
-    const int o = ((wave * Cfg::M_INSTR + t) * Cfg::M_LANES + (lane < Cfg::M_LANES ? lane : 0)) * 4;
-    int64_t row = m0 + (o >> 3);
-    row = row < R ? row : R - 1;
-    m_src[t] = meta + row * mrow + (o & 7);
-  }
+    for (int t = 0; t < Cfg::AV_INSTR; ++t)
+      dma16(a_src[t] + (int64_t)j * 64, uniform(st + (wave * Cfg::AV_INSTR + t) * 1024));
+    const uint32_t dst = uniform(st + Cfg::AV_BYTES + wave * Cfg::AM_LANES * 16);
+    if (Cfg::AM_LANES == 64 || lane < Cfg::AM_LANES) dma16(m_src + (int64_t)j * 16, dst);
+  };
 
   // ---- B blocks: job u = tid + NT*jj covers k rows 4*(u / (BN/8)) .. +3 (one group of 4),
   //      columns 8*(u % (BN/8)) .. +7 ----
-  int b_kq[NJ];           // first k row of the block within the stage (multiple of 4)
+  int b_kq[NJ];           // first k row of the block within the step (multiple of 4)
   int b_nb[NJ];           // first column within the tile (multiple of 8)
   int64_t b_col[NJ];      // global column (clamped into the matrix)
 #pragma unroll
@@ -161,19 +174,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
     const int64_t col = n0 + b_nb[jj];
     b_col[jj] = col < Nc ? col : 0;          // columns past Nc: any valid data, never stored
   }
-
-  // direct loads of k-step kdata into the LDS buffer of stage `stage`
-  auto issue_direct = [&](int stage, int kdata) {
-    const uint32_t st = smem_base + (stage % STAGES) * Cfg::STAGE;
-    const int64_t k0 = (int64_t)kdata * 64;
-#pragma unroll
-    for (int t = 0; t < Cfg::A_INSTR; ++t) dma16(a_src[t] + k0 / 2, uniform(st + (wave * Cfg::A_INSTR + t) * 1024));
-#pragma unroll
-    for (int t = 0; t < Cfg::M_INSTR; ++t) {
-      const uint32_t dst = uniform(st + Cfg::A_BYTES + (wave * Cfg::M_INSTR + t) * Cfg::M_LANES * 4);
-      if (Cfg::M_LANES == 64 || lane < Cfg::M_LANES) dma4(m_src[t] + k0 / 8, dst);
-    }
-  };
 
   auto load_b = [&](int kt, u32x4 (&rb)[NJ][4]) {
     const int64_t k0 = (int64_t)kt * 64;
@@ -198,8 +198,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
     }
   };
 
-  auto store_b = [&](int kt, const u32x4 (&rb)[NJ][4]) {
-    unsigned char* Bs = smem + (kt % STAGES) * Cfg::STAGE + Cfg::A_BYTES + Cfg::M_BYTES;
+  // B rows of a step, transposed, into B buffer `buf` ([BN][64 k], swizzled 16-byte chunks)
+  auto store_b = [&](int buf, const u32x4 (&rb)[NJ][4]) {
+    unsigned char* Bs = b_lds + buf * Cfg::B_STAGE;
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       const int chunk = b_kq[jj] >> 3, half = (b_kq[jj] >> 2) & 1;
@@ -225,20 +226,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int l32 = lane & 31, aa = lane >> 5;
+  // step kt: A super-stage buffer (kt/2)%2, half s = kt%2; B buffer kt%2
   auto compute = [&](int kt) {
-    const unsigned char* st = smem + (kt % STAGES) * Cfg::STAGE;
-    const unsigned char* As = st;
-    const unsigned char* Ms = st + Cfg::A_BYTES;
-    const unsigned char* Bs = st + Cfg::A_BYTES + Cfg::M_BYTES;
+    const int s = kt & 1;
+    const unsigned char* As = a_lds + ((kt >> 1) & 1) * Cfg::A_STAGE;
+    const unsigned char* Ms = As + Cfg::AV_BYTES;
+    const unsigned char* Bs = b_lds + (kt & 1) * Cfg::B_STAGE;
+    u32x2 mm[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) mm[i] = *reinterpret_cast<const u32x2*>(Ms + ((wm * FM + i) * 32 + l32) * 16 + 8 * s);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t idx[FM];
       bf16x8 a[FM];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int rf = wm * FM + i;
-        idx[i] = *reinterpret_cast<const uint32_t*>(Ms + (rf * 32 + l32) * 8 + 4 * h) >> (16 * aa);
-        a[i] = *reinterpret_cast<const bf16x8*>(As + (rf * 2 + h) * 1024 + lane * 16);
+        const int r = (wm * FM + i) * 32 + l32;
+        idx[i] = mm[i][h] >> (16 * aa);
+        a[i] = *reinterpret_cast<const bf16x8*>(As + r * 128 + (apos(r, 4 * s + 2 * h + aa) << 4));
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -255,37 +260,35 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
   };
 
   // ---- pipeline ----
-  // Step kt: the B rows of stage kt+2 are loaded into the register set that
-  // held stage kt, the direct loads of stage kt+2 are issued, stage kt runs
-  // on the matrix cores, and then the B rows of stage kt+1 (loaded one step
-  // earlier) are transposed into LDS.  Loads complete in issue order, so
-  // waiting until only this step's loads are outstanding covers everything
-  // older.  Past the last k-step the loads repeat the last k-step into buffers
-  // that are never read again, which keeps every step (and every wait count)
-  // alike; a trailing odd step only skips its matrix instructions.
-  const int klast = KT - 1;
+  // Even step kt = 2j: load the B rows of step kt+2, issue super-stage j+1 (k-steps kt+2, kt+3)
+  // into the other A buffer, run step kt, then (once only this step's loads are outstanding)
+  // transpose B of step kt+1 into LDS.  Odd step: load B of step kt+2, run step kt, and wait
+  // for everything but this step's B loads -- which includes super-stage j+1 -- before storing
+  // B of step kt+1.  Loads complete in issue order.  Past the end, loads repeat the last
+  // step / super-stage into buffers that are never read again, so every step looks alike.
+  const int klast = KT - 1, jlast = KT / 2 - 1;
   auto kc = [&](int k) { return k < klast ? k : klast; };
   u32x4 rb0[NJ][4], rb1[NJ][4];
+  issue_a(0, 0);
   load_b(0, rb0);
-  issue_direct(0, 0);
   load_b(kc(1), rb1);
-  issue_direct(1, kc(1));
-  wait_vmcnt_regs<Cfg::L_B + Cfg::L_A>(rb0);
+  wait_vmcnt_regs<Cfg::L_B>(rb0);     // super-stage 0 and B of step 0 have landed
   store_b(0, rb0);
-  auto step = [&](int kt, auto parity, bool run) {
-    constexpr int P = decltype(parity)::value;
-    u32x4(&cur)[NJ][4] = P == 0 ? rb0 : rb1;   // stage kt (in LDS) -> reloaded with stage kt+2
-    u32x4(&nxt)[NJ][4] = P == 0 ? rb1 : rb0;   // stage kt+1
-    barrier();   // stage kt is in LDS for every wave; every wave is done with stage kt-1
-    load_b(kc(kt + 2), cur);
-    issue_direct(kt + 2, kc(kt + 2));
-    if (run) compute(kt);
-    wait_vmcnt_regs<Cfg::L_B + Cfg::L_A>(nxt);
-    store_b(kt + 1, nxt);
-  };
   for (int kt = 0; kt < KT; kt += 2) {
-    step(kt, std::integral_constant<int, 0>{}, true);
-    step(kt + 1, std::integral_constant<int, 1>{}, kt + 1 < KT);
+    const int j = kt >> 1;
+    // even step kt
+    barrier();   // step kt's A and B are in LDS for every wave; every wave is done with step kt-1
+    load_b(kc(kt + 2), rb0);
+    issue_a((j + 1) & 1, j + 1 < jlast ? j + 1 : jlast);
+    compute(kt);
+    wait_vmcnt_regs<Cfg::L_B + Cfg::L_A>(rb1);
+    store_b(1, rb1);
+    // odd step kt+1
+    barrier();
+    load_b(kc(kt + 3), rb1);
+    compute(kt + 1);
+    wait_vmcnt_regs<Cfg::L_B>(rb0);
+    store_b(0, rb0);
   }
   // Drain: no load may land in LDS or in a register after this point.  Both
   // register sets are operands of the wait, so neither can be reused before
@@ -313,7 +316,7 @@ static hipError_t run_dma(const void* values, const uint8_t* meta, const uint8_t
                           int V, int M, int64_t G, const void* B, int64_t ldb, int64_t Nc, float* C, int64_t ldc,
                           hipStream_t s) {
   using Cfg = SpCfg<BM, BN, WAVES_M, WAVES_N>;
-  const size_t lds = (size_t)Cfg::STAGE * Cfg::STAGES;
+  const size_t lds = (size_t)Cfg::LDS;
   auto kern = spmm_dma_kernel<BM, BN, WAVES_M, WAVES_N, VENOM>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int64_t ntiles = ((R + BM - 1) / BM) * ((Nc + BN - 1) / BN);
@@ -322,11 +325,11 @@ static hipError_t run_dma(const void* values, const uint8_t* meta, const uint8_t
   return hipGetLastError();
 }
 
-// Conditions: bf16, 64-element k-steps without a tail, 16-byte loads of
-// values and B rows, 4-byte metadata loads.
+// Conditions: bf16, whole 128-k super-stages, 16-byte loads of values,
+// metadata (16 bytes per row and super-stage) and B rows.
 bool spmm_dma_ok(const void* values, const uint8_t* meta, const void* B, int64_t ldb, int64_t Nc, int64_t Kd) {
-  return Kd % 64 == 0 && Kd >= 64 && Nc % 8 == 0 && ldb % 8 == 0 && (uintptr_t)values % 16 == 0 &&
-         (uintptr_t)meta % 4 == 0 && (uintptr_t)B % 16 == 0;
+  return Kd % 128 == 0 && Kd >= 128 && Nc % 8 == 0 && ldb % 8 == 0 && (uintptr_t)values % 16 == 0 &&
+         (uintptr_t)meta % 16 == 0 && (uintptr_t)B % 16 == 0;
 }
 
 hipError_t launch_spmm_nm_dma(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* B,
