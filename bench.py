@@ -211,12 +211,24 @@ def cpu_baseline(name):
 # counters recorded with rocprofv3 (profiles/), valid while the kernel source is unchanged
 # ---------------------------------------------------------------------------
 
+# sources whose code runs in each kernel: a change to any of them voids recorded counters
+_KERNEL_SOURCES = {
+    "spmm_nm": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp", "launch.hpp"],
+    "spmm_venom": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp", "launch.hpp"],
+    "sddmm_nm": ["sddmm.hip", "common.hpp", "dma.hpp", "launch.hpp"],
+    "prune_act_venom": ["venom.hip", "common.hpp", "launch.hpp"],
+}
+
+
 def _src_hash(kernel):
-    src = {"spmm_nm": "spmm.hip", "spmm_venom": "spmm.hip", "sddmm_nm": "sddmm.hip"}.get(kernel)
-    if src is None:
+    srcs = _KERNEL_SOURCES.get(kernel)
+    if srcs is None:
         return None
-    with open(os.path.join(ROOT, "sparse_matmul_ffns_amd", "csrc", src), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in srcs:
+        with open(os.path.join(ROOT, "sparse_matmul_ffns_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic(workload, kernel):
