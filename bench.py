@@ -18,6 +18,9 @@ A step is one pass of the hot path over the workload's synthetic inputs
 pruned zeros counted as if dense).  The JSON line also carries the roofline
 of the step's dominant kernel, timed with HIP events on the stream it runs on,
 and the fp64 CPU oracle timed on the host (rank 0, N = 1 only).
+
+Warm-up: the W untimed steps are repeated until at least one second of them
+has run, so that the timed steps see settled GPU clocks.
 """
 
 from __future__ import annotations
@@ -37,6 +40,7 @@ import numpy as np  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
+WARMUP_MIN_S = 1.0            # minimum warm-up wall time (see main)
 METRIC = "dense-equivalent TFLOP/s of 2:4 & V:N:M SpMM at FFN shapes; % of bf16 MFMA peak"
 
 
@@ -266,9 +270,17 @@ def main():
     steps, flops, algo, dominant = build_workload(args.workload)
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
+    # W untimed warm-up steps, continued until at least WARMUP_MIN_S of them have run: from idle the
+    # GPU needs a few hundred milliseconds of load before its clocks settle, and steps timed
+    # earlier run up to 20% slower
+    t_w = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
         for _, fn in steps:
             fn()
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -307,6 +319,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": done,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

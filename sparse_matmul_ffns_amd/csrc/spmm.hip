@@ -372,7 +372,7 @@ hipError_t launch_spmm_venom(int dt, const void* values, const uint8_t* meta, co
   const int64_t G = K / M;
   const int64_t Kd = G * 4;  // the 2:4 domain: 4 selected columns per group
   if (dt == DT_BF16 && !force_generic() && kernel_tier() == 0 && spmm_dma_ok(values, meta, B, ldb, Nc, Kd) &&
-      (uintptr_t)colsel % 4 == 0 && V % 64 == 0)
+      (uintptr_t)colsel % 16 == 0 && V % 64 == 0)
     return launch_spmm_venom_dma(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
   if (dt == DT_BF16 && !force_generic() && fast_ok(values, meta, B, ldb, Nc, C, ldc, Kd) &&
       (uintptr_t)colsel % 4 == 0) {

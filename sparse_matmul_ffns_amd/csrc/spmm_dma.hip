@@ -18,22 +18,25 @@
 //    the B operand is transposed in registers on its way into LDS and read
 //    back with ds_read_b128.
 //
-// Data flow per workgroup (BM x BN tile of C, 64 dense k per stage):
-//  * values: direct-to-LDS, one 1 KB block per (32-row fragment, 32-k half)
-//    in instruction lane order: every A operand read is one conflict-free
-//    ds_read_b128 at block + 16*lane;
-//  * metadata: direct-to-LDS, [BM][8 bytes]; one ds_read_b32 per fragment
-//    and k half gives the index operand;
-//  * B: each lane loads 4 rows x 8 columns (16-byte row loads, coalesced along
-//    n; for V:N:M the 4 rows are one group's selected rows), transposes them
-//    in registers and writes 8-byte k-runs to LDS laid out n-major ([BN][64 k]),
-//    16-byte chunks XOR-swizzled by (n + n/8) & 7 so that both the writes and
-//    the ds_read_b128 operand reads are conflict-free;
-//  * three LDS stages and two register sets for B: the loads of stages k+1
-//    and k+2 are in flight while stage k runs on the matrix cores (one wave
-//    per SIMD, accumulators in AGPRs, 128 x 128 per wave); B of stage k+1 is
-//    written to LDS after stage k's instructions.  All loads are issued from
-//    inline assembly and waited for with explicit vmcnt counts.
+// Data flow per workgroup (BM x BN tile of C, 64 dense k per step):
+//  * values: direct-to-LDS, two steps (128 bytes of every row) at a time, as
+//    whole rows, the 16-byte chunks of a row XOR-swizzled (apos) so that the
+//    A operand reads -- one ds_read_b128 per fragment and 32-k half -- hit 16
+//    distinct bank groups per 16 lanes;
+//  * metadata: direct-to-LDS, 16 bytes per row and super-stage; one ds_read_b64
+//    per fragment and step gives the index operands of both 32-k halves;
+//  * B: each lane loads 8 rows x 8 columns (16-byte row loads, coalesced along
+//    n; for V:N:M the 8 rows are two groups' selected rows), transposes them in
+//    registers with v_perm and writes 16-byte k-runs to LDS laid out n-major
+//    ([BN][64 k]), chunks swizzled by (n + n/8) & 7 (bpos); half of the lanes
+//    write their columns in swapped pairs so that both the writes and the
+//    ds_read_b128 operand reads are free of bank conflicts;
+//  * two LDS buffers for B, two A super-stages, and two register sets for B:
+//    the B loads of steps k+1 and k+2 are in flight while step k runs on the
+//    matrix cores (one wave per SIMD, accumulators in AGPRs, 128 x 128 per wave
+//    for 2:4); B of step k+1 is written to LDS after step k's instructions.
+//    All loads are issued from inline assembly and waited for with explicit
+//    vmcnt counts.
 // Epilogue: each (fragment, element) store covers 128 contiguous bytes of a
 // row of C (non-temporal: C is written once).
 #include <type_traits>
@@ -53,18 +56,22 @@ __device__ __forceinline__ u32x4 load16_async(const void* g) {
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(g));
   return r;
 }
-template <int N, int NJ>
-__device__ __forceinline__ void wait_vmcnt_regs(u32x4 (&rb)[NJ][4]) {
-  static_assert(NJ == 1 || NJ == 2, "B register sets");
-  if constexpr (NJ == 1) {
-    asm volatile("s_waitcnt vmcnt(%4)" : "+v"(rb[0][0]), "+v"(rb[0][1]), "+v"(rb[0][2]), "+v"(rb[0][3]) : "n"(N) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(%8)"
-                 : "+v"(rb[0][0]), "+v"(rb[0][1]), "+v"(rb[0][2]), "+v"(rb[0][3]), "+v"(rb[1][0]), "+v"(rb[1][1]),
-                   "+v"(rb[1][2]), "+v"(rb[1][3])
-                 : "n"(N)
-                 : "memory");
-  }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_regs(u32x4 (&rb)[8]) {
+  asm volatile("s_waitcnt vmcnt(%8)"
+               : "+v"(rb[0]), "+v"(rb[1]), "+v"(rb[2]), "+v"(rb[3]), "+v"(rb[4]), "+v"(rb[5]), "+v"(rb[6]),
+                 "+v"(rb[7])
+               : "n"(N)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_regs(u32x4 (&r0)[8], u32x4 (&r1)[8]) {
+  asm volatile("s_waitcnt vmcnt(%16)"
+               : "+v"(r0[0]), "+v"(r0[1]), "+v"(r0[2]), "+v"(r0[3]), "+v"(r0[4]), "+v"(r0[5]), "+v"(r0[6]),
+                 "+v"(r0[7]), "+v"(r1[0]), "+v"(r1[1]), "+v"(r1[2]), "+v"(r1[3]), "+v"(r1[4]), "+v"(r1[5]),
+                 "+v"(r1[6]), "+v"(r1[7])
+               : "n"(N)
+               : "memory");
 }
 
 // swizzled 16-byte chunk position of B row n (column n of the tile)
@@ -84,20 +91,21 @@ struct SpCfg {
   static constexpr int LDS = 2 * A_STAGE + 2 * B_STAGE;
   static constexpr int AV_INSTR = AV_BYTES / 1024 / NW;   // 1 KB (8 rows) per direct load
   static constexpr int AM_LANES = BM / NW;               // one 16-byte metadata row per lane
-  static constexpr int B_JOBS = 16 * BN / 8 / NT;        // (4-row, 8-column) B blocks per lane and step
+  static constexpr int B_ROWS = 8;                      // each lane: 8 k rows x 8 columns of B per step
   static constexpr int L_A = AV_INSTR + 1;               // vmcnt of a super-stage's direct loads
-  static constexpr int L_B = 4 * B_JOBS;                 // vmcnt of a step's B row loads
+  static constexpr int L_B = B_ROWS;                     // vmcnt of a step's B row loads
   static_assert(AV_BYTES % (1024 * NW) == 0 && AV_INSTR >= 1, "A blocks per wave");
   static_assert(AM_LANES >= 1 && AM_LANES <= 64 && BM % NW == 0, "metadata lanes per wave");
-  static_assert((16 * BN / 8) % NT == 0 && B_JOBS >= 1, "B blocks per lane");
+  static_assert(8 * (BN / 8) == NT, "one (8 k x 8 column) B block per lane: 8 chunks x BN/8 column blocks");
   static_assert(WM % 32 == 0 && WN % 32 == 0 && FM >= 1 && FN >= 1, "fragments");
   static_assert(L_A + L_B <= 63, "vmcnt range");
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert(BN == 256 && NT % 64 == 0, "a wave's B blocks span exactly two groups (BN/8 = 32 lanes each)");
+  static_assert(BN == 256 && NW == 4, "a wave's B blocks: two 8-k chunks (lanes 0-31, 32-63) of 32 column blocks");
 };
 
-// 16-byte chunk position of chunk c in A row r (rows are 128 bytes = 8 chunks)
-__device__ __forceinline__ int apos(int r, int c) { return c ^ (r & 7); }
+// 16-byte chunk position of chunk c in A row r (rows are 128 bytes = 8 chunks).  16 consecutive
+// rows read at one chunk index land on 16 distinct 16-byte bank groups (two rows per 256 bytes).
+__device__ __forceinline__ int apos(int r, int c) { return c ^ ((r + (r >> 3)) & 7); }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool VENOM>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
     int64_t R, int64_t Kd, int V, int M, int64_t G, const uint16_t* __restrict__ B, int64_t ldb, int64_t Nc,
     float* __restrict__ C, int64_t ldc) {
   using Cfg = SpCfg<BM, BN, WAVES_M, WAVES_N>;
-  constexpr int FM = Cfg::FM, FN = Cfg::FN, NJ = Cfg::B_JOBS;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN;
   extern __shared__ __align__(1024) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -161,59 +169,55 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
     if (Cfg::AM_LANES == 64 || lane < Cfg::AM_LANES) dma16(m_src + (int64_t)j * 16, dst);
   };
 
-  // ---- B blocks: job u = tid + NT*jj covers k rows 4*(u / (BN/8)) .. +3 (one group of 4),
-  //      columns 8*(u % (BN/8)) .. +7 ----
-  int b_kq[NJ];           // first k row of the block within the step (multiple of 4)
-  int b_nb[NJ];           // first column within the tile (multiple of 8)
-  int64_t b_col[NJ];      // global column (clamped into the matrix)
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
-    const int u = tid + Cfg::NT * jj;
-    b_kq[jj] = 4 * (u / (BN / 8));
-    b_nb[jj] = 8 * (u % (BN / 8));
-    const int64_t col = n0 + b_nb[jj];
-    b_col[jj] = col < Nc ? col : 0;          // columns past Nc: any valid data, never stored
-  }
+  // ---- B: lane l of wave w owns k chunk bc = 2w + l/32 (k = 8bc .. 8bc+7 of the step) and
+  //      column block bcb = l%32 (columns 8bcb .. 8bcb+7 of the tile) ----
+  const int bc = 2 * wave + (lane >> 5);
+  const int bcb = lane & 31;
+  int64_t b_col = n0 + 8 * bcb;
+  b_col = b_col < Nc ? b_col : 0;          // columns past Nc: any valid data, never stored
 
-  auto load_b = [&](int kt, u32x4 (&rb)[NJ][4]) {
+  auto load_b = [&](int kt, u32x4 (&rb)[8]) {
     const int64_t k0 = (int64_t)kt * 64;
+    int64_t rows[8];
+    if constexpr (VENOM) {
+      // 16 groups per step; the wave's lanes cover groups 4w .. 4w+3 (two per chunk): one
+      // wave-uniform (scalar) load of their 16 column bytes.  k0 + 64 <= Kd, so all 16 exist.
+      const int64_t g_first = (k0 >> 2) + 4 * wave;
+      const u32x4 sel4 = *reinterpret_cast<const u32x4*>(colsel + 4 * (vblk * G + g_first));
+      const uint32_t s_lo = (lane >> 5) ? sel4[2] : sel4[0];
+      const uint32_t s_hi = (lane >> 5) ? sel4[3] : sel4[1];
+      const int64_t g = g_first + 2 * (lane >> 5);
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int64_t kd = k0 + b_kq[jj];
-      int64_t rows[4] = {kd, kd + 1, kd + 2, kd + 3};
-      if constexpr (VENOM) {
-        // the wave's lanes cover two consecutive groups (lanes 0-31 and 32-63):
-        // one wave-uniform (scalar) load of their 8 column bytes
-        const int64_t g = kd >> 2;
-        const int64_t g_first = (int64_t)__builtin_amdgcn_readfirstlane((int)(g - (lane >> 5)));
-        const uint32_t* cs = reinterpret_cast<const uint32_t*>(colsel) + vblk * G + g_first;
-        const uint32_t s0 = cs[0];
-        const uint32_t s1 = (g_first + 1 < G) ? cs[1] : s0;
-        const uint32_t sel = (lane >> 5) ? s1 : s0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) rows[q] = g * M + ((sel >> (8 * q)) & (uint32_t)(M - 1));
+      for (int q = 0; q < 4; ++q) {
+        rows[q] = g * M + ((s_lo >> (8 * q)) & (uint32_t)(M - 1));
+        rows[q + 4] = (g + 1) * M + ((s_hi >> (8 * q)) & (uint32_t)(M - 1));
       }
+    } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) rb[jj][q] = load16_async(B + rows[q] * ldb + b_col[jj]);
+      for (int q = 0; q < 8; ++q) rows[q] = k0 + 8 * bc + q;
     }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) rb[q] = load16_async(B + rows[q] * ldb + b_col);
   };
 
-  // B rows of a step, transposed, into B buffer `buf` ([BN][64 k], swizzled 16-byte chunks)
-  auto store_b = [&](int buf, const u32x4 (&rb)[NJ][4]) {
+  // B rows of a step, transposed, into B buffer `buf` ([BN][64 k], 16-byte chunks swizzled by bpos).
+  // Write slot e stores one column's 8 k values (chunk bc) with one ds_write_b128; lanes with
+  // bit 3 set write column e^1 in slot e, so every 16 lanes of a write cover both column parities
+  // and 16 distinct bank groups.  v_perm picks the even or odd bf16 of each row pair.
+  const int bflip = (lane >> 3) & 1;
+  const uint32_t sel_lo = 0x05040100u, sel_hi = 0x07060302u;
+  const uint32_t sel_even = bflip ? sel_hi : sel_lo, sel_odd = bflip ? sel_lo : sel_hi;
+  auto store_b = [&](int buf, const u32x4 (&rb)[8]) {
     unsigned char* Bs = b_lds + buf * Cfg::B_STAGE;
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int chunk = b_kq[jj] >> 3, half = (b_kq[jj] >> 2) & 1;
+    for (int e = 0; e < 8; ++e) {
+      const int p = e >> 1;
+      const uint32_t sel = (e & 1) ? sel_odd : sel_even;
+      u32x4 d;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // column e of the 4 rows: low half = even row, high half = odd row
-        const uint32_t x0 = rb[jj][0][e >> 1], x1 = rb[jj][1][e >> 1];
-        const uint32_t x2 = rb[jj][2][e >> 1], x3 = rb[jj][3][e >> 1];
-        const uint32_t w0 = (e & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
-        const uint32_t w1 = (e & 1) ? ((x2 >> 16) | (x3 & 0xFFFF0000u)) : ((x2 & 0xFFFFu) | (x3 << 16));
-        const int n = b_nb[jj] + e;
-        *reinterpret_cast<u32x2*>(Bs + n * 128 + (bpos(n, chunk) << 4) + half * 8) = u32x2{w0, w1};
-      }
+      for (int j = 0; j < 4; ++j) d[j] = __builtin_amdgcn_perm(rb[2 * j + 1][p], rb[2 * j][p], sel);
+      const int n = 8 * bcb + (e ^ bflip);
+      *reinterpret_cast<u32x4*>(Bs + n * 128 + (bpos(n, bc) << 4)) = d;
     }
   };
 
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
   // step / super-stage into buffers that are never read again, so every step looks alike.
   const int klast = KT - 1, jlast = KT / 2 - 1;
   auto kc = [&](int k) { return k < klast ? k : klast; };
-  u32x4 rb0[NJ][4], rb1[NJ][4];
+  u32x4 rb0[8], rb1[8];
   issue_a(0, 0);
   load_b(0, rb0);
   load_b(kc(1), rb1);
@@ -293,8 +297,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
   // Drain: no load may land in LDS or in a register after this point.  Both
   // register sets are operands of the wait, so neither can be reused before
   // its (redundant) loads have arrived.
-  wait_vmcnt_regs<0>(rb0);
-  wait_vmcnt_regs<0>(rb1);
+  wait_vmcnt_regs<0>(rb0, rb1);
 
   // ---- epilogue ----
 #pragma unroll
