@@ -103,9 +103,10 @@ struct SpCfg {
   static_assert(BN == 256 && NW == 4, "a wave's B blocks: two 8-k chunks (lanes 0-31, 32-63) of 32 column blocks");
 };
 
-// 16-byte chunk position of chunk c in A row r (rows are 128 bytes = 8 chunks).  16 consecutive
-// rows read at one chunk index land on 16 distinct 16-byte bank groups (two rows per 256 bytes).
-__device__ __forceinline__ int apos(int r, int c) { return c ^ ((r + (r >> 3)) & 7); }
+// 16-byte chunk position of chunk c in A row r (rows are 128 bytes = 8 chunks).  The two rows
+// of a 256-byte LDS line share one XOR, consecutive lines take distinct ones: with this choice
+// (measured on gfx950) 16 consecutive rows read at one chunk index are free of bank conflicts.
+__device__ __forceinline__ int apos(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool VENOM>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
@@ -230,24 +231,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int l32 = lane & 31, aa = lane >> 5;
-  // step kt: A super-stage buffer (kt/2)%2, half s = kt%2; B buffer kt%2
-  auto compute = [&](int kt) {
+  // Step kt: A super-stage buffer (kt/2)%2, half s = kt%2; B buffer kt%2.  The B rows of step kt+1
+  // (register set rbs, waited for by `wait`) are transposed into B buffer (kt+1)%2 while the
+  // matrix instructions of step kt run: the operand reads of both 32-k halves are issued first,
+  // then the first half's 16 instructions are interleaved with the transposes and LDS writes.
+  auto step = [&](int kt, const u32x4 (&rbs)[8], auto wait) {
     const int s = kt & 1;
     const unsigned char* As = a_lds + ((kt >> 1) & 1) * Cfg::A_STAGE;
     const unsigned char* Ms = As + Cfg::AV_BYTES;
     const unsigned char* Bs = b_lds + (kt & 1) * Cfg::B_STAGE;
     u32x2 mm[FM];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) mm[i] = *reinterpret_cast<const u32x2*>(Ms + ((wm * FM + i) * 32 + l32) * 16 + 8 * s);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t idx[FM];
-      bf16x8 a[FM];
+    uint32_t idx[2][FM];
+    bf16x8 a[2][FM];
+    bf16x16 b[2][FN];
+    auto operands = [&](int h) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = (wm * FM + i) * 32 + l32;
-        idx[i] = mm[i][h] >> (16 * aa);
-        a[i] = *reinterpret_cast<const bf16x8*>(As + r * 128 + (apos(r, 4 * s + 2 * h + aa) << 4));
+        idx[h][i] = mm[i][h] >> (16 * aa);
+        a[h][i] = *reinterpret_cast<const bf16x8*>(As + r * 128 + (apos(r, 4 * s + 2 * h + aa) << 4));
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -255,21 +257,33 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
         const unsigned char* row = Bs + n * 128;
         const bf16x8 lo = *reinterpret_cast<const bf16x8*>(row + (bpos(n, 4 * h + aa) << 4));
         const bf16x8 hi = *reinterpret_cast<const bf16x8*>(row + (bpos(n, 4 * h + 2 + aa) << 4));
-        const bf16x16 b = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+        b[h][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      }
+    };
+    auto mfma = [&](int h) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a[i], b, acc[i][j], (int)idx[i], 0, 0);
-      }
-    }
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a[h][i], b[h][j], acc[i][j], (int)idx[h][i], 0, 0);
+    };
+#pragma unroll
+    for (int i = 0; i < FM; ++i) mm[i] = *reinterpret_cast<const u32x2*>(Ms + ((wm * FM + i) * 32 + l32) * 16 + 8 * s);
+    operands(0);
+    operands(1);
+    wait();
+    mfma(0);
+    store_b((kt + 1) & 1, rbs);
+    mfma(1);
   };
 
   // ---- pipeline ----
   // Even step kt = 2j: load the B rows of step kt+2, issue super-stage j+1 (k-steps kt+2, kt+3)
-  // into the other A buffer, run step kt, then (once only this step's loads are outstanding)
-  // transpose B of step kt+1 into LDS.  Odd step: load B of step kt+2, run step kt, and wait
-  // for everything but this step's B loads -- which includes super-stage j+1 -- before storing
-  // B of step kt+1.  Loads complete in issue order.  Past the end, loads repeat the last
-  // step / super-stage into buffers that are never read again, so every step looks alike.
+  // into the other A buffer, wait until only these loads are outstanding (so B of step kt+1 has
+  // landed) and run step kt.  Odd step: load B of step kt+2, wait for everything but these loads
+  // -- which includes super-stage j+1 -- and run step kt.  Loads complete in issue order.  Past
+  // the end, loads repeat the last step / super-stage into buffers that are never read again,
+  // so every step looks alike.
   const int klast = KT - 1, jlast = KT / 2 - 1;
   auto kc = [&](int k) { return k < klast ? k : klast; };
   u32x4 rb0[8], rb1[8];
@@ -284,15 +298,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
     barrier();   // step kt's A and B are in LDS for every wave; every wave is done with step kt-1
     load_b(kc(kt + 2), rb0);
     issue_a((j + 1) & 1, j + 1 < jlast ? j + 1 : jlast);
-    compute(kt);
-    wait_vmcnt_regs<Cfg::L_B + Cfg::L_A>(rb1);
-    store_b(1, rb1);
+    step(kt, rb1, [&]() { wait_vmcnt_regs<Cfg::L_B + Cfg::L_A>(rb1); });
     // odd step kt+1
     barrier();
     load_b(kc(kt + 3), rb1);
-    compute(kt + 1);
-    wait_vmcnt_regs<Cfg::L_B>(rb0);
-    store_b(0, rb0);
+    step(kt + 1, rb0, [&]() { wait_vmcnt_regs<Cfg::L_B>(rb0); });
   }
   // Drain: no load may land in LDS or in a register after this point.  Both
   // register sets are operands of the wait, so neither can be reused before
