@@ -28,8 +28,8 @@
 //  * B: each lane loads 8 rows x 8 columns (16-byte row loads, coalesced along
 //    n; for V:N:M the 8 rows are two groups' selected rows), transposes them in
 //    registers with v_perm and writes 16-byte k-runs to LDS laid out n-major
-//    ([BN][64 k]), chunks swizzled by (n + n/8) & 7 (bpos); half of the lanes
-//    write their columns in swapped pairs so that both the writes and the
+//    ([BN][64 k]), chunks XOR-swizzled by row (bpos); half of the lanes write
+//    their columns in swapped pairs, so that both the writes and the
 //    ds_read_b128 operand reads are free of bank conflicts;
 //  * two LDS buffers for B, two A super-stages, and two register sets for B:
 //    the B loads of steps k+1 and k+2 are in flight while step k runs on the
@@ -74,8 +74,11 @@ __device__ __forceinline__ void wait_vmcnt_regs(u32x4 (&r0)[8], u32x4 (&r1)[8]) 
                : "memory");
 }
 
-// swizzled 16-byte chunk position of B row n (column n of the tile)
-__device__ __forceinline__ int bpos(int n, int chunk) { return chunk ^ ((n + (n >> 3)) & 7); }
+// Swizzled 16-byte chunk position of chunk c in B row n (the LDS row of tile column n).  Chosen
+// by measurement on gfx950: with it, 16 consecutive rows read at one chunk index, and the
+// transposing writes (16 lanes writing columns 8b + (e ^ ((b >> 3) & 1)) of consecutive blocks
+// b at one chunk), are both free of LDS bank conflicts.
+__device__ __forceinline__ int bpos(int n, int chunk) { return chunk ^ (((n >> 1) ^ (n >> 4)) & 7); }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 struct SpCfg {
