@@ -45,19 +45,26 @@ __device__ inline int rank_of(const uint32_t (&k)[M], int p) {
   return r;
 }
 
-// 2:4 selection on four keys: returns the nibble p0 | p1 << 2 (p0 < p1).
+// 2:4 selection on four keys: returns the nibble p0 | p1 << 2 (p0 < p1) of the two positions
+// with rank < 2 under rank_of.  Each key is extended by its position, (k << 2) | (3 - p), so
+// that the extended keys are distinct and order exactly like rank_of (larger key first, then
+// lower position); the two largest extended keys are found with three max/min pairs.
+template <typename K>
+__device__ inline uint32_t select24_ext(K c0, K c1, K c2, K c3) {
+  const K m01 = c0 > c1 ? c0 : c1, n01 = c0 > c1 ? c1 : c0;
+  const K m23 = c2 > c3 ? c2 : c3, n23 = c2 > c3 ? c3 : c2;
+  const K t1 = m01 > m23 ? m01 : m23;
+  const K lo = m01 > m23 ? m23 : m01, hi_n = n01 > n23 ? n01 : n23;
+  const K t2 = lo > hi_n ? lo : hi_n;
+  const uint32_t pa = 3u - (uint32_t)(t1 & 3), pb = 3u - (uint32_t)(t2 & 3);
+  const uint32_t p0 = pa < pb ? pa : pb, p1 = pa < pb ? pb : pa;
+  return p0 | (p1 << 2);
+}
 __device__ inline uint32_t select24(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3) {
-  uint32_t k[4] = {k0, k1, k2, k3};
-  uint32_t nib = 0;
-  int s = 0;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    if (rank_of<4>(k, p) < 2) {
-      nib |= (uint32_t)p << (2 * s);
-      ++s;
-    }
-  }
-  return nib;
+  if ((k0 | k1 | k2 | k3) < (1u << 30))
+    return select24_ext<uint32_t>((k0 << 2) | 3u, (k1 << 2) | 2u, (k2 << 2) | 1u, k3 << 2);
+  return select24_ext<uint64_t>(((uint64_t)k0 << 2) | 3u, ((uint64_t)k1 << 2) | 2u, ((uint64_t)k2 << 2) | 1u,
+                                (uint64_t)k3 << 2);
 }
 
 __device__ inline int ceil_log2(int m) {

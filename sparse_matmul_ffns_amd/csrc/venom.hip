@@ -33,54 +33,97 @@ __device__ inline int rank_f64(const double (&k)[M], int p) {
   return r;
 }
 
+// Chunks of 16 bytes per thread and tile on the streaming path (a 64 KB tile, 256 threads).
+constexpr int kStreamChunks = 16;
+
 template <typename T, int M>
 __global__ __launch_bounds__(256) void venom_prune_kernel(const T* __restrict__ Z, int64_t ldz, int64_t K, int V,
                                                           int relu, int CW, T* __restrict__ values,
                                                           uint8_t* __restrict__ meta, uint8_t* __restrict__ colsel,
                                                           uint8_t* __restrict__ mask, int64_t ldmask, int vec_in,
-                                                          int vec_out) {
+                                                          int vec_out, int ntx, int64_t ntiles, int stream) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int EPC = 16 / sizeof(T);       // elements per 16-byte chunk
   const int tid = threadIdx.x;
-  const int64_t blk = blockIdx.x;
-  const int64_t c0 = (int64_t)blockIdx.y * CW;
   const int64_t G = K / M;
-  const int cols = (int)((K - c0) < CW ? (K - c0) : CW);  // valid columns in this tile (multiple of M)
-  const int ngr = cols / M;                                // valid groups
-  const int pitch = CW;                                    // elements per LDS row
-
+  const int pitch = CW + 8;   // elements per LDS row: 16 bytes of padding spread the rows over the banks
   T* tile = reinterpret_cast<T*>(smem);
-  double* l1 = reinterpret_cast<double*>(smem + (size_t)V * CW * sizeof(T));
+  double* l1 = reinterpret_cast<double*>(smem + (size_t)V * pitch * sizeof(T));
   uint8_t* csel = reinterpret_cast<uint8_t*>(l1 + CW);
-
-  // 1. stage the tile (ReLU'd) in LDS
   const int cpr = CW / EPC;
-  const T* zb = Z + blk * V * ldz + c0;
-  for (int i = tid; i < V * cpr; i += 256) {
-    const int r = i / cpr, ch = i - r * cpr;
-    const int c = ch * EPC;
-    T x[EPC];
-    if (vec_in && c + EPC <= cols) {
-      u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(zb + (int64_t)r * ldz + c));
-      __builtin_memcpy(x, &t, 16);
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) x[e] = (c + e < cols) ? zb[(int64_t)r * ldz + c + e] : (T)0;
-    }
+  const int nch = V * cpr;
+
+  auto relu_chunk = [&](u32x4 t) {
     if (relu) {
+      T x[EPC];
+      __builtin_memcpy(x, &t, 16);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) x[e] = Elem<T>::positive(x[e]) ? x[e] : (T)0;
+      __builtin_memcpy(&t, x, 16);
     }
-    u32x4 t;
-    __builtin_memcpy(&t, x, 16);
-    *reinterpret_cast<u32x4*>(tile + r * pitch + c) = t;
+    return t;
+  };
+  // streaming path: full aligned 64 KB tiles; the next tile's chunks are loaded into registers
+  // while the current tile is ranked and written out
+  u32x4 pre[kStreamChunks];
+  auto load_tile = [&](int64_t t) {
+    const int64_t b = t / ntx;
+    const T* zb = Z + b * V * ldz + (t - b * ntx) * CW;
+#pragma unroll
+    for (int u = 0; u < kStreamChunks; ++u) {
+      const int i = tid + 256 * u;
+      const int r = i / cpr, c = (i - r * cpr) * EPC;
+      pre[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(zb + (int64_t)r * ldz + c));
+    }
+  };
+  if (stream && (int64_t)blockIdx.x < ntiles) load_tile(blockIdx.x);
+
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  const int64_t blk = t / ntx;
+  const int64_t c0 = (t - blk * ntx) * CW;
+  const int cols = (int)((K - c0) < CW ? (K - c0) : CW);  // valid columns in this tile (multiple of M)
+  const int ngr = cols / M;                                // valid groups
+
+  // 1. stage the tile (ReLU'd) in LDS
+  if (stream) {
+#pragma unroll
+    for (int u = 0; u < kStreamChunks; ++u) {
+      const int i = tid + 256 * u;
+      const int r = i / cpr, c = (i - r * cpr) * EPC;
+      *reinterpret_cast<u32x4*>(tile + r * pitch + c) = relu_chunk(pre[u]);
+    }
+    if (t + gridDim.x < ntiles) load_tile(t + gridDim.x);
+  } else {
+    const T* zb = Z + blk * V * ldz + c0;
+    for (int i = tid; i < nch; i += 256) {
+      const int r = i / cpr, c = (i - r * cpr) * EPC;
+      u32x4 v;
+      if (vec_in && c + EPC <= cols) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(zb + (int64_t)r * ldz + c));
+      } else {
+        T x[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) x[e] = (c + e < cols) ? zb[(int64_t)r * ldz + c + e] : (T)0;
+        __builtin_memcpy(&v, x, 16);
+      }
+      *reinterpret_cast<u32x4*>(tile + r * pitch + c) = relu_chunk(v);
+    }
   }
   __syncthreads();
 
-  // 2. block column L1 norms, fp64, rows in ascending order
+  // 2. block column L1 norms, fp64, rows in ascending order: LDS values fetched 8 rows at a
+  //    time, added one by one
   for (int c = tid; c < cols; c += 256) {
     double acc = 0.0;
-    for (int r = 0; r < V; ++r) acc += (double)fabsf(Elem<T>::to_f32(tile[r * pitch + c]));
+    int r = 0;
+    for (; r + 8 <= V; r += 8) {
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = fabsf(Elem<T>::to_f32(tile[(r + k) * pitch + c]));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += (double)x[k];
+    }
+    for (; r < V; ++r) acc += (double)fabsf(Elem<T>::to_f32(tile[r * pitch + c]));
     l1[c] = acc;
   }
   __syncthreads();
@@ -160,14 +203,20 @@ __global__ __launch_bounds__(256) void venom_prune_kernel(const T* __restrict__ 
       for (int e = 0; e < 2 * gq; ++e) vd[e] = v[e];
     }
     uint8_t* md = meta + row * meta_row + gglob / 2;
-    md[0] = (uint8_t)(nibs & 0xFF);
-    if (gq > 2) md[1] = (uint8_t)((nibs >> 8) & 0xFF);
+    if (gq > 2 && ((uintptr_t)md & 1) == 0) {
+      *reinterpret_cast<uint16_t*>(md) = (uint16_t)(nibs & 0xFFFF);
+    } else {
+      md[0] = (uint8_t)(nibs & 0xFF);
+      if (gq > 2) md[1] = (uint8_t)((nibs >> 8) & 0xFF);
+    }
     if (mask) {
       uint8_t* mk = mask + row * ldmask + c0 + 4 * q * M;
       for (int gi = 0; gi < gq; ++gi)
 #pragma unroll
         for (int p = 0; p < M; ++p) mk[gi * M + p] = msk[gi][p];
     }
+  }
+  __syncthreads();   // every thread is done with the tile before the next one is staged
   }
 }
 
@@ -180,14 +229,18 @@ static hipError_t venom_dispatch(const void* Z, int64_t ldz, int64_t R, int64_t 
   CW = (CW / 64) * 64;
   if (CW > 512) CW = 512;
   if (CW < 64) CW = 64;
-  const size_t lds = (size_t)V * CW * esz + (size_t)CW * sizeof(double) + (size_t)(CW / 4) * 4 + 64;
+  const size_t lds = (size_t)V * (CW + 8) * esz + (size_t)CW * sizeof(double) + (size_t)(CW / 4) * 4 + 64;
   const int vec_in = ((uintptr_t)Z % 16 == 0) && ((ldz * esz) % 16 == 0);
   const int vec_out = ((uintptr_t)values % 16 == 0) && (((K / M) * 2 * esz) % 16 == 0);
-  dim3 grid((unsigned)(R / V), (unsigned)((K + CW - 1) / CW));
+  const int ntx = (int)((K + CW - 1) / CW);
+  const int64_t ntiles = (R / V) * (int64_t)ntx;
+  const int stream = vec_in && K % CW == 0 && (int64_t)V * (CW / (16 / esz)) == 256 * kStreamChunks;
+  // streaming path: two resident workgroups per CU walk the tiles; otherwise one workgroup per tile
+  const int64_t grid = stream ? (ntiles < 512 ? ntiles : 512) : ntiles;
   auto run = [&](auto kern) {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, (const T*)Z, ldz, K, V, relu, CW, (T*)values, meta, colsel,
-                       mask, ldmask, vec_in, vec_out);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, (const T*)Z, ldz, K, V, relu, CW, (T*)values,
+                       meta, colsel, mask, ldmask, vec_in, vec_out, ntx, ntiles, stream);
     return hipGetLastError();
   };
   switch (M) {
