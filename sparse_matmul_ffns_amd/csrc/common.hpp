@@ -60,11 +60,32 @@ __device__ inline uint32_t select24_ext(K c0, K c1, K c2, K c3) {
   const uint32_t p0 = pa < pb ? pa : pb, p1 = pa < pb ? pb : pa;
   return p0 | (p1 << 2);
 }
+// 32-bit extended keys: the largest and second largest of c0..c3 (the second largest of four is
+// the median of {max(c0,c1,c2), med(c0,c1,c2), c3}); the compiler maps these to the 3-input
+// max / median instructions.
+__device__ inline uint32_t umax2(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ inline uint32_t umin2(uint32_t a, uint32_t b) { return a < b ? a : b; }
+__device__ inline uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  return umax2(umin2(a, b), umin2(umax2(a, b), c));
+}
+__device__ inline uint32_t select24_ext32(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+  const uint32_t m3 = umax2(umax2(c0, c1), c2);
+  const uint32_t d3 = umed3(c0, c1, c2);
+  const uint32_t t1 = umax2(m3, c3);
+  const uint32_t t2 = umed3(m3, d3, c3);
+  const uint32_t pa = (~t1) & 3u, pb = (~t2) & 3u;
+  const uint32_t p0 = pa < pb ? pa : pb, p1 = pa < pb ? pb : pa;
+  return p0 | (p1 << 2);
+}
 __device__ inline uint32_t select24(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3) {
   if ((k0 | k1 | k2 | k3) < (1u << 30))
-    return select24_ext<uint32_t>((k0 << 2) | 3u, (k1 << 2) | 2u, (k2 << 2) | 1u, k3 << 2);
+    return select24_ext32((k0 << 2) | 3u, (k1 << 2) | 2u, (k2 << 2) | 1u, k3 << 2);
   return select24_ext<uint64_t>(((uint64_t)k0 << 2) | 3u, ((uint64_t)k1 << 2) | 2u, ((uint64_t)k2 << 2) | 1u,
                                 (uint64_t)k3 << 2);
+}
+// The same selection on four raw bf16 patterns (the sign bit is shifted out of the key).
+__device__ inline uint32_t select24_bf16(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  return select24_ext32((b0 << 17) | 3u, (b1 << 17) | 2u, (b2 << 17) | 1u, b3 << 17);
 }
 
 __device__ inline int ceil_log2(int m) {

@@ -156,6 +156,47 @@ __global__ __launch_bounds__(256) void venom_prune_kernel(const T* __restrict__ 
   // 4. per row, 2 of the 4 selected columns of each group
   const int nq = (ngr + 3) / 4;
   const int64_t meta_row = (G + 1) / 2;
+  if (sizeof(T) == 2 && !mask && vec_out && ngr % 4 == 0 && 256 % nq == 0) {
+    // Fast path: a lane keeps one quad of groups (q) for the whole tile and walks rows; the LDS
+    // offsets of its 16 selected columns are computed once.
+    const int q = tid % nq, rstep = 256 / nq;
+    int ofs[4][4];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int g = 4 * q + gi;
+      const uint32_t cs = *reinterpret_cast<const uint32_t*>(csel + 4 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ofs[gi][j] = g * M + (int)((cs >> (8 * j)) & 0xFF);
+    }
+    const int64_t gglob = c0 / M + 4 * q;
+    for (int r = tid / nq; r < V; r += rstep) {
+      const uint16_t* trow = reinterpret_cast<const uint16_t*>(tile) + r * pitch;
+      uint32_t out[4];
+      uint32_t nibs = 0;
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        uint32_t x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = trow[ofs[gi][j]];
+        const uint32_t nib = select24_bf16(x[0], x[1], x[2], x[3]);
+        const uint32_t d01 = x[0] | (x[1] << 16), d23 = x[2] | (x[3] << 16);
+        const uint32_t j0 = nib & 3, j1 = nib >> 2;
+        // bytes 2j, 2j+1 of the pair (d23:d01) hold value j
+        const uint32_t sel = (j0 * 0x202u + 0x100u) | ((j1 * 0x202u + 0x100u) << 16);
+        out[gi] = __builtin_amdgcn_perm(d23, d01, sel);
+        nibs |= nib << (4 * gi);
+      }
+      const int64_t row = blk * V + r;
+      *reinterpret_cast<u32x4*>(values + row * (G * 2) + gglob * 2) = u32x4{out[0], out[1], out[2], out[3]};
+      uint8_t* md = meta + row * meta_row + gglob / 2;
+      if (((uintptr_t)md & 1) == 0) {
+        *reinterpret_cast<uint16_t*>(md) = (uint16_t)nibs;
+      } else {
+        md[0] = (uint8_t)(nibs & 0xFF);
+        md[1] = (uint8_t)(nibs >> 8);
+      }
+    }
+  } else
   for (int u = tid; u < V * nq; u += 256) {
     const int r = u / nq, q = u - r * nq;
     const int64_t row = blk * V + r;

@@ -171,12 +171,18 @@ def test_prune_act_venom(R, K, V, M, relu, dtype):
     mean = -0.5 if relu else 0.0
     raw = synth.normal((R, K), R + K + V, mean=mean, dtype=dtype)
     raw[: min(R, V), :M] = synth.tie_rich((min(R, V), M), 1, dtype=dtype)   # ties in one group
-    vals, meta, colsel, mask = nm.prune_act_venom(dev(raw, dtype), V, M, apply_relu=relu, want_mask=True)
+    Z = dev(raw, dtype)
+    vals, meta, colsel, mask = nm.prune_act_venom(Z, V, M, apply_relu=relu, want_mask=True)
     wv, wm, wc, wmask, _ = O.prune_venom(raw, dtype, V, M, relu)
     assert np.array_equal(host(colsel), wc)
     assert host(vals).tobytes() == wv.tobytes()
     assert np.array_equal(host(meta), wm)
     assert np.array_equal(host(mask), wmask)
+    # without the mask output the kernel takes its row-streaming selection path where it applies
+    vals, meta, colsel = nm.prune_act_venom(Z, V, M, apply_relu=relu)
+    assert np.array_equal(host(colsel), wc)
+    assert host(vals).tobytes() == wv.tobytes()
+    assert np.array_equal(host(meta), wm)
 
 
 SPMM_VENOM_CASES = [(256, 1024, 264, 64, 8), (384, 512, 136, 128, 8), (48, 96, 40, 3, 16), (128, 136, 64, 64, 8),
