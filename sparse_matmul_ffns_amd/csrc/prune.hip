@@ -71,6 +71,53 @@ __global__ __launch_bounds__(256) void nm_prune_kernel(const T* __restrict__ A, 
 }
 
 // ---------------------------------------------------------------------------
+// nm_prune, 2:4 with 16-byte rows: each thread owns kPruneU 16-byte chunks (one group of four
+// fp32 or two groups of bf16 each), all loaded before any is ranked, so that a thread keeps
+// several loads in flight; the 2:4 choice is the extended-key network of select24.  I is the
+// chunk index type (32-bit whenever the matrix has fewer than 2^32 chunks).
+// ---------------------------------------------------------------------------
+constexpr int kPruneU = 4;
+
+template <typename T, typename I>
+__global__ __launch_bounds__(256) void nm_prune24_vec_kernel(const T* __restrict__ A, int64_t lda, int64_t R,
+                                                             int64_t K, uint8_t* __restrict__ mask,
+                                                             int64_t ldmask) {
+  constexpr int EPC = 16 / (int)sizeof(T);          // elements per chunk: 8 (bf16) or 4 (fp32)
+  const I per_row = (I)(K / EPC);
+  const I total = (I)R * per_row;
+  const I base = (I)blockIdx.x * (256 * kPruneU) + threadIdx.x;
+  u32x4 x[kPruneU];
+  I rr[kPruneU], cc[kPruneU];
+#pragma unroll
+  for (int u = 0; u < kPruneU; ++u) {
+    const I cid = base + 256 * u;
+    rr[u] = cid / per_row;
+    cc[u] = (cid - rr[u] * per_row) * EPC;
+    if (cid < total)
+      x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(A + (int64_t)rr[u] * lda + cc[u]));
+  }
+#pragma unroll
+  for (int u = 0; u < kPruneU; ++u) {
+    if (base + 256 * u >= total) break;
+    uint8_t* m = mask + (int64_t)rr[u] * ldmask + cc[u];
+    if constexpr (sizeof(T) == 2) {
+      uint32_t mw[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t lo = x[u][2 * g], hi = x[u][2 * g + 1];
+        const uint32_t nib = select24_bf16(lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16);
+        mw[g] = (1u << (8 * (nib & 3))) | (1u << (8 * (nib >> 2)));
+      }
+      *reinterpret_cast<u32x2*>(m) = u32x2{mw[0], mw[1]};
+    } else {
+      const uint32_t nib = select24(x[u][0] & 0x7FFFFFFFu, x[u][1] & 0x7FFFFFFFu, x[u][2] & 0x7FFFFFFFu,
+                                    x[u][3] & 0x7FFFFFFFu);
+      *reinterpret_cast<uint32_t*>(m) = (1u << (8 * (nib & 3))) | (1u << (8 * (nib >> 2)));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Bit-stream writer/reader for the packed positions of one row segment that
 // starts on a byte boundary.
 // ---------------------------------------------------------------------------
@@ -183,63 +230,66 @@ __global__ __launch_bounds__(256) void nm_compress_kernel(const T* __restrict__ 
 // (4 groups): 16-byte loads of A and mask, one 16- or 32-byte store of the 8
 // kept values and one 2-byte store of their 4 nibbles.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, typename I>
 __global__ __launch_bounds__(256) void nm_compress24_vec_kernel(const T* __restrict__ A, int64_t lda,
                                                                 const uint8_t* __restrict__ mask, int64_t ldmask,
                                                                 int64_t R, int64_t K, T* __restrict__ values,
                                                                 uint8_t* __restrict__ meta, int32_t* bad_groups) {
-  const int64_t per_row = K / 16;
-  const int64_t cid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int bad = 0;
-  if (cid < R * per_row) {
-    const int64_t r = cid / per_row;
-    const int64_t c0 = (cid - r * per_row) * 16;
-    T x[16];
-    uint8_t m[16];
-    const u32x4* a4 = reinterpret_cast<const u32x4*>(A + r * lda + c0);
+  // each thread: kCompressU chunks of 16 elements (4 groups), all loaded before any is packed
+  constexpr int kCompressU = 2;
+  constexpr int NA = (int)sizeof(T);               // 16-byte loads of A per chunk (16 elements)
+  const I per_row = (I)(K / 16);
+  const I total = (I)R * per_row;
+  const I base = (I)blockIdx.x * (256 * kCompressU) + threadIdx.x;
+  u32x4 xa[kCompressU][NA], xm[kCompressU];
+  I rr[kCompressU], cc[kCompressU];
 #pragma unroll
-    for (int i = 0; i < 16 * (int)sizeof(T) / 16; ++i) {
-      u32x4 t = __builtin_nontemporal_load(a4 + i);
-      __builtin_memcpy(&x[i * 16 / sizeof(T)], &t, 16);
+  for (int u = 0; u < kCompressU; ++u) {
+    const I cid = base + 256 * u;
+    rr[u] = cid / per_row;
+    cc[u] = (cid - rr[u] * per_row) * 16;
+    if (cid < total) {
+      const u32x4* a4 = reinterpret_cast<const u32x4*>(A + (int64_t)rr[u] * lda + cc[u]);
+#pragma unroll
+      for (int q = 0; q < NA; ++q) xa[u][q] = __builtin_nontemporal_load(a4 + q);
+      xm[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(mask + (int64_t)rr[u] * ldmask + cc[u]));
     }
-    {
-      u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(mask + r * ldmask + c0));
-      __builtin_memcpy(m, &t, 16);
-    }
-    T v[8];
+  }
+  int bad = 0;
+#pragma unroll
+  for (int u = 0; u < kCompressU; ++u) {
+    if (base + 256 * u >= total) break;
+    const int64_t r = rr[u], c0 = cc[u];
+    uint32_t out[2 * NA];   // the 8 kept values of the chunk, packed
     uint32_t nibs = 0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      int cnt = 0;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) cnt += m[4 * g + p] ? 1 : 0;
-      uint32_t nib = 0;
-      T v0 = (T)0, v1 = (T)0;
-      if (cnt == 2) {
-        int s = 0;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          if (m[4 * g + p]) {
-            if (s == 0) v0 = x[4 * g + p]; else v1 = x[4 * g + p];
-            nib |= (uint32_t)p << (2 * s);
-            ++s;
-          }
-        }
+      // kept flags of the group as 4 bits: bit p set iff mask byte p is nonzero
+      const uint32_t m32 = xm[u][g];
+      const uint32_t nz = ((((m32 & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | m32) & 0x80808080u) >> 7;
+      const uint32_t bits = (nz * 0x01020408u) >> 24;
+      const bool ok = __builtin_popcount(bits) == 2;
+      const uint32_t p0 = __builtin_ctz(bits | 0x10u) & 3u, p1 = (31 - __builtin_clz(bits | 1u)) & 3u;
+      if (!ok) ++bad;
+      // a group without exactly two survivors: positions 0 and 1, values +0.0
+      nibs |= (ok ? (p0 | (p1 << 2)) : 0x4u) << (4 * g);
+      if constexpr (sizeof(T) == 2) {
+        // bytes 2p, 2p+1 of the pair (d23:d01) hold the group's value p
+        const uint32_t d01 = xa[u][g >> 1][(g & 1) * 2], d23 = xa[u][g >> 1][(g & 1) * 2 + 1];
+        const uint32_t sel = (p0 * 0x202u + 0x100u) | ((p1 * 0x202u + 0x100u) << 16);
+        out[g] = ok ? __builtin_amdgcn_perm(d23, d01, sel) : 0u;
       } else {
-        ++bad;
-        nib = 0x4;  // positions 0 and 1, values +0.0
+        const u32x4 q = xa[u][g];
+        auto pick = [&](uint32_t p) { return p == 0 ? q[0] : p == 1 ? q[1] : p == 2 ? q[2] : q[3]; };
+        out[2 * g] = ok ? pick(p0) : 0u;
+        out[2 * g + 1] = ok ? pick(p1) : 0u;
       }
-      v[2 * g] = v0;
-      v[2 * g + 1] = v1;
-      nibs |= nib << (4 * g);
     }
     T* vd = values + r * (K / 2) + c0 / 2;
 #pragma unroll
-    for (int i = 0; i < 8 * (int)sizeof(T) / 16; ++i) {
-      u32x4 t;
-      __builtin_memcpy(&t, &v[i * 16 / sizeof(T)], 16);
-      __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(vd) + i);
-    }
+    for (int q = 0; q < NA / 2; ++q)
+      __builtin_nontemporal_store(u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]},
+                                  reinterpret_cast<u32x4*>(vd) + q);
     *reinterpret_cast<uint16_t*>(meta + r * (K / 8) + c0 / 8) = (uint16_t)nibs;
   }
   if (bad_groups != nullptr && bad > 0) atomicAdd(bad_groups, bad);
@@ -295,6 +345,18 @@ static hipError_t prune_dispatch(const void* A, int64_t lda, int64_t R, int64_t 
     return hipGetLastError();
   };
   const int E4 = 4 * esz >= 16 ? 4 : 16 / esz, E8 = 8 * esz >= 16 ? 8 : 16 / esz, E16 = 16;
+  const int epc = 16 / esz;
+  if (N == 2 && M == 4 && K % epc == 0 && (uintptr_t)A % 16 == 0 && (lda * esz) % 16 == 0 &&
+      (uintptr_t)mask % (epc == 8 ? 8 : 4) == 0 && ldmask % (epc == 8 ? 8 : 4) == 0) {
+    const int64_t n = R * (K / epc);
+    if (n + 256 * kPruneU < (int64_t)UINT32_MAX)
+      hipLaunchKernelGGL((nm_prune24_vec_kernel<T, uint32_t>), dim3(nblocks(n, 256 * kPruneU)), dim3(256), 0, s,
+                         (const T*)A, lda, R, K, mask, ldmask);
+    else
+      hipLaunchKernelGGL((nm_prune24_vec_kernel<T, int64_t>), dim3(nblocks(n, 256 * kPruneU)), dim3(256), 0, s,
+                         (const T*)A, lda, R, K, mask, ldmask);
+    return hipGetLastError();
+  }
   switch (M) {
     case 4: return run(nm_prune_kernel<T, 4>, E4);
     case 8: return run(nm_prune_kernel<T, 8>, E8);
@@ -316,8 +378,12 @@ static hipError_t compress_dispatch(const void* A, int64_t lda, const uint8_t* m
   if (N == 2 && M == 4 && K % 16 == 0 && (uintptr_t)A % 16 == 0 && (lda * esz) % 16 == 0 &&
       (uintptr_t)mask % 16 == 0 && ldmask % 16 == 0 && (uintptr_t)values % 16 == 0 && (uintptr_t)meta % 2 == 0) {
     const int64_t n = R * (K / 16);
-    hipLaunchKernelGGL(nm_compress24_vec_kernel<T>, dim3(nblocks(n, 256)), dim3(256), 0, s, (const T*)A, lda, mask,
-                       ldmask, R, K, (T*)values, meta, bad);
+    if (n + 512 < (int64_t)UINT32_MAX)
+      hipLaunchKernelGGL((nm_compress24_vec_kernel<T, uint32_t>), dim3(nblocks(n, 512)), dim3(256), 0, s, (const T*)A,
+                         lda, mask, ldmask, R, K, (T*)values, meta, bad);
+    else
+      hipLaunchKernelGGL((nm_compress24_vec_kernel<T, int64_t>), dim3(nblocks(n, 512)), dim3(256), 0, s, (const T*)A,
+                         lda, mask, ldmask, R, K, (T*)values, meta, bad);
     return hipGetLastError();
   }
   const int64_t G = K / M;
