@@ -221,14 +221,15 @@ __global__ __launch_bounds__(256) void sddmm_mfma_kernel(
 // 8*(e/4) + 4*(l/32) + e%4.  A wave owns 64 rows x 128 output columns; its
 // four B fragments j = 0..3 map lane c to output column 4c + j, so lane c holds
 // every column of 2:4 group c and selects two of them by the group's nibble.
-// Tiles are staged per 32 t: D rows and X rows of 64 bytes, loaded with
-// direct-to-LDS dwordx4 loads; X rows are placed so that fragment j's 32 rows
-// are consecutive in LDS, and the 16-byte chunks of LDS row r are XOR-swizzled
-// by (r >> 1) & 3, which makes every ds_read_b128 of an operand conflict-free.
+// Tiles are staged per 64 t (128-byte rows, whole cache lines) in two buffers,
+// loaded with direct-to-LDS dwordx4 loads; X rows are placed so that fragment
+// j's 32 rows are consecutive in LDS, and the 16-byte chunks of LDS row r are
+// XOR-swizzled by (r >> 1) & 7, which keeps the ds_read_b128 operand reads of
+// 16 consecutive rows free of bank conflicts.
 // ---------------------------------------------------------------------------
-constexpr int TK = 32;   // t per stage
+constexpr int TK = 64;   // t per stage
 
-__device__ __forceinline__ int sd_swz(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int sd_swz(int r) { return (r >> 1) & 7; }
 // LDS row of output column n (within a 128-column wave group): fragment j = n%4, lane c = n/4
 __device__ __forceinline__ int sd_xrow(int n) { return (n & ~127) | ((n & 3) << 5) | ((n & 127) >> 2); }
 
@@ -243,7 +244,7 @@ struct SdCfg {
   static constexpr int LOADS = A_INSTR + B_INSTR;
   static_assert(WN == 128, "a wave owns 128 output columns (32 whole 2:4 groups)");
   static_assert(WM % 32 == 0 && A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "tiling");
-  static_assert(LOADS * (STAGES - 2) <= 63 && STAGE * STAGES <= 160 * 1024, "pipeline");
+  static_assert(STAGES == 2 && STAGE * STAGES <= 160 * 1024, "two LDS buffers");
 };
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
@@ -270,13 +271,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   const int KT = (int)(Tn / TK);
   const uint32_t smem_base = lds_addr(smem);
 
-  // DMA sources: instruction q covers LDS bytes q*1024.. = 16 rows of 64 bytes;
-  // lane -> LDS row 16q + lane/4, chunk position lane%4 (holding chunk pos ^ swz)
+  // DMA sources: instruction q covers LDS bytes q*1024.. = 8 rows of 128 bytes;
+  // lane -> LDS row 8q + lane/8, chunk position lane%8 (holding chunk pos ^ swz)
   const uint16_t* a_src[Cfg::A_INSTR];
 #pragma unroll
   for (int t = 0; t < Cfg::A_INSTR; ++t) {
-    const int r = 16 * (wave * Cfg::A_INSTR + t) + (lane >> 2);
-    const int c = (lane & 3) ^ sd_swz(r);
+    const int r = 8 * (wave * Cfg::A_INSTR + t) + (lane >> 3);
+    const int c = (lane & 7) ^ sd_swz(r);
     int64_t row = m0 + r;
     row = row < R ? row : R - 1;
     a_src[t] = D + row * ldd + 8 * c;
@@ -284,8 +285,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   const uint16_t* b_src[Cfg::B_INSTR];
 #pragma unroll
   for (int t = 0; t < Cfg::B_INSTR; ++t) {
-    const int r = 16 * (wave * Cfg::B_INSTR + t) + (lane >> 2);     // LDS row
-    const int c = (lane & 3) ^ sd_swz(r);
+    const int r = 8 * (wave * Cfg::B_INSTR + t) + (lane >> 3);      // LDS row
+    const int c = (lane & 7) ^ sd_swz(r);
     const int n = (r & ~127) | ((r & 31) << 2) | ((r & 127) >> 5);   // inverse of sd_xrow
     int64_t col = n0 + n;
     col = col < Kc ? col : Kc - 1;
@@ -310,47 +311,37 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int l32 = lane & 31, aa = lane >> 5;
-  int a_off[FM][2], b_off[4][2];
+  int a_row[FM], b_row[4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int c = 2 * kk + aa;
+  for (int i = 0; i < FM; ++i) a_row[i] = wm * Cfg::WM + 32 * i + l32;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int r = wm * Cfg::WM + 32 * i + l32;
-      a_off[i][kk] = r * (TK * 2) + ((c ^ sd_swz(r)) << 4);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 128 + 32 * j + l32;   // = sd_xrow(wn*128 + 4*l32 + j)
-      b_off[j][kk] = Cfg::A_BYTES + r * (TK * 2) + ((c ^ sd_swz(r)) << 4);
-    }
-  }
+  for (int j = 0; j < 4; ++j) b_row[j] = wn * 128 + 32 * j + l32;   // = sd_xrow(wn*128 + 4*l32 + j)
 
   auto compute = [&](int kt) {
     const unsigned char* st = smem + (kt % STAGES) * Cfg::STAGE;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < TK / 16; ++kk) {
+      const int c = 2 * kk + aa;
       bf16x8 a[FM];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const bf16x8*>(st + a_off[i][kk]);
+      for (int i = 0; i < FM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(st + a_row[i] * (TK * 2) + ((c ^ sd_swz(a_row[i])) << 4));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(st + b_off[j][kk]);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(st + Cfg::A_BYTES + b_row[j] * (TK * 2) +
+                                                           ((c ^ sd_swz(b_row[j])) << 4));
 #pragma unroll
         for (int i = 0; i < FM; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][j], 0, 0, 0);
       }
     }
   };
 
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s);
+  // two buffers: the loads of stage kt+1 are in flight while stage kt runs on the matrix cores
+  if (KT > 0) issue(0);
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + STAGES - 2 < KT) wait_vmcnt<Cfg::LOADS * (STAGES - 2)>();
-    else if (kt + 1 < KT) wait_vmcnt<Cfg::LOADS>();   // fewer stages left: at most one newer stage outstanding
-    else wait_vmcnt<0>();
-    barrier();
-    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+    wait_vmcnt<0>();   // this wave's loads of stage kt have landed
+    barrier();         // ... every wave's; and every wave is done with stage kt-1 (the other buffer)
+    if (kt + 1 < KT) issue(kt + 1);
     compute(kt);
   }
 
@@ -358,13 +349,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   const int64_t G = Kc / 4, mrow = (Kc + 7) / 8;
   const int64_t gq = (n0 + wn * 128) / 4 + l32;
   if (gq < G) {
+    uint32_t mb[FM][16];   // the metadata byte of every output row of the lane, loaded up front
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        int64_t row = m0 + wm * Cfg::WM + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
+        row = row < R ? row : R - 1;
+        mb[i][e] = meta[row * mrow + gq / 2];
+      }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t row = m0 + wm * Cfg::WM + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
         if (row < R) {
-          const uint32_t nib = (meta[row * mrow + gq / 2] >> (4 * (gq & 1))) & 0xF;
+          const uint32_t nib = (mb[i][e] >> (4 * (gq & 1))) & 0xF;
           const float v0 = acc[i][0][e], v1 = acc[i][1][e], v2 = acc[i][2][e], v3 = acc[i][3][e];
           const uint32_t p0 = nib & 3, p1 = (nib >> 2) & 3;
           typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -412,7 +412,7 @@ hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, in
   const bool staged = tier && tier[0] == '1';
   if (dt == DT_BF16 && !force && !staged && Tn % TK == 0 && ldd % 8 == 0 && ldx % 8 == 0 && (uintptr_t)D % 16 == 0 &&
       (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0)
-    return run_sddmm_dma<256, 256, 4, 2, 4>(D, ldd, X, ldx, R, Kc, Tn, meta, out, s);
+    return run_sddmm_dma<256, 256, 4, 2, 2>(D, ldd, X, ldx, R, Kc, Tn, meta, out, s);
   if (dt == DT_BF16 && !force && Tn % 8 == 0 && ldd % 8 == 0 && ldx % 8 == 0 && (uintptr_t)D % 16 == 0 &&
       (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0)
     return run_sddmm_mfma<256, 128, 128, 64>(D, ldd, X, ldx, R, Kc, Tn, meta, out, s);

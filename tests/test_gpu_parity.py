@@ -224,7 +224,8 @@ def test_reprune_t(R, K, dtype, kind):
     assert np.array_equal(host(mt), wmt)
 
 
-SDDMM_CASES = [(300, 136, 200), (256, 256, 512), (37, 20, 13), (64, 64, 64), (129, 68, 96), (520, 1032, 1024)]
+SDDMM_CASES = [(300, 136, 200), (256, 256, 512), (37, 20, 13), (64, 64, 64), (129, 68, 96), (520, 1032, 1024),
+               (300, 136, 256)]
 
 
 @pytest.mark.parametrize("R,Kc,T", SDDMM_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SDDMM_CASES])
