@@ -26,6 +26,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Barrier that first waits for this wave's LDS reads and writes (and scalar loads): after it,
+// every wave's LDS writes issued before it are visible and its LDS reads have completed.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)p;

@@ -340,7 +340,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   if (KT > 0) issue(0);
   for (int kt = 0; kt < KT; ++kt) {
     wait_vmcnt<0>();   // this wave's loads of stage kt have landed
-    barrier();         // ... every wave's; and every wave is done with stage kt-1 (the other buffer)
+    lds_barrier();     // ... every wave's; and every wave is done reading stage kt-1 (the other buffer)
     if (kt + 1 < KT) issue(kt + 1);
     compute(kt);
   }

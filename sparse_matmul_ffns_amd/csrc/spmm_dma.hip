@@ -298,12 +298,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
   for (int kt = 0; kt < KT; kt += 2) {
     const int j = kt >> 1;
     // even step kt
-    barrier();   // step kt's A and B are in LDS for every wave; every wave is done with step kt-1
+    lds_barrier();   // step kt's A and B are in LDS for every wave; every wave is done with step kt-1
     load_b(kc(kt + 2), rb0);
     issue_a((j + 1) & 1, j + 1 < jlast ? j + 1 : jlast);
     step(kt, rb1, [&]() { wait_vmcnt_regs<Cfg::L_B + Cfg::L_A>(rb1); });
     // odd step kt+1
-    barrier();
+    lds_barrier();
     load_b(kc(kt + 3), rb1);
     step(kt + 1, rb0, [&]() { wait_vmcnt_regs<Cfg::L_B>(rb0); });
   }
