@@ -236,8 +236,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
   const int l32 = lane & 31, aa = lane >> 5;
   // Step kt: A super-stage buffer (kt/2)%2, half s = kt%2; B buffer kt%2.  The B rows of step kt+1
   // (register set rbs, waited for by `wait`) are transposed into B buffer (kt+1)%2 while the
-  // matrix instructions of step kt run: the operand reads of both 32-k halves are issued first,
-  // then the first half's 16 instructions are interleaved with the transposes and LDS writes.
+  // matrix instructions of step kt run: the first half's operands are read first, the second
+  // half's during the first half's 16 instructions, the transposes during the second half's.
   auto step = [&](int kt, const u32x4 (&rbs)[8], auto wait) {
     const int s = kt & 1;
     const unsigned char* As = a_lds + ((kt >> 1) & 1) * Cfg::A_STAGE;
@@ -272,10 +272,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
     };
 #pragma unroll
     for (int i = 0; i < FM; ++i) mm[i] = *reinterpret_cast<const u32x2*>(Ms + ((wm * FM + i) * 32 + l32) * 16 + 8 * s);
+    // the first half's operand reads are issued before anything else of the step (the scheduler
+    // would otherwise sink them next to their matrix instructions and expose the LDS latency)
     operands(0);
-    operands(1);
+    __builtin_amdgcn_sched_barrier(0);
     wait();
+    operands(1);
     mfma(0);
+    __builtin_amdgcn_sched_barrier(0);
     store_b((kt + 1) & 1, rbs);
     mfma(1);
   };
