@@ -104,6 +104,20 @@ nm_status nm_compress(nm_dtype dt, const void* A, int64_t lda, const uint8_t* ma
                       int32_t* bad_groups, nm_stream stream);
 
 /*
+ * nm_prune_compress -- nm_prune and nm_compress in one call: the N:M magnitude
+ * selection of A ("Success story: ESPLAG", Highlights and Solution: pruning to
+ * N:M and its compressed storage) written both as the mask and as values +
+ * metadata.  Outputs are byte-identical to nm_prune followed by nm_compress.
+ *   A [R][lda], mask [R][ldmask] u8 output, values [R][(K/M)*N] and
+ *   meta [R][ceil((K/M)*N*ceil(log2 M)/8)] outputs, dtype dt.
+ * 2:4 with 16-byte aligned rows (A, mask, values) and K % 16 == 0 runs as one
+ * pass over A; other calls run the two passes.  Errors as for nm_compress.
+ */
+nm_status nm_prune_compress(nm_dtype dt, const void* A, int64_t lda, int64_t R, int64_t K, int N,
+                            int M, uint8_t* mask, int64_t ldmask, void* values, uint8_t* meta,
+                            nm_stream stream);
+
+/*
  * nm_decompress -- inverse of nm_compress: dense A_out [R][lda] with +0.0 at
  * every position that is not kept.
  */
@@ -121,6 +135,30 @@ nm_status nm_decompress(nm_dtype dt, const void* values, const uint8_t* meta, in
  */
 nm_status spmm_nm(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
                   const void* B, int64_t ldb, int64_t Nc, float* C, int64_t ldc, nm_stream stream);
+
+/*
+ * spmm_nm_t -- spmm_nm with the dense operand given K-contiguous:
+ * C[r][n] = sum_k decompress(values, meta)[r][k] * Bt[n][k]
+ * ("Success story: ESPLAG", Research Topic: the SpMM of a 2:4 layer).
+ *   values [R][K/2], meta [R][ceil(K/8)] (2:4 form of an R x K matrix), dtype dt
+ *   Bt     [Nc][ldbt] dense, dtype dt: row n holds column n of B (the token-major
+ *          activation layout of an FFN, [tokens][d_model])
+ *   C      [R][ldc] fp32 output, C[r][n] for n < Nc
+ * K must be a multiple of 4.  Errors as for spmm_nm.  The pipelined bf16 kernel
+ * runs when K % 256 == 0, ldbt % 8 == 0 and values, meta and Bt are 16-byte
+ * aligned; other calls take a slower general kernel.
+ */
+nm_status spmm_nm_t(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                    const void* Bt, int64_t ldbt, int64_t Nc, float* C, int64_t ldc, nm_stream stream);
+
+/*
+ * nm_transpose -- dst[c][r] = src[r][c] for an R x Cn matrix: turns a row-major
+ * dense operand B [K][Nc] into the K-contiguous form spmm_nm_t takes.
+ *   src [R][lds], dst [Cn][ldd] (ldd >= R), dtype dt; dst must not overlap src.
+ * bf16 only (NM_ERR_UNSUPPORTED for other dtypes).
+ */
+nm_status nm_transpose(nm_dtype dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst,
+                       int64_t ldd, nm_stream stream);
 
 /*
  * prune_act_venom -- V:N:M prune (N = 2) and compress in one pass, optionally

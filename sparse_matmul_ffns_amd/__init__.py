@@ -12,10 +12,13 @@ from .nmsparse import (  # noqa: F401
     nm_compress,
     nm_decompress,
     nm_prune,
+    nm_prune_compress,
     nm_reprune_t,
     prune_act_venom,
     sddmm_nm,
     sizes,
     spmm_nm,
+    spmm_nm_t,
     spmm_venom,
+    transpose,
 )

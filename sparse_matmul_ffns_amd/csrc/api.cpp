@@ -51,6 +51,15 @@ nm_status nm_compress(nm_dtype dt, const void* A, int64_t lda, const uint8_t* ma
       nms::launch_nm_compress(dt, A, lda, mask, ldmask, R, K, N, M, values, meta, bad_groups, hs(stream)));
 }
 
+nm_status nm_prune_compress(nm_dtype dt, const void* A, int64_t lda, int64_t R, int64_t K, int N, int M,
+                            uint8_t* mask, int64_t ldmask, void* values, uint8_t* meta, nm_stream stream) {
+  if (!A || !mask || !values || !meta) return NM_ERR_NULL;
+  if (!dtype_ok(dt) || !nm_ok(N, M)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || K % M != 0 || lda < K || ldmask < K) return NM_ERR_SHAPE;
+  if (!aligned(A, esize(dt)) || !aligned(values, esize(dt))) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_nm_prune_compress(dt, A, lda, R, K, N, M, mask, ldmask, values, meta, hs(stream)));
+}
+
 nm_status nm_decompress(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, int N, int M,
                         void* A_out, int64_t lda, nm_stream stream) {
   if (!values || !meta || !A_out) return NM_ERR_NULL;
@@ -67,6 +76,24 @@ nm_status spmm_nm(nm_dtype dt, const void* values, const uint8_t* meta, int64_t 
   if (R <= 0 || K <= 0 || Nc <= 0 || K % 4 != 0 || ldb < Nc || ldc < Nc) return NM_ERR_SHAPE;
   if (!aligned(values, esize(dt)) || !aligned(B, esize(dt)) || !aligned(C, 4)) return NM_ERR_ALIGN;
   return hip_status(nms::launch_spmm_nm(dt, values, meta, R, K, B, ldb, Nc, C, ldc, hs(stream)));
+}
+
+nm_status spmm_nm_t(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
+                    int64_t ldbt, int64_t Nc, float* C, int64_t ldc, nm_stream stream) {
+  if (!values || !meta || !Bt || !C) return NM_ERR_NULL;
+  if (!dtype_ok(dt)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || Nc <= 0 || K % 4 != 0 || ldbt < K || ldc < Nc) return NM_ERR_SHAPE;
+  if (!aligned(values, esize(dt)) || !aligned(Bt, esize(dt)) || !aligned(C, 4)) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_spmm_nm_t(dt, values, meta, R, K, Bt, ldbt, Nc, C, ldc, hs(stream)));
+}
+
+nm_status nm_transpose(nm_dtype dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst, int64_t ldd,
+                       nm_stream stream) {
+  if (!src || !dst) return NM_ERR_NULL;
+  if (dt != NM_BF16) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || Cn <= 0 || lds < Cn || ldd < R) return NM_ERR_SHAPE;
+  if (!aligned(src, esize(dt)) || !aligned(dst, esize(dt))) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_nm_transpose(dt, src, lds, R, Cn, dst, ldd, hs(stream)));
 }
 
 nm_status prune_act_venom(nm_dtype dt, const void* Z, int64_t ldz, int64_t R, int64_t K, int V, int M,

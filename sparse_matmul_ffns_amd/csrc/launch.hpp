@@ -20,6 +20,8 @@ hipError_t launch_nm_prune(int dt, const void* A, int64_t lda, int64_t R, int64_
 hipError_t launch_nm_compress(int dt, const void* A, int64_t lda, const uint8_t* mask, int64_t ldmask,
                               int64_t R, int64_t K, int N, int M, void* values, uint8_t* meta, int32_t* bad,
                               hipStream_t s);
+hipError_t launch_nm_prune_compress(int dt, const void* A, int64_t lda, int64_t R, int64_t K, int N, int M,
+                                    uint8_t* mask, int64_t ldmask, void* values, uint8_t* meta, hipStream_t s);
 hipError_t launch_nm_decompress(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, int N,
                                 int M, void* out, int64_t lda, hipStream_t s);
 hipError_t launch_prune_act_venom(int dt, const void* Z, int64_t ldz, int64_t R, int64_t K, int V, int M,
@@ -38,6 +40,14 @@ hipError_t launch_spmm_nm_dma(const void* values, const uint8_t* meta, int64_t R
 hipError_t launch_spmm_venom_dma(const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R,
                                  int64_t Kd, int V, int M, int64_t G, const void* B, int64_t ldb, int64_t Nc,
                                  float* C, int64_t ldc, hipStream_t s);
+bool spmm_nt_ok(const void* values, const uint8_t* meta, const void* Bt, int64_t ldbt, int64_t R, int64_t Nc,
+                int64_t Kd);
+hipError_t launch_spmm_nm_t(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
+                            int64_t ldbt, int64_t Nc, float* C, int64_t ldc, hipStream_t s);
+hipError_t launch_spmm_nm_nt_dma(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
+                                 int64_t ldbt, int64_t Nc, float* C, int64_t ldc, hipStream_t s);
+hipError_t launch_nm_transpose(int dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst, int64_t ldd,
+                               hipStream_t s);
 hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R,
                            int64_t Kc, int64_t T, const uint8_t* meta, float* out, hipStream_t s);
 

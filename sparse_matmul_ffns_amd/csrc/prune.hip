@@ -296,6 +296,76 @@ __global__ __launch_bounds__(256) void nm_compress24_vec_kernel(const T* __restr
 }
 
 // ---------------------------------------------------------------------------
+// nm_prune_compress, 2:4 with 16-byte aligned rows: the selection of nm_prune and the packing of
+// nm_compress in one pass over A (one read of A instead of two, no read of the mask).  One thread
+// per 16 elements (4 groups) and kFusedU such chunks, all loaded before any is ranked: 16-byte
+// loads of A, one 16-byte store of the chunk's mask bytes, one 16- or 32-byte store of its 8 kept
+// values and one 2-byte store of its 4 nibbles.
+// ---------------------------------------------------------------------------
+constexpr int kFusedU = 2;
+
+template <typename T, typename I>
+__global__ __launch_bounds__(256) void nm_prune_compress24_vec_kernel(const T* __restrict__ A, int64_t lda,
+                                                                      int64_t R, int64_t K,
+                                                                      uint8_t* __restrict__ mask, int64_t ldmask,
+                                                                      T* __restrict__ values,
+                                                                      uint8_t* __restrict__ meta) {
+  constexpr int NA = (int)sizeof(T);               // 16-byte loads of A per chunk (16 elements)
+  const I per_row = (I)(K / 16);
+  const I total = (I)R * per_row;
+  const I base = (I)blockIdx.x * (256 * kFusedU) + threadIdx.x;
+  u32x4 xa[kFusedU][NA];
+  I rr[kFusedU], cc[kFusedU];
+#pragma unroll
+  for (int u = 0; u < kFusedU; ++u) {
+    const I cid = base + 256 * u;
+    rr[u] = cid / per_row;
+    cc[u] = (cid - rr[u] * per_row) * 16;
+    if (cid < total) {
+      const u32x4* a4 = reinterpret_cast<const u32x4*>(A + (int64_t)rr[u] * lda + cc[u]);
+#pragma unroll
+      for (int q = 0; q < NA; ++q) xa[u][q] = __builtin_nontemporal_load(a4 + q);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kFusedU; ++u) {
+    if (base + 256 * u >= total) break;
+    const int64_t r = rr[u], c0 = cc[u];
+    uint32_t out[2 * NA];   // the 8 kept values of the chunk, packed
+    uint32_t mk[4];         // mask bytes of the 4 groups
+    uint32_t nibs = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t nib;
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t d01 = xa[u][g >> 1][(g & 1) * 2], d23 = xa[u][g >> 1][(g & 1) * 2 + 1];
+        nib = select24_bf16(d01 & 0xFFFFu, d01 >> 16, d23 & 0xFFFFu, d23 >> 16);
+        const uint32_t p0 = nib & 3u, p1 = nib >> 2;
+        // bytes 2p, 2p+1 of the pair (d23:d01) hold the group's value p
+        out[g] = __builtin_amdgcn_perm(d23, d01, (p0 * 0x202u + 0x100u) | ((p1 * 0x202u + 0x100u) << 16));
+      } else {
+        const u32x4 q = xa[u][g];
+        nib = select24(q[0] & 0x7FFFFFFFu, q[1] & 0x7FFFFFFFu, q[2] & 0x7FFFFFFFu, q[3] & 0x7FFFFFFFu);
+        const uint32_t p0 = nib & 3u, p1 = nib >> 2;
+        auto pick = [&](uint32_t p) { return p == 0 ? q[0] : p == 1 ? q[1] : p == 2 ? q[2] : q[3]; };
+        out[2 * g] = pick(p0);
+        out[2 * g + 1] = pick(p1);
+      }
+      mk[g] = (1u << (8 * (nib & 3u))) | (1u << (8 * (nib >> 2)));
+      nibs |= nib << (4 * g);
+    }
+    __builtin_nontemporal_store(u32x4{mk[0], mk[1], mk[2], mk[3]},
+                                reinterpret_cast<u32x4*>(mask + r * ldmask + c0));
+    T* vd = values + r * (K / 2) + c0 / 2;
+#pragma unroll
+    for (int q = 0; q < NA / 2; ++q)
+      __builtin_nontemporal_store(u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]},
+                                  reinterpret_cast<u32x4*>(vd) + q);
+    *reinterpret_cast<uint16_t*>(meta + r * (K / 8) + c0 / 8) = (uint16_t)nibs;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // nm_decompress: one thread per chunk of CG groups of one row.
 // ---------------------------------------------------------------------------
 template <typename T, int M>
@@ -412,6 +482,33 @@ hipError_t launch_nm_compress(int dt, const void* A, int64_t lda, const uint8_t*
                               hipStream_t s) {
   return dt == DT_BF16 ? compress_dispatch<uint16_t>(A, lda, mask, ldmask, R, K, N, M, values, meta, bad, s)
                        : compress_dispatch<uint32_t>(A, lda, mask, ldmask, R, K, N, M, values, meta, bad, s);
+}
+
+template <typename T>
+static hipError_t prune_compress_dispatch(const void* A, int64_t lda, int64_t R, int64_t K, int N, int M,
+                                          uint8_t* mask, int64_t ldmask, void* values, uint8_t* meta, hipStream_t s) {
+  const int esz = sizeof(T);
+  if (N == 2 && M == 4 && K % 16 == 0 && (uintptr_t)A % 16 == 0 && (lda * esz) % 16 == 0 &&
+      (uintptr_t)mask % 16 == 0 && ldmask % 16 == 0 && (uintptr_t)values % 16 == 0 && (uintptr_t)meta % 2 == 0) {
+    const int64_t n = R * (K / 16);
+    if (n + 256 * kFusedU < (int64_t)UINT32_MAX)
+      hipLaunchKernelGGL((nm_prune_compress24_vec_kernel<T, uint32_t>), dim3(nblocks(n, 256 * kFusedU)), dim3(256), 0,
+                         s, (const T*)A, lda, R, K, mask, ldmask, (T*)values, meta);
+    else
+      hipLaunchKernelGGL((nm_prune_compress24_vec_kernel<T, int64_t>), dim3(nblocks(n, 256 * kFusedU)), dim3(256), 0,
+                         s, (const T*)A, lda, R, K, mask, ldmask, (T*)values, meta);
+    return hipGetLastError();
+  }
+  // other patterns and layouts: the two passes, mask in between
+  const hipError_t e = prune_dispatch<T>(A, lda, R, K, N, M, mask, ldmask, s);
+  if (e != hipSuccess) return e;
+  return compress_dispatch<T>(A, lda, mask, ldmask, R, K, N, M, values, meta, nullptr, s);
+}
+
+hipError_t launch_nm_prune_compress(int dt, const void* A, int64_t lda, int64_t R, int64_t K, int N, int M,
+                                    uint8_t* mask, int64_t ldmask, void* values, uint8_t* meta, hipStream_t s) {
+  return dt == DT_BF16 ? prune_compress_dispatch<uint16_t>(A, lda, R, K, N, M, mask, ldmask, values, meta, s)
+                       : prune_compress_dispatch<uint32_t>(A, lda, R, K, N, M, mask, ldmask, values, meta, s);
 }
 
 template <typename T>

@@ -42,8 +42,9 @@ namespace nms {
 template <typename T, bool VENOM>
 __global__ __launch_bounds__(256) void spmm_generic_kernel(const T* __restrict__ values, const uint8_t* __restrict__ meta,
                                                            const uint8_t* __restrict__ colsel, int64_t R, int64_t K,
-                                                           int V, int M, const T* __restrict__ B, int64_t ldb,
-                                                           int64_t Nc, float* __restrict__ C, int64_t ldc) {
+                                                           int V, int M, const T* __restrict__ B, int64_t sbk,
+                                                           int64_t sbn, int64_t Nc, float* __restrict__ C,
+                                                           int64_t ldc) {
   constexpr int TM = 64, TN = 64, KC = 32;
   __shared__ float As[KC][TM + 4];
   __shared__ float Bs[KC][TN + 4];
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(256) void spmm_generic_kernel(const T* __restrict__
     for (int i = tid; i < KC * TN; i += 256) {
       const int kk = i / TN, nn = i % TN;
       const int64_t k = k0 + kk, n = n0 + nn;
-      Bs[kk][nn] = (k < K && n < Nc) ? Elem<T>::to_f32(B[k * ldb + n]) : 0.f;
+      Bs[kk][nn] = (k < K && n < Nc) ? Elem<T>::to_f32(B[k * sbk + n * sbn]) : 0.f;
     }
     __syncthreads();
 #pragma unroll 4
@@ -330,11 +331,11 @@ static hipError_t run_smfmac(const void* values, const uint8_t* meta, const uint
 
 template <typename T, bool VENOM>
 static hipError_t run_generic(const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R, int64_t K,
-                              int V, int M, const void* B, int64_t ldb, int64_t Nc, float* C, int64_t ldc,
+                              int V, int M, const void* B, int64_t sbk, int64_t sbn, int64_t Nc, float* C, int64_t ldc,
                               hipStream_t s) {
   dim3 grid((unsigned)((Nc + 63) / 64), (unsigned)((R + 63) / 64));
   hipLaunchKernelGGL((spmm_generic_kernel<T, VENOM>), grid, dim3(256), 0, s, (const T*)values, meta, colsel, R, K, V,
-                     M, (const T*)B, ldb, Nc, C, ldc);
+                     M, (const T*)B, sbk, sbn, Nc, C, ldc);
   return hipGetLastError();
 }
 
@@ -362,8 +363,16 @@ hipError_t launch_spmm_nm(int dt, const void* values, const uint8_t* meta, int64
     return launch_spmm_nm_dma(values, meta, R, K, B, ldb, Nc, C, ldc, s);
   if (dt == DT_BF16 && !force_generic() && fast_ok(values, meta, B, ldb, Nc, C, ldc, K))
     return run_smfmac<256, 128, 128, 64, false>(values, meta, nullptr, R, K, 4, 4, K / 4, B, ldb, Nc, C, ldc, s);
-  return dt == DT_BF16 ? run_generic<uint16_t, false>(values, meta, nullptr, R, K, 4, 4, B, ldb, Nc, C, ldc, s)
-                       : run_generic<uint32_t, false>(values, meta, nullptr, R, K, 4, 4, B, ldb, Nc, C, ldc, s);
+  return dt == DT_BF16 ? run_generic<uint16_t, false>(values, meta, nullptr, R, K, 4, 4, B, ldb, 1, Nc, C, ldc, s)
+                       : run_generic<uint32_t, false>(values, meta, nullptr, R, K, 4, 4, B, ldb, 1, Nc, C, ldc, s);
+}
+
+hipError_t launch_spmm_nm_t(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
+                            int64_t ldbt, int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
+  if (dt == DT_BF16 && !force_generic() && spmm_nt_ok(values, meta, Bt, ldbt, R, Nc, K))
+    return launch_spmm_nm_nt_dma(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
+  return dt == DT_BF16 ? run_generic<uint16_t, false>(values, meta, nullptr, R, K, 4, 4, Bt, 1, ldbt, Nc, C, ldc, s)
+                       : run_generic<uint32_t, false>(values, meta, nullptr, R, K, 4, 4, Bt, 1, ldbt, Nc, C, ldc, s);
 }
 
 hipError_t launch_spmm_venom(int dt, const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R,
@@ -381,8 +390,8 @@ hipError_t launch_spmm_venom(int dt, const void* values, const uint8_t* meta, co
     if (V % 64 == 0)
       return run_smfmac<64, 256, 64, 64, true>(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
   }
-  return dt == DT_BF16 ? run_generic<uint16_t, true>(values, meta, colsel, R, K, V, M, B, ldb, Nc, C, ldc, s)
-                       : run_generic<uint32_t, true>(values, meta, colsel, R, K, V, M, B, ldb, Nc, C, ldc, s);
+  return dt == DT_BF16 ? run_generic<uint16_t, true>(values, meta, colsel, R, K, V, M, B, ldb, 1, Nc, C, ldc, s)
+                       : run_generic<uint32_t, true>(values, meta, colsel, R, K, V, M, B, ldb, 1, Nc, C, ldc, s);
 }
 
 }  // namespace nms

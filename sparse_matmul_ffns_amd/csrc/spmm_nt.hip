@@ -1,0 +1,298 @@
+// 2:4 SpMM with the dense operand given K-contiguous ("NT" form), gfx950.
+//
+// Product: C[r][n] = sum_k A[r][k] Bt[n][k], A in 2:4 form (values + nibbles)
+// ("Success story: ESPLAG", Research Topic: the SpMM of a 2:4 layer; "To 2:4
+// Sparsity and Beyond", abstract: 2:4 weights in every FFN matmul).  Bt is the
+// dense operand with its reduction index contiguous -- the token-major layout
+// in which an FFN's activations [tokens][d_model] are usually kept -- which is
+// also the order v_smfmac wants for its B operand (each lane holds 16 k values
+// of one column).  Both operands therefore go from HBM to LDS with
+// direct-to-LDS loads, as whole rows, and nothing is transposed on the way: the
+// kernel's instruction stream is operand reads from LDS and matrix
+// instructions.  A transpose pass (nm_transpose_bf16_kernel below) turns a
+// row-major B [K][Nc] into Bt once; every row tile of the SpMM then reads Bt's
+// panels directly.
+//
+// v_smfmac_f32_32x32x32_bf16 on gfx950: lane l holds A row l%32 with the 8 kept
+// values of dense k 16*(l/32)..+15 (index operand: one nibble p0 | p1 << 2 per
+// group of 4, group 0 in bits 0..3 -- the stored metadata order); B column l%32
+// with k = 8*(l/32)..+7 in elements 0..7 and k = 16 + 8*(l/32)..+7 in elements
+// 8..15; C column l%32, element e at row 8*(e/4) + 4*(l/32) + e%4.
+//
+// Loads (measured on gfx950): the vector L1 of a CU spends about two cycles per
+// 128-byte line an instruction touches, however few of its bytes are used, so
+// every operand is fetched as whole lines: values two 64-k steps at a time (128
+// bytes of a row), metadata four steps at a time (32 bytes of a row), Bt one
+// step at a time (128 bytes of a column), each into two LDS buffers (144 KB).
+// The 16-byte chunks of a 128-byte LDS row are XOR-swizzled by (row >> 1) & 7
+// and the two 16-byte halves of a 32-byte metadata row swap every 8 rows, so
+// the operand reads of 16 (32) consecutive rows are free of bank conflicts.
+// 8 waves (two per SIMD) own 128 x 64 of the 256 x 256 tile each, 4 x 2
+// fragments with accumulators in VGPRs.
+#include "common.hpp"
+#include "dma.hpp"
+#include "launch.hpp"
+
+namespace nms {
+
+__device__ __forceinline__ int nt_apos(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int nt_bpos(int n, int c) { return c ^ ((n >> 1) & 7); }
+__device__ __forceinline__ int nt_mpos(int r, int p) { return p ^ ((r >> 3) & 1); }
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+struct NtCfg {
+  static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int SA = BM * 128;     // values of two steps
+  static constexpr int SM = BM * 32;      // metadata of four steps
+  static constexpr int SB = BN * 128;     // Bt of one step
+  static constexpr int OFF_A = 0, OFF_B = 2 * SA, OFF_M = 2 * SA + 2 * SB;
+  static constexpr int LDS = 2 * (SA + SB + SM);
+  static constexpr int A_INSTR = SA / 1024 / NW, M_INSTR = SM / 1024 / NW, B_INSTR = SB / 1024 / NW;
+  static_assert(A_INSTR >= 1 && M_INSTR >= 1 && B_INSTR >= 1, "every wave loads a share of each operand");
+  static_assert(SA % (1024 * NW) == 0 && SM % (1024 * NW) == 0 && SB % (1024 * NW) == 0, "tiling");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "fragments");
+  static_assert(A_INSTR + M_INSTR + B_INSTR <= 63, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
+    const uint16_t* __restrict__ values, const uint8_t* __restrict__ meta, int64_t R, int64_t Kd,
+    const uint16_t* __restrict__ Bt, int64_t ldbt, int64_t Nc, float* __restrict__ C, int64_t ldc) {
+  using Cfg = NtCfg<BM, BN, WAVES_M, WAVES_N>;
+  constexpr int FM = Cfg::FM, FN = Cfg::FN;
+  extern __shared__ __align__(1024) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+  const int ntm = (int)((R + BM - 1) / BM), ntn = (int)((Nc + BN - 1) / BN);
+  const int nwg = ntm * ntn;
+  const int wg = xcd_remap(blockIdx.x, nwg);
+  constexpr int GM = 4;
+  const int grp = wg / (GM * ntn);
+  const int first_m = grp * GM;
+  const int gsz = (ntm - first_m) < GM ? (ntm - first_m) : GM;
+  const int within = wg - grp * GM * ntn;
+  const int tm = first_m + within % gsz, tn = within / gsz;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int64_t vrow = Kd / 2, mrow = Kd / 8;
+  const int KT = (int)(Kd / 64);            // a multiple of 4
+  const int jlast = KT / 2 - 1, clast = KT / 4 - 1;
+  const uint32_t smem_base = lds_addr(smem);
+
+  // Sources as 32-bit byte offsets from wave-uniform bases (the dispatch guarantees every operand
+  // is smaller than 4 GiB).
+  // values, instruction t: LDS rows 8q .. 8q+7 of 128 bytes; lane -> row 8q + lane/8, chunk lane%8
+  uint32_t a_off[Cfg::A_INSTR];
+#pragma unroll
+  for (int t = 0; t < Cfg::A_INSTR; ++t) {
+    const int r = 8 * (wave * Cfg::A_INSTR + t) + (lane >> 3);
+    int64_t row = m0 + r;
+    row = row < R ? row : R - 1;
+    a_off[t] = (uint32_t)(2 * (row * vrow + 8 * nt_apos(r, lane & 7)));
+  }
+  // metadata, instruction t: LDS rows 32q .. 32q+31 of 32 bytes; lane -> row 32q + lane/2, piece lane%2
+  uint32_t m_off[Cfg::M_INSTR];
+#pragma unroll
+  for (int t = 0; t < Cfg::M_INSTR; ++t) {
+    const int r = 32 * (wave * Cfg::M_INSTR + t) + (lane >> 1);
+    int64_t row = m0 + r;
+    row = row < R ? row : R - 1;
+    m_off[t] = (uint32_t)(row * mrow + 16 * nt_mpos(r, lane & 1));
+  }
+  // Bt, instruction t: LDS rows 8q .. 8q+7 of 128 bytes; lane -> row 8q + lane/8, chunk lane%8
+  uint32_t b_off[Cfg::B_INSTR];
+#pragma unroll
+  for (int t = 0; t < Cfg::B_INSTR; ++t) {
+    const int n = 8 * (wave * Cfg::B_INSTR + t) + (lane >> 3);
+    int64_t col = n0 + n;
+    col = col < Nc ? col : Nc - 1;
+    b_off[t] = (uint32_t)(2 * (col * ldbt + 8 * nt_bpos(n, lane & 7)));
+  }
+  auto issue_a = [&](int buf, int j) {   // values of steps 2j, 2j+1
+    const uint32_t st = smem_base + Cfg::OFF_A + buf * Cfg::SA;
+    const uint16_t* base = values + (int64_t)j * 64;
+#pragma unroll
+    for (int t = 0; t < Cfg::A_INSTR; ++t) dma16s(a_off[t], base, uniform(st + (wave * Cfg::A_INSTR + t) * 1024));
+  };
+  auto issue_m = [&](int buf, int c) {   // metadata of steps 4c .. 4c+3
+    const uint32_t st = smem_base + Cfg::OFF_M + buf * Cfg::SM;
+    const uint8_t* base = meta + (int64_t)c * 32;
+#pragma unroll
+    for (int t = 0; t < Cfg::M_INSTR; ++t) dma16s(m_off[t], base, uniform(st + (wave * Cfg::M_INSTR + t) * 1024));
+  };
+  auto issue_b = [&](int buf, int kt) {
+    const uint32_t st = smem_base + Cfg::OFF_B + buf * Cfg::SB;
+    const uint16_t* base = Bt + (int64_t)kt * 64;
+#pragma unroll
+    for (int t = 0; t < Cfg::B_INSTR; ++t) dma16s(b_off[t], base, uniform(st + (wave * Cfg::B_INSTR + t) * 1024));
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int l32 = lane & 31, aa = lane >> 5;
+  auto step = [&](int kt) {
+    const int s = kt & 1, u = kt & 3;
+    const unsigned char* As = smem + Cfg::OFF_A + ((kt >> 1) & 1) * Cfg::SA;
+    const unsigned char* Ms = smem + Cfg::OFF_M + ((kt >> 2) & 1) * Cfg::SM;
+    const unsigned char* Bs = smem + Cfg::OFF_B + (kt & 1) * Cfg::SB;
+    u32x2 mm[FM];
+    bf16x8 a[2][FM];
+    bf16x16 b[2][FN];
+    auto operands = [&](int h) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = (wm * FM + i) * 32 + l32;
+        a[h][i] = *reinterpret_cast<const bf16x8*>(As + r * 128 + (nt_apos(r, 4 * s + 2 * h + aa) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = wn * Cfg::WN + 32 * j + l32;
+        const unsigned char* row = Bs + n * 128;
+        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(row + (nt_bpos(n, 4 * h + aa) << 4));
+        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(row + (nt_bpos(n, 4 * h + 2 + aa) << 4));
+        b[h][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      }
+    };
+    auto mfma = [&](int h) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a[h][i], b[h][j], acc[i][j],
+                                                               (int)(mm[i][h] >> (16 * aa)), 0, 0);
+    };
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = (wm * FM + i) * 32 + l32;
+      mm[i] = *reinterpret_cast<const u32x2*>(Ms + r * 32 + (nt_mpos(r, u >> 1) << 4) + 8 * (u & 1));
+    }
+    operands(0);
+    __builtin_amdgcn_sched_barrier(0);
+    operands(1);
+    mfma(0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(1);
+  };
+
+  // Step kt needs values super-stage kt/2 (loaded during step kt-2), metadata chunk kt/4 (during
+  // step kt-4) and Bt step kt (during step kt-1, as the first loads of that step).  The wait before
+  // step kt lets through the loads issued after Bt step kt: a values super-stage when kt-1 is even,
+  // a metadata chunk when kt-1 is a multiple of 4.  Past the end the loads repeat the last stage
+  // into buffers that are never read again, so every step looks alike.
+  issue_a(0, 0);
+  issue_m(0, 0);
+  issue_b(0, 0);
+  auto body = [&](int kt, auto wait) {
+    wait();
+    lds_barrier();   // step kt's operands are in LDS for every wave; every wave is done with step kt-1
+    issue_b((kt + 1) & 1, kt + 1 < KT ? kt + 1 : KT - 1);
+    if ((kt & 1) == 0) issue_a(((kt >> 1) + 1) & 1, (kt >> 1) + 1 <= jlast ? (kt >> 1) + 1 : jlast);
+    if ((kt & 3) == 0) issue_m(((kt >> 2) + 1) & 1, (kt >> 2) + 1 <= clast ? (kt >> 2) + 1 : clast);
+    step(kt);
+  };
+  for (int kt = 0; kt < KT; kt += 4) {
+    body(kt, [] { wait_vmcnt<0>(); });
+    body(kt + 1, [] { wait_vmcnt<Cfg::A_INSTR + Cfg::M_INSTR>(); });
+    body(kt + 2, [] { wait_vmcnt<0>(); });
+    body(kt + 3, [] { wait_vmcnt<Cfg::A_INSTR>(); });
+  }
+  wait_vmcnt<0>();   // drain: no load may land in LDS after the workgroup ends
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = n0 + wn * Cfg::WN + 32 * j + l32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * Cfg::WM + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
+        if (row < R && col < Nc) __builtin_nontemporal_store(acc[i][j][e], C + row * ldc + col);
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+static hipError_t run_nt(const void* values, const uint8_t* meta, int64_t R, int64_t Kd, const void* Bt, int64_t ldbt,
+                         int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
+  using Cfg = NtCfg<BM, BN, WAVES_M, WAVES_N>;
+  auto kern = spmm_nt_kernel<BM, BN, WAVES_M, WAVES_N>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+  const int64_t ntiles = ((R + BM - 1) / BM) * ((Nc + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg::NT), (size_t)Cfg::LDS, s, (const uint16_t*)values, meta,
+                     R, Kd, (const uint16_t*)Bt, ldbt, Nc, C, ldc);
+  return hipGetLastError();
+}
+
+// Conditions: bf16, whole 256-k chunks (four steps), 16-byte loads of values, metadata and Bt
+// rows, and every operand addressable with 32-bit byte offsets.
+bool spmm_nt_ok(const void* values, const uint8_t* meta, const void* Bt, int64_t ldbt, int64_t R, int64_t Nc,
+                int64_t Kd) {
+  return Kd % 256 == 0 && ldbt % 8 == 0 && (uintptr_t)values % 16 == 0 && (uintptr_t)meta % 16 == 0 &&
+         (uintptr_t)Bt % 16 == 0 && R * Kd < (int64_t(1) << 32) && Nc * ldbt * 2 < (int64_t(1) << 32);
+}
+
+hipError_t launch_spmm_nm_nt_dma(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
+                                 int64_t ldbt, int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
+  return run_nt<256, 256, 2, 4>(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
+}
+
+// ---------------------------------------------------------------------------
+// Transpose of a bf16 matrix: dst[c][r] = src[r][c].  A lane moves an 8 x 8
+// block: eight 16-byte row loads, v_perm into eight 8-row columns, eight
+// 16-byte stores.  The 64 lanes of a wave cover a 64 x 64 tile (lanes 8b..8b+7
+// take row block b), so both the loads and the stores of a wave cover whole
+// 128-byte runs.  Edges (rows or columns not a multiple of 8) take the
+// element-wise path.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void nm_transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                                int64_t R, int64_t Cn, uint16_t* __restrict__ dst,
+                                                                int64_t ldd) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t tiles_c = (Cn + 63) / 64;
+  const int64_t tile = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t tr = tile / tiles_c, tc = tile % tiles_c;
+  const int64_t r0 = tr * 64 + 8 * (lane & 7), c0 = tc * 64 + 8 * (lane >> 3);
+  if (r0 >= R || c0 >= Cn) return;
+  const bool full = r0 + 8 <= R && c0 + 8 <= Cn && lds % 8 == 0 && ldd % 8 == 0 && (uintptr_t)src % 16 == 0 &&
+                    (uintptr_t)dst % 16 == 0;
+  if (full) {
+    u32x4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (r0 + q) * lds + c0));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 d;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[j] = __builtin_amdgcn_perm(v[2 * j + 1][e >> 1], v[2 * j][e >> 1], sel);
+      __builtin_nontemporal_store(d, reinterpret_cast<u32x4*>(dst + (c0 + e) * ldd + r0));
+    }
+  } else {
+    for (int q = 0; q < 8 && r0 + q < R; ++q)
+      for (int e = 0; e < 8 && c0 + e < Cn; ++e) dst[(c0 + e) * ldd + r0 + q] = src[(r0 + q) * lds + c0 + e];
+  }
+}
+
+hipError_t launch_nm_transpose(int dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst, int64_t ldd,
+                               hipStream_t s) {
+  if (dt != DT_BF16) return hipErrorNotSupported;
+  const int64_t tiles = ((R + 63) / 64) * ((Cn + 63) / 64);
+  hipLaunchKernelGGL(nm_transpose_bf16_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s,
+                     (const uint16_t*)src, lds, R, Cn, (uint16_t*)dst, ldd);
+  return hipGetLastError();
+}
+
+}  // namespace nms

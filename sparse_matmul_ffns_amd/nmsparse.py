@@ -30,8 +30,11 @@ _vp = ctypes.c_void_p
 _SIGNATURES = {
     "nm_prune": [_int, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp],
     "nm_compress": [_int, _vp, _i64, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp],
+    "nm_prune_compress": [_int, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _vp, _vp],
     "nm_decompress": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _vp],
     "spmm_nm": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
+    "spmm_nm_t": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
+    "nm_transpose": [_int, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "prune_act_venom": [_int, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _i64, _vp],
     "spmm_venom": [_int, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
     "nm_reprune_t": [_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp],
@@ -154,6 +157,23 @@ def nm_compress(A: torch.Tensor, mask: torch.Tensor, N: int = 2, M: int = 4,
     return values, meta
 
 
+def nm_prune_compress(A: torch.Tensor, N: int = 2, M: int = 4, mask=None, values=None, meta=None):
+    """nm_prune and nm_compress in one call: returns (mask, values, meta)."""
+    _dev(A, mask, values, meta)
+    R, K = A.shape
+    nv, mb, _ = sizes(R, K, N, M)
+    if mask is None:
+        mask = torch.empty((R, K), dtype=torch.uint8, device=A.device)
+    if values is None:
+        values = torch.empty((R, nv // R), dtype=A.dtype, device=A.device)
+    if meta is None:
+        meta = torch.empty((R, mb // R), dtype=torch.uint8, device=A.device)
+    _flat(values, "values"), _flat(meta, "meta")
+    _check(lib().nm_prune_compress(_dt(A), _p(A), _rows(A, "A"), R, K, N, M, _p(mask), _rows(mask, "mask"),
+                                   _p(values), _p(meta), _stream()), "nm_prune_compress")
+    return mask, values, meta
+
+
 def nm_decompress(values: torch.Tensor, meta: torch.Tensor, K: int, N: int = 2, M: int = 4, out=None):
     _dev(values, meta, out)
     _flat(values, "values"), _flat(meta, "meta")
@@ -178,6 +198,36 @@ def spmm_nm(values: torch.Tensor, meta: torch.Tensor, K: int, B: torch.Tensor, o
         out = torch.empty((R, Nc), dtype=torch.float32, device=B.device)
     _check(lib().spmm_nm(_dt(B), _p(values), _p(meta), R, K, _p(B), _rows(B, "B"), Nc, _p(out),
                          _rows(out, "out"), _stream()), "spmm_nm")
+    return out
+
+
+def spmm_nm_t(values: torch.Tensor, meta: torch.Tensor, K: int, Bt: torch.Tensor, out=None) -> torch.Tensor:
+    """C = decompress(values, meta) @ Bt.T with Bt [Nc, K] (rows contiguous)."""
+    _dev(values, meta, Bt, out)
+    _flat(values, "values"), _flat(meta, "meta")
+    if Bt.dtype != values.dtype:
+        raise TypeError("values and Bt must share a dtype")
+    R = values.shape[0]
+    Nc = Bt.shape[0]
+    if Bt.shape[1] != K:
+        raise ValueError("Bt must have K columns")
+    if out is None:
+        out = torch.empty((R, Nc), dtype=torch.float32, device=Bt.device)
+    _check(lib().spmm_nm_t(_dt(Bt), _p(values), _p(meta), R, K, _p(Bt), _rows(Bt, "Bt"), Nc, _p(out),
+                           _rows(out, "out"), _stream()), "spmm_nm_t")
+    return out
+
+
+def transpose(X: torch.Tensor, out=None) -> torch.Tensor:
+    """out[c, r] = X[r, c] (bf16), e.g. B [K, Nc] -> Bt [Nc, K] for spmm_nm_t."""
+    _dev(X, out)
+    R, C = X.shape
+    if out is None:
+        out = torch.empty((C, R), dtype=X.dtype, device=X.device)
+    if out.shape != (C, R) or out.dtype != X.dtype:
+        raise ValueError("out must be [C, R] with X's dtype")
+    _check(lib().nm_transpose(_dt(X), _p(X), _rows(X, "X"), R, C, _p(out), _rows(out, "out"), _stream()),
+           "nm_transpose")
     return out
 
 

@@ -60,7 +60,8 @@ def _check_cols(C_dev, A64, B64_cols, cols, what):
 
 
 # ---------------------------------------------------------------------------
-# 2:4 up-projection: nm_prune -> nm_compress -> spmm_nm, W [8192 x 2048], X [2048 x 4096]
+# 2:4 up-projection: nm_prune -> nm_compress -> spmm_nm (and nm_transpose -> spmm_nm_t),
+# W [8192 x 2048], X [2048 x 4096]
 # ---------------------------------------------------------------------------
 
 def test_ffn_up_nm24_full():
@@ -86,6 +87,15 @@ def test_ffn_up_nm24_full():
     _check_rows(C, A64[rows], X64, rows, "ffn_up spmm_nm")
     cols = _sample(Nc, 24, 12)
     _check_cols(C, A64, X64[:, cols], cols, "ffn_up spmm_nm")
+    del C
+
+    # the same product from the K-contiguous activations: nm_transpose, then spmm_nm_t
+    Xt = nm.transpose(Xd)
+    assert np.array_equal(host(Xt[:64]), np.ascontiguousarray(X[:, :64].T))
+    C = nm.spmm_nm_t(vals, meta, K, Xt)
+    _finite(C, "spmm_nm_t")
+    _check_rows(C, A64[rows], X64, rows, "ffn_up spmm_nm_t")
+    _check_cols(C, A64, X64[:, cols], cols, "ffn_up spmm_nm_t")
 
 
 # ---------------------------------------------------------------------------
@@ -181,6 +191,10 @@ def test_train_step_nm24_full():
     rows = _sample(dff, 32, 41)
     Ws_rows = O.decode(O.decompress_nm(wv[rows], wm[rows], len(rows), dm, 2, 4), "bf16")
     _check_rows(Y, Ws_rows, X64, rows, "train Y")
+    del Y
+    Y = nm.spmm_nm_t(vals, meta, dm, nm.transpose(Xd))
+    _finite(Y, "Y (spmm_nm_t)")
+    _check_rows(Y, Ws_rows, X64, rows, "train Y (spmm_nm_t)")
     del Y
 
     # dX = W_ds^T dY

@@ -63,6 +63,31 @@ def test_prune_compress_decompress(N, M, R, K, dtype, kind, pad):
     assert host(out).tobytes() == O.decompress_nm(wv, wm, R, K, N, M).tobytes()
 
 
+FUSED_CASES = [(2, 4, 37, 48), (2, 4, 300, 1024), (2, 4, 513, 2064), (2, 4, 8, 16), (2, 4, 5, 44), (2, 8, 33, 88),
+               (4, 16, 17, 96)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["ties", "normal"])
+@pytest.mark.parametrize("N,M,R,K", FUSED_CASES, ids=[f"{n}of{m}_{r}x{k}" for n, m, r, k in FUSED_CASES])
+@pytest.mark.parametrize("pad", [0, 16])
+def test_prune_compress_fused(N, M, R, K, dtype, kind, pad):
+    """nm_prune_compress: mask, values and metadata byte-identical to the oracle (2:4 with K % 16 == 0
+    runs the one-pass kernel, the rest the two passes)."""
+    raw = _inputs(kind, (R, K), seed=R * 5 + K + N, dtype=dtype)
+    A = dev(raw, dtype, pad=pad)
+    mask_t = torch.full((R, K + pad), 7, dtype=torch.uint8, device="cuda")[:, :K]
+    mask, vals, meta = nm.nm_prune_compress(A, N, M, mask=mask_t)
+    want = O.prune_nm(raw, dtype, N, M)
+    assert np.array_equal(host(mask), want)
+    wv, wm, bad = O.compress_nm(raw, want, N, M)
+    assert bad == 0
+    assert host(vals).tobytes() == wv.tobytes()
+    assert np.array_equal(host(meta), wm)
+    if pad:
+        assert bool((mask_t.as_strided((R, pad), (K + pad, 1), K) == 7).all())   # padding untouched
+
+
 def test_compress_bad_groups():
     raw = synth.normal((64, 64), 5, dtype="bf16")
     mask = O.prune_nm(raw, "bf16", 2, 4)
@@ -154,6 +179,87 @@ def test_spmm_nm_deterministic():
     c1 = nm.spmm_nm(v, m, K, B)
     c2 = nm.spmm_nm(v, m, K, B)
     assert torch.equal(c1, c2)
+
+
+# ---------------------------------------------------------------------------
+# spmm_nm_t (dense operand given K-contiguous) and nm_transpose
+# ---------------------------------------------------------------------------
+
+SPMM_T_CASES = [
+    # (R, K, Nc, pad_bt, pad_c): the pipelined kernel needs K % 256 == 0 (bf16); the rest runs the
+    # SIMT kernel
+    (300, 512, 136, 0, 0),
+    (1000, 2048, 520, 8, 0),
+    (520, 1024, 264, 0, 4),
+    (256, 256, 256, 0, 0),
+    (64, 768, 8, 0, 0),
+    (17, 132, 40, 0, 0),      # K % 256 != 0: generic kernel
+    (40, 192, 13, 3, 1),
+]
+
+
+@pytest.fixture(params=["dma", "generic"])
+def tier_t(request, monkeypatch):
+    if request.param == "generic":
+        monkeypatch.setenv("NMSPARSE_FORCE_GENERIC", "1")
+    return request.param
+
+
+@pytest.mark.parametrize("R,K,Nc,pb,pc", SPMM_T_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SPMM_T_CASES])
+@pytest.mark.parametrize("kind", ["normal", "ints"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_spmm_nm_t(R, K, Nc, pb, pc, kind, dtype, tier_t):
+    raw = _inputs(kind, (R, K), seed=R + K + 5, dtype=dtype)
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, dtype, 2, 4), 2, 4)
+    Btraw = _inputs(kind, (Nc, K), seed=Nc + 7, dtype=dtype)
+    Cbuf = torch.full((R, Nc + pc), float("nan"), dtype=torch.float32, device="cuda")
+    C = host(nm.spmm_nm_t(dev(vals, dtype), dev(meta, "u8"), K, dev(Btraw, dtype, pad=pb), out=Cbuf[:, :Nc]))
+    Braw = np.ascontiguousarray(Btraw.T)
+    Cref = O.spmm_nm(vals, meta, R, K, Braw, dtype)
+    if kind == "ints" and K <= 1024:
+        assert np.array_equal(C, Cref)     # every partial sum is an exact fp32 integer
+    A64 = O.decode(O.decompress_nm(vals, meta, R, K, 2, 4), dtype)
+    check_close(C, Cref, O.abs_bound(A64, O.decode(Braw, dtype)), f"spmm_nm_t {R}x{K}x{Nc}")
+    if pc:
+        assert torch.isnan(Cbuf[:, Nc:]).all()   # the padding columns are untouched
+
+
+TRANSPOSE_CASES = [(64, 64, 0), (2048, 520, 0), (300, 136, 8), (17, 40, 0), (13, 7, 3), (1, 96, 0), (520, 1, 0)]
+
+
+@pytest.mark.parametrize("R,C,pad", TRANSPOSE_CASES, ids=[f"{c[0]}x{c[1]}" for c in TRANSPOSE_CASES])
+def test_transpose(R, C, pad):
+    raw = synth.normal((R, C), R * 31 + C, dtype="bf16")
+    got = host(nm.transpose(dev(raw, "bf16", pad=pad)))
+    assert np.array_equal(got, np.ascontiguousarray(raw.T))
+
+
+def test_transpose_then_spmm_nm_t_matches_spmm_nm():
+    # the two layouts of the same product: identical fp32 results (same kernel arithmetic order
+    # is not promised, so compare against the oracle and against each other within tolerance)
+    R, K, Nc = 512, 1024, 384
+    raw = synth.normal((R, K), 77, dtype="bf16")
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, "bf16", 2, 4), 2, 4)
+    Braw = synth.normal((K, Nc), 78, dtype="bf16")
+    v, m, B = dev(vals, "bf16"), dev(meta, "u8"), dev(Braw, "bf16")
+    C1 = host(nm.spmm_nm(v, m, K, B))
+    C2 = host(nm.spmm_nm_t(v, m, K, nm.transpose(B)))
+    Cref = O.spmm_nm(vals, meta, R, K, Braw, "bf16")
+    bound = O.abs_bound(O.decode(O.decompress_nm(vals, meta, R, K, 2, 4), "bf16"), O.decode(Braw, "bf16"))
+    check_close(C1, Cref, bound, "spmm_nm")
+    check_close(C2, Cref, bound, "transpose + spmm_nm_t")
+
+
+def test_spmm_nm_t_rejects_bad_arguments():
+    m = torch.zeros((8, 2), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):            # Bt must have K columns
+        nm.spmm_nm_t(torch.zeros((8, 8), dtype=torch.bfloat16, device="cuda"), m, 12,
+                     torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(nm.NmError):            # K % 4 != 0: NM_ERR_SHAPE from the C ABI
+        nm.spmm_nm_t(torch.zeros((8, 7), dtype=torch.bfloat16, device="cuda"), m, 14,
+                     torch.zeros((8, 14), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(nm.NmError):            # bf16 only: NM_ERR_UNSUPPORTED
+        nm.transpose(torch.zeros((4, 4), dtype=torch.float32, device="cuda"))
 
 
 # ---------------------------------------------------------------------------
