@@ -288,8 +288,7 @@ __global__ __launch_bounds__(256) void nm_compress24_vec_kernel(const T* __restr
     T* vd = values + r * (K / 2) + c0 / 2;
 #pragma unroll
     for (int q = 0; q < NA / 2; ++q)
-      __builtin_nontemporal_store(u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]},
-                                  reinterpret_cast<u32x4*>(vd) + q);
+      reinterpret_cast<u32x4*>(vd)[q] = u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
     *reinterpret_cast<uint16_t*>(meta + r * (K / 8) + c0 / 8) = (uint16_t)nibs;
   }
   if (bad_groups != nullptr && bad > 0) atomicAdd(bad_groups, bad);
@@ -300,7 +299,9 @@ __global__ __launch_bounds__(256) void nm_compress24_vec_kernel(const T* __restr
 // nm_compress in one pass over A (one read of A instead of two, no read of the mask).  One thread
 // per 16 elements (4 groups) and kFusedU such chunks, all loaded before any is ranked: 16-byte
 // loads of A, one 16-byte store of the chunk's mask bytes, one 16- or 32-byte store of its 8 kept
-// values and one 2-byte store of its 4 nibbles.
+// values and one 2-byte store of its 4 nibbles.  Values and metadata are written with ordinary
+// stores (the SpMM reads them next and finds them in the last-level cache); the mask, which
+// nothing in the step reads, with non-temporal ones.
 // ---------------------------------------------------------------------------
 constexpr int kFusedU = 2;
 
@@ -359,8 +360,7 @@ __global__ __launch_bounds__(256) void nm_prune_compress24_vec_kernel(const T* _
     T* vd = values + r * (K / 2) + c0 / 2;
 #pragma unroll
     for (int q = 0; q < NA / 2; ++q)
-      __builtin_nontemporal_store(u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]},
-                                  reinterpret_cast<u32x4*>(vd) + q);
+      reinterpret_cast<u32x4*>(vd)[q] = u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
     *reinterpret_cast<uint16_t*>(meta + r * (K / 8) + c0 / 8) = (uint16_t)nibs;
   }
 }

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int l32 = lane & 31, aa = lane >> 5;
-  auto step = [&](int kt) {
+  auto step = [&](int kt, auto issue_batch) {
     const int s = kt & 1, u = kt & 3;
     const unsigned char* As = smem + Cfg::OFF_A + ((kt >> 1) & 1) * Cfg::SA;
     const unsigned char* Ms = smem + Cfg::OFF_M + ((kt >> 2) & 1) * Cfg::SM;
@@ -178,6 +178,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
       const int r = (wm * FM + i) * 32 + l32;
       mm[i] = *reinterpret_cast<const u32x2*>(Ms + r * 32 + (nt_mpos(r, u >> 1) << 4) + 8 * (u & 1));
     }
+    issue_batch();
     operands(0);
     __builtin_amdgcn_sched_barrier(0);
     operands(1);
@@ -197,10 +198,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
   auto body = [&](int kt, auto wait) {
     wait();
     lds_barrier();   // step kt's operands are in LDS for every wave; every wave is done with step kt-1
-    issue_b((kt + 1) & 1, kt + 1 < KT ? kt + 1 : KT - 1);
-    if ((kt & 1) == 0) issue_a(((kt >> 1) + 1) & 1, (kt >> 1) + 1 <= jlast ? (kt >> 1) + 1 : jlast);
-    if ((kt & 3) == 0) issue_m(((kt >> 2) + 1) & 1, (kt >> 2) + 1 <= clast ? (kt >> 2) + 1 : clast);
-    step(kt);
+    step(kt, [&] {
+      issue_b((kt + 1) & 1, kt + 1 < KT ? kt + 1 : KT - 1);
+      if ((kt & 1) == 0) issue_a(((kt >> 1) + 1) & 1, (kt >> 1) + 1 <= jlast ? (kt >> 1) + 1 : jlast);
+      if ((kt & 3) == 0) issue_m(((kt >> 2) + 1) & 1, (kt >> 2) + 1 <= clast ? (kt >> 2) + 1 : clast);
+    });
   };
   for (int kt = 0; kt < KT; kt += 4) {
     body(kt, [] { wait_vmcnt<0>(); });
@@ -255,7 +257,9 @@ hipError_t launch_spmm_nm_nt_dma(const void* values, const uint8_t* meta, int64_
 // 16-byte stores.  The 64 lanes of a wave cover a 64 x 64 tile (lanes 8b..8b+7
 // take row block b), so both the loads and the stores of a wave cover whole
 // 128-byte runs.  Edges (rows or columns not a multiple of 8) take the
-// element-wise path.
+// element-wise path.  The result is written with ordinary stores: the SpMM reads
+// it right after, and non-temporal stores (which bypass the last-level cache)
+// made that SpMM ~11% slower at 8192 x 2048 x 4096.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void nm_transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                                 int64_t R, int64_t Cn, uint16_t* __restrict__ dst,
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(256) void nm_transpose_bf16_kernel(const uint16_t* 
       u32x4 d;
 #pragma unroll
       for (int j = 0; j < 4; ++j) d[j] = __builtin_amdgcn_perm(v[2 * j + 1][e >> 1], v[2 * j][e >> 1], sel);
-      __builtin_nontemporal_store(d, reinterpret_cast<u32x4*>(dst + (c0 + e) * ldd + r0));
+      *reinterpret_cast<u32x4*>(dst + (c0 + e) * ldd + r0) = d;
     }
   } else {
     for (int q = 0; q < 8 && r0 + q < R; ++q)
