@@ -142,7 +142,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int l32 = lane & 31, aa = lane >> 5;
-  auto step = [&](int kt, auto issue_batch) {
+  auto step = [&](int kt, auto issue_b_next, auto issue_am_next) {
     const int s = kt & 1, u = kt & 3;
     const unsigned char* As = smem + Cfg::OFF_A + ((kt >> 1) & 1) * Cfg::SA;
     const unsigned char* Ms = smem + Cfg::OFF_M + ((kt >> 2) & 1) * Cfg::SM;
@@ -178,12 +178,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
       const int r = (wm * FM + i) * 32 + l32;
       mm[i] = *reinterpret_cast<const u32x2*>(Ms + r * 32 + (nt_mpos(r, u >> 1) << 4) + 8 * (u & 1));
     }
-    issue_batch();
+    // Bt of the next step is issued first (one step of lookahead); the values and metadata stages
+    // (two and four steps ahead) only once the first half's matrix instructions are issued, so
+    // that they do not delay the Bt loads
+    issue_b_next();
     operands(0);
     __builtin_amdgcn_sched_barrier(0);
     operands(1);
     mfma(0);
     __builtin_amdgcn_sched_barrier(0);
+    issue_am_next();
     mfma(1);
   };
 
@@ -198,11 +202,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
   auto body = [&](int kt, auto wait) {
     wait();
     lds_barrier();   // step kt's operands are in LDS for every wave; every wave is done with step kt-1
-    step(kt, [&] {
-      issue_b((kt + 1) & 1, kt + 1 < KT ? kt + 1 : KT - 1);
+    auto am = [&] {
       if ((kt & 1) == 0) issue_a(((kt >> 1) + 1) & 1, (kt >> 1) + 1 <= jlast ? (kt >> 1) + 1 : jlast);
       if ((kt & 3) == 0) issue_m(((kt >> 2) + 1) & 1, (kt >> 2) + 1 <= clast ? (kt >> 2) + 1 : clast);
-    });
+    };
+    step(kt, [&] { issue_b((kt + 1) & 1, kt + 1 < KT ? kt + 1 : KT - 1); }, am);
   };
   for (int kt = 0; kt < KT; kt += 4) {
     body(kt, [] { wait_vmcnt<0>(); });
