@@ -204,6 +204,10 @@ def test_train_step_nm24_full():
     Wt_rows = O.decode(O.decompress_nm(wvt[rows], wmt[rows], len(rows), dff, 2, 4), "bf16")
     _check_rows(dX, Wt_rows, O.decode(dY, "bf16"), rows, "train dX")
     del dX
+    dX = nm.spmm_nm_t(vt, mt, dff, nm.transpose(dYd))
+    _finite(dX, "dX (spmm_nm_t)")
+    _check_rows(dX, Wt_rows, O.decode(dY, "bf16"), rows, "train dX (spmm_nm_t)")
+    del dX
 
     # dW = (dY X^T) read at W_s's kept positions
     dW = nm.sddmm_nm(dYd, Xd, meta)
