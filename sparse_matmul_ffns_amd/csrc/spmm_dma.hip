@@ -33,8 +33,14 @@
 //    ds_read_b128 operand reads are free of bank conflicts;
 //  * two LDS buffers for B, two A super-stages, and two register sets for B:
 //    the B loads of steps k+1 and k+2 are in flight while step k runs on the
-//    matrix cores (one wave per SIMD, accumulators in AGPRs, 128 x 128 per wave
-//    for 2:4); B of step k+1 is written to LDS after step k's instructions.
+//    matrix cores; B of step k+1 is written to LDS after step k's instructions.
+//    Tiles: 2:4 256 x 256 with one wave per SIMD (128 x 128 per wave,
+//    accumulators in AGPRs); V:N:M with V % 128 == 0 128 x 256, one wave per
+//    SIMD; other V:N:M 64 x 512 with two waves per SIMD (64 x 64 per wave): a
+//    64-row block reuses each gathered B row only 64 times, so the L2 -> LDS
+//    stream per matrix instruction is large, and the second wave per SIMD
+//    keeps more LDS reads and loads in flight (19% faster at 2048 x 8192 x 4096,
+//    V=64, than 64 x 256 with one wave per SIMD).
 //    All loads are issued from inline assembly and waited for with explicit
 //    vmcnt counts.
 // Epilogue: each (fragment, element) store covers 128 contiguous bytes of a
@@ -99,11 +105,11 @@ struct SpCfg {
   static constexpr int L_B = B_ROWS;                     // vmcnt of a step's B row loads
   static_assert(AV_BYTES % (1024 * NW) == 0 && AV_INSTR >= 1, "A blocks per wave");
   static_assert(AM_LANES >= 1 && AM_LANES <= 64 && BM % NW == 0, "metadata lanes per wave");
-  static_assert(8 * (BN / 8) == NT, "one (8 k x 8 column) B block per lane: 8 chunks x BN/8 column blocks");
+  static_assert(BN == NT, "one (8 k x 8 column) B block per lane: 8 chunks x BN/8 column blocks");
   static_assert(WM % 32 == 0 && WN % 32 == 0 && FM >= 1 && FN >= 1, "fragments");
   static_assert(L_A + L_B <= 63, "vmcnt range");
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert(BN == 256 && NW == 4, "a wave's B blocks: two 8-k chunks (lanes 0-31, 32-63) of 32 column blocks");
+  static_assert(NW == 4 || NW == 8, "a wave's B blocks: two 8-k chunks (lanes 0-31, 32-63) of 32 column blocks");
 };
 
 // 16-byte chunk position of chunk c in A row r (rows are 128 bytes = 8 chunks).  The two rows
@@ -173,10 +179,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
     if (Cfg::AM_LANES == 64 || lane < Cfg::AM_LANES) dma16(m_src + (int64_t)j * 16, dst);
   };
 
-  // ---- B: lane l of wave w owns k chunk bc = 2w + l/32 (k = 8bc .. 8bc+7 of the step) and
-  //      column block bcb = l%32 (columns 8bcb .. 8bcb+7 of the tile) ----
-  const int bc = 2 * wave + (lane >> 5);
-  const int bcb = lane & 31;
+  // ---- B: lane l of wave w owns k chunk bc = 2(w%4) + l/32 (k = 8bc .. 8bc+7 of the step) and
+  //      column block bcb = l%32 + 32(w/4) (columns 8bcb .. 8bcb+7 of the tile) ----
+  const int bc = 2 * (wave & 3) + (lane >> 5);
+  const int bcb = (lane & 31) + 32 * (wave >> 2);
   int64_t b_col = n0 + 8 * bcb;
   b_col = b_col < Nc ? b_col : 0;          // columns past Nc: any valid data, never stored
 
@@ -184,9 +190,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_dma_kernel(
     const int64_t k0 = (int64_t)kt * 64;
     int64_t rows[8];
     if constexpr (VENOM) {
-      // 16 groups per step; the wave's lanes cover groups 4w .. 4w+3 (two per chunk): one
+      // 16 groups per step; the wave's lanes cover groups 4(w%4) .. 4(w%4)+3 (two per chunk): one
       // wave-uniform (scalar) load of their 16 column bytes.  k0 + 64 <= Kd, so all 16 exist.
-      const int64_t g_first = (k0 >> 2) + 4 * wave;
+      const int64_t g_first = (k0 >> 2) + 4 * (wave & 3);
       const u32x4 sel4 = *reinterpret_cast<const u32x4*>(colsel + 4 * (vblk * G + g_first));
       const uint32_t s_lo = (lane >> 5) ? sel4[2] : sel4[0];
       const uint32_t s_hi = (lane >> 5) ? sel4[3] : sel4[1];
@@ -362,7 +368,7 @@ hipError_t launch_spmm_venom_dma(const void* values, const uint8_t* meta, const 
                                  float* C, int64_t ldc, hipStream_t s) {
   if (V % 128 == 0)
     return run_dma<128, 256, 1, 4, true>(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
-  return run_dma<64, 256, 1, 4, true>(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
+  return run_dma<64, 512, 1, 8, true>(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
 }
 
 }  // namespace nms

@@ -292,7 +292,7 @@ def test_prune_act_venom(R, K, V, M, relu, dtype):
 
 
 SPMM_VENOM_CASES = [(256, 1024, 264, 64, 8), (384, 512, 136, 128, 8), (48, 96, 40, 3, 16), (128, 136, 64, 64, 8),
-                    (512, 2048, 512, 128, 8), (128, 256, 72, 64, 4), (64, 512, 256, 64, 16)]
+                    (512, 2048, 512, 128, 8), (128, 256, 72, 64, 4), (64, 512, 256, 64, 16), (192, 1024, 1096, 64, 8)]
 
 
 @pytest.mark.parametrize("R,K,Nc,V,M", SPMM_VENOM_CASES,
