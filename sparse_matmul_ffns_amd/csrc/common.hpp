@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace nms {
 
@@ -103,5 +104,13 @@ __device__ inline int xcd_remap(int wg, int nwg) {
   const int per = nwg / nx;
   return (wg % nx) * per + (wg / nx);
 }
+
+// Host-side knob, read on every call: NMSPARSE_FORCE_GENERIC=1 makes every call take its
+// plain SIMT kernel instead of the tiled ones (the tests compare the two).
+inline bool env_is_one(const char* name) {
+  const char* e = getenv(name);
+  return e && e[0] == '1';
+}
+inline bool force_generic() { return env_is_one("NMSPARSE_FORCE_GENERIC"); }
 
 }  // namespace nms

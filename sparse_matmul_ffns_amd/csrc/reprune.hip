@@ -5,7 +5,9 @@
 // W_s [R x K] (compressed along K) is decompressed with +0.0 fill, transposed
 // and pruned 2:4 along R, giving W_ds^T [K x R] compressed along R.
 //
-// One workgroup owns a 128-row x 64-column tile of W_s:
+// bf16 operands whose sides are multiples of 128 take the tiled kernel below
+// (reprune_t_bf16_kernel); the others this one, where one workgroup owns a
+// 128-row x 64-column tile of W_s:
 //   1. each lane decompresses 4 groups (16 columns of one row) into LDS;
 //   2. each lane takes 16 consecutive rows of one column (4 output groups),
 //      keeps 2 of every 4 by magnitude (lower row on ties) and writes 8 values
@@ -121,10 +123,128 @@ __global__ __launch_bounds__(256) void reprune_t_kernel(const T* __restrict__ va
   }
 }
 
+// bf16 tiles of 128 rows x 128 columns of W_s, whole 128-byte lines in and out.
+//   1. Unit (row r, 16-column chunk c): lane l of a wave takes chunk l%8 of row l/8 + 8i, so each
+//      load instruction reads 8 whole 128-byte rows of values; the four units of a lane are
+//      loaded one tile ahead, while the workgroup works on the previous tile.  The 16 dense
+//      columns are written to LDS as two 16-byte runs; the LDS row holds the 128 columns as 64
+//      dwords, run c of row r at dword 8(c ^ s(r)), s(r) = (r / 16) % 8.
+//   2. Unit (column pair j, 16-row chunk ch), chunk fastest: 16 dword reads give both columns of
+//      16 rows (the lanes of one read hit 64 distinct banks through the XOR); each column's 4
+//      groups of 4 rows keep their 2 largest magnitudes; the 8 lanes of a pair write 128
+//      contiguous bytes of each of the two output rows.
+constexpr int RB_TILE = 128;
+
+__global__ __launch_bounds__(256) void reprune_t_bf16_kernel(const uint16_t* __restrict__ values,
+                                                             const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+                                                             uint16_t* __restrict__ values_t,
+                                                             uint8_t* __restrict__ meta_t) {
+  __shared__ uint32_t tile[RB_TILE * 64];
+  const int tid = threadIdx.x;
+  const int64_t vrow = K / 2, mrow = K / 8;
+  const uint32_t nbx = (uint32_t)(R / RB_TILE), ntiles = nbx * (uint32_t)(K / RB_TILE);
+
+  // a workgroup walks tiles t, t + gridDim.x, ...; the next tile's loads are in flight while the
+  // current one is re-pruned and written
+  u32x4 v[4];
+  uint32_t m[4];
+  // tile t -> logical tile L: each XCD (workgroups t % 8) takes a contiguous range of logical
+  // tiles, so the 8 neighbouring tiles whose 16-byte metadata runs share one 128-byte output
+  // line are written through one L2
+  const bool remap = ntiles % 8 == 0;
+  auto logical = [&](uint32_t t) { return remap ? (t % 8) * (ntiles / 8) + t / 8 : t; };
+  auto load = [&](uint32_t t) {
+    t = logical(t);
+    const int64_t r0 = (int64_t)(t % nbx) * RB_TILE, k0 = (int64_t)(t / nbx) * RB_TILE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i;
+      const int64_t row = r0 + (u >> 3);
+      const int c = u & 7;
+      v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(values + row * vrow + k0 / 2 + 8 * c));
+      m[i] = *reinterpret_cast<const uint16_t*>(meta + row * mrow + k0 / 8 + 2 * c);
+    }
+  };
+  if (blockIdx.x < ntiles) load(blockIdx.x);
+  for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const uint32_t lt = logical(t);
+    const int64_t r0 = (int64_t)(lt % nbx) * RB_TILE, k0 = (int64_t)(lt / nbx) * RB_TILE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i;
+      const int r = u >> 3, c = u & 7;
+      uint32_t d[8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t nib = (m[i] >> (4 * g)) & 0xF;
+        const uint32_t p0 = nib & 3, p1 = nib >> 2;
+        const uint32_t a = v[i][g] & 0xFFFF, b = v[i][g] >> 16;
+        uint32_t x[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) x[p] = (p == (int)p1) ? b : ((p == (int)p0) ? a : 0u);
+        d[2 * g] = x[0] | (x[1] << 16);
+        d[2 * g + 1] = x[2] | (x[3] << 16);
+      }
+      // odd rows write their second 16-byte half first: the 16 lanes of two rows then cover all
+      // 64 banks in each write
+      uint32_t* dst = tile + r * 64 + 8 * (c ^ ((r >> 4) & 7));
+      const bool odd = r & 1;
+      *reinterpret_cast<u32x4*>(dst + (odd ? 4 : 0)) =
+          odd ? u32x4{d[4], d[5], d[6], d[7]} : u32x4{d[0], d[1], d[2], d[3]};
+      *reinterpret_cast<u32x4*>(dst + (odd ? 0 : 4)) =
+          odd ? u32x4{d[0], d[1], d[2], d[3]} : u32x4{d[4], d[5], d[6], d[7]};
+    }
+    if (t + gridDim.x < ntiles) load(t + gridDim.x);
+    __syncthreads();
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i;
+      const int ch = u & 7, j = u >> 3;
+      uint32_t x[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] = tile[(16 * ch + e) * 64 + (j ^ (8 * ch))];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        // the column's 16-bit halves of rows 4h..4h+3 packed as (d23:d01); value q is bytes 2q, 2q+1
+        const uint32_t pick = half ? 0x07060302u : 0x05040100u;
+        uint32_t out[4];
+        uint32_t nibs = 0;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t d01 = __builtin_amdgcn_perm(x[4 * h + 1], x[4 * h], pick);
+          const uint32_t d23 = __builtin_amdgcn_perm(x[4 * h + 3], x[4 * h + 2], pick);
+          const uint32_t nib = select24(Elem<uint16_t>::key((uint16_t)(d01 & 0xFFFF)),
+                                        Elem<uint16_t>::key((uint16_t)(d01 >> 16)),
+                                        Elem<uint16_t>::key((uint16_t)(d23 & 0xFFFF)),
+                                        Elem<uint16_t>::key((uint16_t)(d23 >> 16)));
+          const uint32_t q0 = nib & 3, q1 = nib >> 2;
+          out[h] = __builtin_amdgcn_perm(d23, d01, (q0 * 0x202u + 0x100u) | ((q1 * 0x202u + 0x100u) << 16));
+          nibs |= nib << (4 * h);
+        }
+        const int64_t orow = k0 + 2 * j + half;
+        *reinterpret_cast<u32x4*>(values_t + orow * (R / 2) + (r0 + 16 * ch) / 2) =
+            u32x4{out[0], out[1], out[2], out[3]};
+        *reinterpret_cast<uint16_t*>(meta_t + orow * (R / 8) + (r0 + 16 * ch) / 8) = (uint16_t)nibs;
+      }
+    }
+    __syncthreads();   // every lane is done with the tile before the next one is written
+  }
+}
+
 template <typename T>
 static hipError_t reprune_dispatch(const void* values, const uint8_t* meta, int64_t R, int64_t K, void* values_t,
                                    uint8_t* meta_t, hipStream_t s) {
   const int esz = sizeof(T);
+  if (esz == 2 && R % RB_TILE == 0 && K % RB_TILE == 0 && (uintptr_t)values % 16 == 0 && (uintptr_t)meta % 2 == 0 &&
+      (uintptr_t)values_t % 16 == 0 && (uintptr_t)meta_t % 2 == 0 && !force_generic()) {
+    // four 32 KB workgroups per CU
+    const int64_t ntiles = (R / RB_TILE) * (K / RB_TILE);
+    const unsigned grid = (unsigned)(ntiles < 1024 ? ntiles : 1024);   // ntiles < 2^32: R, K < 2^31
+    hipLaunchKernelGGL(reprune_t_bf16_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t*)values, meta, R, K,
+                       (uint16_t*)values_t, meta_t);
+    return hipGetLastError();
+  }
   const int vec_in = ((uintptr_t)values % 16 == 0) && (((K / 2) * esz) % 16 == 0);
   const int vec_out = ((uintptr_t)values_t % 16 == 0) && (((R / 2) * esz) % 16 == 0);
   dim3 grid((unsigned)((R + RP_ROWS - 1) / RP_ROWS), (unsigned)((K + RP_COLS - 1) / RP_COLS));

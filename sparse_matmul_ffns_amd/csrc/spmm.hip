@@ -347,15 +347,10 @@ static bool fast_ok(const void* values, const uint8_t* meta, const void* B, int6
          (uintptr_t)meta % 2 == 0 && (uintptr_t)B % 16 == 0 && (uintptr_t)C % 16 == 0;
 }
 
-// Kernel selection knobs, read on every call (for A/B tests of the tiers):
+// Kernel selection knob, read on every call (for A/B tests of the tiers):
 // NMSPARSE_SPMM_TIER=1 skips the pipelined DMA kernel (register-staged SMFMAC
-// kernel instead); NMSPARSE_FORCE_GENERIC=1 uses the SIMT kernel everywhere.
-static bool env_is_one(const char* name) {
-  const char* e = getenv(name);
-  return e && e[0] == '1';
-}
+// kernel instead); NMSPARSE_FORCE_GENERIC (common.hpp) selects the SIMT kernel.
 static int kernel_tier() { return env_is_one("NMSPARSE_SPMM_TIER") ? 1 : 0; }
-static bool force_generic() { return env_is_one("NMSPARSE_FORCE_GENERIC"); }
 
 hipError_t launch_spmm_nm(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* B,
                           int64_t ldb, int64_t Nc, float* C, int64_t ldc, hipStream_t s) {

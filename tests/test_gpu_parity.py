@@ -315,7 +315,7 @@ def test_spmm_venom(R, K, Nc, V, M, kind, tier):
 # nm_reprune_t / sddmm_nm
 # ---------------------------------------------------------------------------
 
-REPRUNE_CASES = [(132, 68), (256, 512), (16, 16), (300, 200), (4, 4), (1024, 128)]
+REPRUNE_CASES = [(132, 68), (256, 512), (16, 16), (300, 200), (4, 4), (1024, 128), (384, 640)]
 
 
 @pytest.mark.parametrize("R,K", REPRUNE_CASES, ids=[f"{r}x{k}" for r, k in REPRUNE_CASES])
