@@ -224,6 +224,30 @@ def test_spmm_nm_t(R, K, Nc, pb, pc, kind, dtype, tier_t):
         assert torch.isnan(Cbuf[:, Nc:]).all()   # the padding columns are untouched
 
 
+@pytest.mark.parametrize("kind", ["normal", "ints"])
+def test_spmm_nm_t_many_tiles(kind):
+    """1024 whole 256 x 256 tiles, four rounds of workgroups on the chip.  Checked on two rows of
+    every 256-row block (all column tiles of each row tile) and on 24 columns (all row tiles),
+    against the oracle's dense rows and columns."""
+    R, K, Nc = 2048, 1024, 32768
+    raw = _inputs(kind, (R, K), seed=91, dtype="bf16")
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, "bf16", 2, 4), 2, 4)
+    Btraw = _inputs(kind, (Nc, K), seed=92, dtype="bf16")
+    C = nm.spmm_nm_t(dev(vals, "bf16"), dev(meta, "u8"), K, dev(Btraw, "bf16"))
+    A64 = O.decode(O.decompress_nm(vals, meta, R, K, 2, 4), "bf16")
+    B64 = O.decode(np.ascontiguousarray(Btraw.T), "bf16")
+    rng = np.random.default_rng(93)
+    rows = np.sort(np.concatenate([256 * t + rng.choice(256, 2, replace=False) for t in range(R // 256)]))
+    cols = np.sort(rng.choice(Nc, 24, replace=False))
+    got_r = host(C[torch.as_tensor(rows, device=C.device)])
+    got_c = host(C[:, torch.as_tensor(cols, device=C.device)])
+    want_r, want_c = A64[rows] @ B64, A64 @ B64[:, cols]
+    if kind == "ints":
+        assert np.array_equal(got_r, want_r) and np.array_equal(got_c, want_c)
+    check_close(got_r, want_r, O.abs_bound(A64[rows], B64), "spmm_nm_t many tiles rows")
+    check_close(got_c, want_c, O.abs_bound(A64, B64[:, cols]), "spmm_nm_t many tiles columns")
+
+
 TRANSPOSE_CASES = [(64, 64, 0), (2048, 520, 0), (300, 136, 8), (17, 40, 0), (13, 7, 3), (1, 96, 0), (520, 1, 0)]
 
 
