@@ -4,11 +4,11 @@
 
 A step is one pass of the hot path over the workload's synthetic inputs
 (already resident in HBM when the timed region starts):
-  ffn_up_nm24_8192x2048x4096 (default): nm_prune_compress (the 2:4 mask and
-      the compressed weight in one pass) -> nm_transpose -> spmm_nm_t of a
+  ffn_up_nm24_8192x2048x4096 (default): nm_prune_compress_transpose (the 2:4
+      mask and the compressed weight in one pass over the weight, and the
+      activations turned K-contiguous, in one launch) -> spmm_nm_t of a
       bf16 2:4 weight [8192 x 2048] ~ N(0, 0.02)
-      with activations [2048 x 4096] ~ N(0, 1) (turned K-contiguous by the
-      transpose inside the step);
+      with activations [2048 x 4096] ~ N(0, 1);
   ffn_down_vnm64_2_8_2048x8192x4096: prune_act_venom (V=64, M=8) -> spmm_venom;
   train_step_nm24_dmodel4096_dff16384_tok8192: nm_reprune_t -> nm_transpose
       (X) -> spmm_nm_t (Y) -> nm_transpose (dY) -> spmm_nm_t (dX) -> sddmm_nm
@@ -95,20 +95,20 @@ def _w_nm(w, dtype):
     vals = torch.empty((R, nv // R), dtype=A.dtype, device="cuda")
     meta = torch.empty((R, mb // R), dtype=torch.uint8, device="cuda")
     C = torch.empty((R, Nc), dtype=torch.float32, device="cuda")
-    # selection and compression of the weight in one pass (nm_prune_compress writes the mask and
-    # the values + metadata, byte-identical to nm_prune followed by nm_compress)
-    steps = [("nm_prune_compress", lambda: nm.nm_prune_compress(A, 2, 4, mask=mask, values=vals, meta=meta))]
     if dtype == "bf16":
-        # the activations are turned K-contiguous once (nm_transpose), then spmm_nm_t streams both
-        # operands into LDS as whole rows
+        # one launch selects and compresses the weight (the mask and the values + metadata,
+        # byte-identical to nm_prune then nm_compress) and turns the activations K-contiguous
+        # (nm_transpose); spmm_nm_t then streams both operands into LDS as whole rows
         Bt = torch.empty((Nc, K), dtype=B.dtype, device="cuda")
-        steps += [
-            ("nm_transpose", lambda: nm.transpose(B, out=Bt)),
+        steps = [
+            ("nm_prune_compress_transpose",
+             lambda: nm.nm_prune_compress_transpose(A, B, 2, 4, mask=mask, values=vals, meta=meta, Bt=Bt)),
             ("spmm_nm_t", lambda: nm.spmm_nm_t(vals, meta, K, Bt, out=C)),
         ]
         kernel = "spmm_nm_t"
     else:
-        steps += [("spmm_nm", lambda: nm.spmm_nm(vals, meta, K, B, out=C))]
+        steps = [("nm_prune_compress", lambda: nm.nm_prune_compress(A, 2, 4, mask=mask, values=vals, meta=meta)),
+                 ("spmm_nm", lambda: nm.spmm_nm(vals, meta, K, B, out=C))]
         kernel = "spmm_nm"
     flops = {kernel: 2.0 * R * K * Nc}
     algo = {kernel: ("mfma", R * (K // 2) * Nc * 2.0)}

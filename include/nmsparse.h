@@ -118,6 +118,25 @@ nm_status nm_prune_compress(nm_dtype dt, const void* A, int64_t lda, int64_t R, 
                             nm_stream stream);
 
 /*
+ * nm_prune_compress_transpose -- nm_prune_compress of A and nm_transpose of B
+ * in one launch: the two passes that prepare the 2:4 product of an FFN layer
+ * ("Success story: ESPLAG", Solution: the weight pruned to 2:4 and stored
+ * compressed; the activations then feed spmm_nm_t K-contiguous).
+ *   A, mask, values, meta as for nm_prune_compress;
+ *   B [KB][ldb] dense input, Bt [Nc][ldbt] output (ldbt >= KB): Bt[c][k] = B[k][c].
+ * Outputs are byte-identical to nm_prune_compress followed by nm_transpose.
+ * bf16 only (NM_ERR_UNSUPPORTED otherwise).  2:4 with the single-pass layout of
+ * nm_prune_compress runs as one kernel; other calls run the two kernels.
+ * Bt must not overlap B; no output may overlap an input.  Errors as for the
+ * two calls.
+ */
+nm_status nm_prune_compress_transpose(nm_dtype dt, const void* A, int64_t lda, int64_t R,
+                                      int64_t K, int N, int M, uint8_t* mask, int64_t ldmask,
+                                      void* values, uint8_t* meta, const void* B, int64_t ldb,
+                                      int64_t KB, int64_t Nc, void* Bt, int64_t ldbt,
+                                      nm_stream stream);
+
+/*
  * nm_decompress -- inverse of nm_compress: dense A_out [R][lda] with +0.0 at
  * every position that is not kept.
  */

@@ -13,6 +13,7 @@ from .nmsparse import (  # noqa: F401
     nm_decompress,
     nm_prune,
     nm_prune_compress,
+    nm_prune_compress_transpose,
     nm_reprune_t,
     prune_act_venom,
     sddmm_nm,

@@ -60,6 +60,19 @@ nm_status nm_prune_compress(nm_dtype dt, const void* A, int64_t lda, int64_t R, 
   return hip_status(nms::launch_nm_prune_compress(dt, A, lda, R, K, N, M, mask, ldmask, values, meta, hs(stream)));
 }
 
+nm_status nm_prune_compress_transpose(nm_dtype dt, const void* A, int64_t lda, int64_t R, int64_t K, int N, int M,
+                                      uint8_t* mask, int64_t ldmask, void* values, uint8_t* meta, const void* B,
+                                      int64_t ldb, int64_t KB, int64_t Nc, void* Bt, int64_t ldbt, nm_stream stream) {
+  if (!A || !mask || !values || !meta || !B || !Bt) return NM_ERR_NULL;
+  if (dt != NM_BF16 || !nm_ok(N, M)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || K % M != 0 || lda < K || ldmask < K) return NM_ERR_SHAPE;
+  if (KB <= 0 || Nc <= 0 || ldb < Nc || ldbt < KB) return NM_ERR_SHAPE;
+  if (!aligned(A, esize(dt)) || !aligned(values, esize(dt)) || !aligned(B, esize(dt)) || !aligned(Bt, esize(dt)))
+    return NM_ERR_ALIGN;
+  return hip_status(nms::launch_nm_prune_compress_transpose(dt, A, lda, R, K, N, M, mask, ldmask, values, meta, B,
+                                                            ldb, KB, Nc, Bt, ldbt, hs(stream)));
+}
+
 nm_status nm_decompress(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, int N, int M,
                         void* A_out, int64_t lda, nm_stream stream) {
   if (!values || !meta || !A_out) return NM_ERR_NULL;

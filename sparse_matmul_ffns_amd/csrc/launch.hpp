@@ -22,6 +22,10 @@ hipError_t launch_nm_compress(int dt, const void* A, int64_t lda, const uint8_t*
                               hipStream_t s);
 hipError_t launch_nm_prune_compress(int dt, const void* A, int64_t lda, int64_t R, int64_t K, int N, int M,
                                     uint8_t* mask, int64_t ldmask, void* values, uint8_t* meta, hipStream_t s);
+hipError_t launch_nm_prune_compress_transpose(int dt, const void* A, int64_t lda, int64_t R, int64_t K, int N, int M,
+                                              uint8_t* mask, int64_t ldmask, void* values, uint8_t* meta,
+                                              const void* B, int64_t ldb, int64_t KB, int64_t Nc, void* Bt,
+                                              int64_t ldbt, hipStream_t s);
 hipError_t launch_nm_decompress(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, int N,
                                 int M, void* out, int64_t lda, hipStream_t s);
 hipError_t launch_prune_act_venom(int dt, const void* Z, int64_t ldz, int64_t R, int64_t K, int V, int M,

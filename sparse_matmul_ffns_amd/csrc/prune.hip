@@ -12,6 +12,7 @@
 // consecutive lanes touch consecutive bytes.
 #include "common.hpp"
 #include "launch.hpp"
+#include "prep_bodies.hpp"
 
 namespace nms {
 
@@ -295,74 +296,15 @@ __global__ __launch_bounds__(256) void nm_compress24_vec_kernel(const T* __restr
 }
 
 // ---------------------------------------------------------------------------
-// nm_prune_compress, 2:4 with 16-byte aligned rows: the selection of nm_prune and the packing of
-// nm_compress in one pass over A (one read of A instead of two, no read of the mask).  One thread
-// per 16 elements (4 groups) and kFusedU such chunks, all loaded before any is ranked: 16-byte
-// loads of A, one 16-byte store of the chunk's mask bytes, one 16- or 32-byte store of its 8 kept
-// values and one 2-byte store of its 4 nibbles.  Values and metadata are written with ordinary
-// stores (the SpMM reads them next and finds them in the last-level cache); the mask, which
-// nothing in the step reads, with non-temporal ones.
+// nm_prune_compress, 2:4 with 16-byte aligned rows: one pass (prep_bodies.hpp).
 // ---------------------------------------------------------------------------
-constexpr int kFusedU = 2;
-
 template <typename T, typename I>
 __global__ __launch_bounds__(256) void nm_prune_compress24_vec_kernel(const T* __restrict__ A, int64_t lda,
                                                                       int64_t R, int64_t K,
                                                                       uint8_t* __restrict__ mask, int64_t ldmask,
                                                                       T* __restrict__ values,
                                                                       uint8_t* __restrict__ meta) {
-  constexpr int NA = (int)sizeof(T);               // 16-byte loads of A per chunk (16 elements)
-  const I per_row = (I)(K / 16);
-  const I total = (I)R * per_row;
-  const I base = (I)blockIdx.x * (256 * kFusedU) + threadIdx.x;
-  u32x4 xa[kFusedU][NA];
-  I rr[kFusedU], cc[kFusedU];
-#pragma unroll
-  for (int u = 0; u < kFusedU; ++u) {
-    const I cid = base + 256 * u;
-    rr[u] = cid / per_row;
-    cc[u] = (cid - rr[u] * per_row) * 16;
-    if (cid < total) {
-      const u32x4* a4 = reinterpret_cast<const u32x4*>(A + (int64_t)rr[u] * lda + cc[u]);
-#pragma unroll
-      for (int q = 0; q < NA; ++q) xa[u][q] = __builtin_nontemporal_load(a4 + q);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kFusedU; ++u) {
-    if (base + 256 * u >= total) break;
-    const int64_t r = rr[u], c0 = cc[u];
-    uint32_t out[2 * NA];   // the 8 kept values of the chunk, packed
-    uint32_t mk[4];         // mask bytes of the 4 groups
-    uint32_t nibs = 0;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint32_t nib;
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t d01 = xa[u][g >> 1][(g & 1) * 2], d23 = xa[u][g >> 1][(g & 1) * 2 + 1];
-        nib = select24_bf16(d01 & 0xFFFFu, d01 >> 16, d23 & 0xFFFFu, d23 >> 16);
-        const uint32_t p0 = nib & 3u, p1 = nib >> 2;
-        // bytes 2p, 2p+1 of the pair (d23:d01) hold the group's value p
-        out[g] = __builtin_amdgcn_perm(d23, d01, (p0 * 0x202u + 0x100u) | ((p1 * 0x202u + 0x100u) << 16));
-      } else {
-        const u32x4 q = xa[u][g];
-        nib = select24(q[0] & 0x7FFFFFFFu, q[1] & 0x7FFFFFFFu, q[2] & 0x7FFFFFFFu, q[3] & 0x7FFFFFFFu);
-        const uint32_t p0 = nib & 3u, p1 = nib >> 2;
-        auto pick = [&](uint32_t p) { return p == 0 ? q[0] : p == 1 ? q[1] : p == 2 ? q[2] : q[3]; };
-        out[2 * g] = pick(p0);
-        out[2 * g + 1] = pick(p1);
-      }
-      mk[g] = (1u << (8 * (nib & 3u))) | (1u << (8 * (nib >> 2)));
-      nibs |= nib << (4 * g);
-    }
-    __builtin_nontemporal_store(u32x4{mk[0], mk[1], mk[2], mk[3]},
-                                reinterpret_cast<u32x4*>(mask + r * ldmask + c0));
-    T* vd = values + r * (K / 2) + c0 / 2;
-#pragma unroll
-    for (int q = 0; q < NA / 2; ++q)
-      reinterpret_cast<u32x4*>(vd)[q] = u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
-    *reinterpret_cast<uint16_t*>(meta + r * (K / 8) + c0 / 8) = (uint16_t)nibs;
-  }
+  prune_compress24_body<T, I>(blockIdx.x, A, lda, R, K, mask, ldmask, values, meta);
 }
 
 // ---------------------------------------------------------------------------

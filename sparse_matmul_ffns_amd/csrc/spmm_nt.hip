@@ -32,6 +32,7 @@
 #include "common.hpp"
 #include "dma.hpp"
 #include "launch.hpp"
+#include "prep_bodies.hpp"
 
 namespace nms {
 
@@ -256,42 +257,12 @@ hipError_t launch_spmm_nm_nt_dma(const void* values, const uint8_t* meta, int64_
 }
 
 // ---------------------------------------------------------------------------
-// Transpose of a bf16 matrix: dst[c][r] = src[r][c].  A lane moves an 8 x 8
-// block: eight 16-byte row loads, v_perm into eight 8-row columns, eight
-// 16-byte stores.  The 64 lanes of a wave cover a 64 x 64 tile (lanes 8b..8b+7
-// take row block b), so both the loads and the stores of a wave cover whole
-// 128-byte runs.  Edges (rows or columns not a multiple of 8) take the
-// element-wise path.  The result is written with ordinary stores: the SpMM reads
-// it right after, and non-temporal stores (which bypass the last-level cache)
-// made that SpMM ~11% slower at 8192 x 2048 x 4096.
+// Transpose of a bf16 matrix (prep_bodies.hpp): 64 x 64 tiles, one per wave.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void nm_transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                                 int64_t R, int64_t Cn, uint16_t* __restrict__ dst,
                                                                 int64_t ldd) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t tiles_c = (Cn + 63) / 64;
-  const int64_t tile = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t tr = tile / tiles_c, tc = tile % tiles_c;
-  const int64_t r0 = tr * 64 + 8 * (lane & 7), c0 = tc * 64 + 8 * (lane >> 3);
-  if (r0 >= R || c0 >= Cn) return;
-  const bool full = r0 + 8 <= R && c0 + 8 <= Cn && lds % 8 == 0 && ldd % 8 == 0 && (uintptr_t)src % 16 == 0 &&
-                    (uintptr_t)dst % 16 == 0;
-  if (full) {
-    u32x4 v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (r0 + q) * lds + c0));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 d;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) d[j] = __builtin_amdgcn_perm(v[2 * j + 1][e >> 1], v[2 * j][e >> 1], sel);
-      *reinterpret_cast<u32x4*>(dst + (c0 + e) * ldd + r0) = d;
-    }
-  } else {
-    for (int q = 0; q < 8 && r0 + q < R; ++q)
-      for (int e = 0; e < 8 && c0 + e < Cn; ++e) dst[(c0 + e) * ldd + r0 + q] = src[(r0 + q) * lds + c0 + e];
-  }
+  transpose_bf16_body(blockIdx.x, src, lds, R, Cn, dst, ldd);
 }
 
 hipError_t launch_nm_transpose(int dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst, int64_t ldd,

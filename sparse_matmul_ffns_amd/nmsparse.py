@@ -31,6 +31,8 @@ _SIGNATURES = {
     "nm_prune": [_int, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp],
     "nm_compress": [_int, _vp, _i64, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp],
     "nm_prune_compress": [_int, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _vp, _vp],
+    "nm_prune_compress_transpose": [_int, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _vp, _vp, _i64, _i64,
+                                    _i64, _vp, _i64, _vp],
     "nm_decompress": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _vp],
     "spmm_nm": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
@@ -172,6 +174,32 @@ def nm_prune_compress(A: torch.Tensor, N: int = 2, M: int = 4, mask=None, values
     _check(lib().nm_prune_compress(_dt(A), _p(A), _rows(A, "A"), R, K, N, M, _p(mask), _rows(mask, "mask"),
                                    _p(values), _p(meta), _stream()), "nm_prune_compress")
     return mask, values, meta
+
+
+def nm_prune_compress_transpose(A: torch.Tensor, B: torch.Tensor, N: int = 2, M: int = 4, mask=None, values=None,
+                                meta=None, Bt=None):
+    """nm_prune_compress(A) and transpose(B) in one launch (bf16): returns (mask, values, meta, Bt)."""
+    _dev(A, B, mask, values, meta, Bt)
+    R, K = A.shape
+    KB, Nc = B.shape
+    nv, mb, _ = sizes(R, K, N, M)
+    if mask is None:
+        mask = torch.empty((R, K), dtype=torch.uint8, device=A.device)
+    if values is None:
+        values = torch.empty((R, nv // R), dtype=A.dtype, device=A.device)
+    if meta is None:
+        meta = torch.empty((R, mb // R), dtype=torch.uint8, device=A.device)
+    if Bt is None:
+        Bt = torch.empty((Nc, KB), dtype=B.dtype, device=B.device)
+    if Bt.shape != (Nc, KB) or Bt.dtype != B.dtype:
+        raise ValueError("Bt must be [Nc, KB] with B's dtype")
+    if A.dtype != B.dtype:
+        raise ValueError("A and B must share a dtype")
+    _flat(values, "values"), _flat(meta, "meta")
+    _check(lib().nm_prune_compress_transpose(_dt(A), _p(A), _rows(A, "A"), R, K, N, M, _p(mask), _rows(mask, "mask"),
+                                             _p(values), _p(meta), _p(B), _rows(B, "B"), KB, Nc, _p(Bt),
+                                             _rows(Bt, "Bt"), _stream()), "nm_prune_compress_transpose")
+    return mask, values, meta, Bt
 
 
 def nm_decompress(values: torch.Tensor, meta: torch.Tensor, K: int, N: int = 2, M: int = 4, out=None):

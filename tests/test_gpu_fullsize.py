@@ -96,6 +96,17 @@ def test_ffn_up_nm24_full():
     _finite(C, "spmm_nm_t")
     _check_rows(C, A64[rows], X64, rows, "ffn_up spmm_nm_t")
     _check_cols(C, A64, X64[:, cols], cols, "ffn_up spmm_nm_t")
+    del C, Xt
+
+    # the benchmark's step: nm_prune_compress_transpose (one launch), then spmm_nm_t
+    fmask, fvals, fmeta, fXt = nm.nm_prune_compress_transpose(Wd, Xd)
+    assert np.array_equal(host(fmask), want_mask)
+    assert host(fvals).tobytes() == wv.tobytes()
+    assert np.array_equal(host(fmeta), wm)
+    assert np.array_equal(host(fXt), np.ascontiguousarray(X.T))
+    C = nm.spmm_nm_t(fvals, fmeta, K, fXt)
+    _finite(C, "spmm_nm_t after nm_prune_compress_transpose")
+    _check_rows(C, A64[rows], X64, rows, "ffn_up fused prep + spmm_nm_t")
 
 
 # ---------------------------------------------------------------------------

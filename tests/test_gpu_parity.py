@@ -88,6 +88,51 @@ def test_prune_compress_fused(N, M, R, K, dtype, kind, pad):
         assert bool((mask_t.as_strided((R, pad), (K + pad, 1), K) == 7).all())   # padding untouched
 
 
+PREP_CASES = [
+    # (N, M, R, K, KB, Nc, pad): 2:4 with K % 16 == 0 runs the one-launch kernel (the transpose part
+    # covers whole and ragged 64 x 64 tiles); the others fall back to the two kernels
+    (2, 4, 300, 1024, 520, 136, 0),
+    (2, 4, 513, 2064, 64, 64, 16),
+    (2, 4, 8, 16, 13, 7, 0),
+    (2, 4, 1024, 256, 2048, 1000, 16),
+    (2, 4, 64, 256, 128, 64, 8),    # mask rows of 264 bytes (not a multiple of 16): two kernels
+    (2, 4, 5, 44, 40, 24, 0),       # K % 16 != 0: two kernels
+    (2, 8, 33, 88, 96, 17, 0),      # 2:8: two kernels
+]
+
+
+@pytest.mark.parametrize("kind", ["ties", "normal"])
+@pytest.mark.parametrize("N,M,R,K,KB,Nc,pad", PREP_CASES, ids=[f"{c[0]}of{c[1]}_{c[2]}x{c[3]}_B{c[4]}x{c[5]}" for c in PREP_CASES])
+def test_prune_compress_transpose(N, M, R, K, KB, Nc, pad, kind):
+    """nm_prune_compress_transpose: mask, values and metadata byte-identical to the oracle, Bt the
+    exact transpose of B, and padding columns of the outputs untouched."""
+    raw = _inputs(kind, (R, K), seed=R * 3 + K + N, dtype="bf16")
+    braw = synth.normal((KB, Nc), KB + 7 * Nc, dtype="bf16")
+    A, B = dev(raw, "bf16", pad=pad), dev(braw, "bf16", pad=pad)
+    mask_t = torch.full((R, K + pad), 7, dtype=torch.uint8, device="cuda")[:, :K]
+    bt_buf = torch.full((Nc, KB + pad), 3, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    mask, vals, meta, Bt = nm.nm_prune_compress_transpose(A, B, N, M, mask=mask_t, Bt=bt_buf[:, :KB])
+    want = O.prune_nm(raw, "bf16", N, M)
+    assert np.array_equal(host(mask), want)
+    wv, wm, bad = O.compress_nm(raw, want, N, M)
+    assert bad == 0
+    assert host(vals).tobytes() == wv.tobytes()
+    assert np.array_equal(host(meta), wm)
+    assert np.array_equal(host(Bt), np.ascontiguousarray(braw.T))
+    if pad:
+        assert bool((mask_t.as_strided((R, pad), (K + pad, 1), K) == 7).all())
+        assert bool((bt_buf.view(torch.int16)[:, KB:] == 3).all())
+
+
+def test_prune_compress_transpose_rejects_bad_arguments():
+    A = torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((8, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(nm.NmError):            # fp32: NM_ERR_UNSUPPORTED
+        nm.nm_prune_compress_transpose(A.float(), B.float())
+    with pytest.raises(nm.NmError):            # K % M != 0: NM_ERR_SHAPE
+        nm.nm_prune_compress_transpose(torch.zeros((8, 18), dtype=torch.bfloat16, device="cuda"), B)
+
+
 def test_compress_bad_groups():
     raw = synth.normal((64, 64), 5, dtype="bf16")
     mask = O.prune_nm(raw, "bf16", 2, 4)
