@@ -11,8 +11,9 @@ A step is one pass of the hot path over the workload's synthetic inputs
       with activations [2048 x 4096] ~ N(0, 1);
   ffn_down_vnm64_2_8_2048x8192x4096: prune_act_venom (V=64, M=8) -> spmm_venom;
   train_step_nm24_dmodel4096_dff16384_tok8192: nm_reprune_t -> nm_transpose
-      (X) -> spmm_nm_t (Y) -> nm_transpose (dY) -> spmm_nm_t (dX) -> sddmm_nm
-      (dW) (the weight's own prune and compress run once before timing);
+      (X) -> spmm_nm_t (Y) -> sddmm_nm_dt (dW, and dY^T written from the
+      SDDMM's LDS tiles) -> spmm_nm_t (dX) (the weight's own prune and
+      compress run once before timing);
   relu_act_vnm128_2_8_8192x16384x4096: prune_act_venom (ReLU, V=128, M=8) ->
       spmm_venom;
   nm24_fp32_256x512x128: the small fp32 case.
@@ -158,19 +159,20 @@ def _w_train(w):
     dW = torch.empty((dff, dm // 2), dtype=torch.float32, device="cuda")
     Xt = torch.empty((T, dm), dtype=X.dtype, device="cuda")
     dYt = torch.empty((T, dff), dtype=dY.dtype, device="cuda")
+    # dW comes before dX: the SDDMM stages every tile of dY through LDS and writes dY^T from there
+    # (sddmm_nm_dt), which the dX product then reads K-contiguous
     steps = [
         ("nm_reprune_t", lambda: nm.nm_reprune_t(vals, meta, dff, dm, values_t=vt, meta_t=mt)),
         ("nm_transpose_x", lambda: nm.transpose(X, out=Xt)),
         ("spmm_nm_t_fwd", lambda: nm.spmm_nm_t(vals, meta, dm, Xt, out=Y)),
-        ("nm_transpose_dy", lambda: nm.transpose(dY, out=dYt)),
+        ("sddmm_nm_dt", lambda: nm.sddmm_nm(dY, X, meta, out=dW, Dt=dYt)),
         ("spmm_nm_t_dx", lambda: nm.spmm_nm_t(vt, mt, dff, dYt, out=dX)),
-        ("sddmm_nm", lambda: nm.sddmm_nm(dY, X, meta, out=dW)),
     ]
     g = 2.0 * dff * dm * T
-    flops = {"spmm_nm_t_fwd": g, "spmm_nm_t_dx": g, "sddmm_nm": g}
-    algo = {"spmm_nm_t_fwd": ("mfma", g / 2), "spmm_nm_t_dx": ("mfma", g / 2), "sddmm_nm": ("mfma", g),
+    flops = {"spmm_nm_t_fwd": g, "spmm_nm_t_dx": g, "sddmm_nm_dt": g}
+    algo = {"spmm_nm_t_fwd": ("mfma", g / 2), "spmm_nm_t_dx": ("mfma", g / 2), "sddmm_nm_dt": ("mfma", g),
             "nm_reprune_t": ("hbm", 2 * (dff * dm // 2 * 2 + dff * dm // 8))}
-    return steps, flops, algo, "sddmm_nm"
+    return steps, flops, algo, "sddmm_nm_dt"
 
 
 def build_workload(name):
@@ -238,6 +240,7 @@ _KERNEL_SOURCES = {
     "spmm_nm_t": ["spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
     "spmm_venom": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp"],
     "sddmm_nm": ["sddmm.hip", "common.hpp", "dma.hpp"],
+    "sddmm_nm_dt": ["sddmm.hip", "common.hpp", "dma.hpp"],
     "prune_act_venom": ["venom.hip", "common.hpp"],
 }
 

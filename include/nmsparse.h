@@ -232,6 +232,23 @@ nm_status sddmm_nm(nm_dtype dt, const void* D, int64_t ldd, const void* X, int64
                    int64_t Kc, int64_t T, const uint8_t* meta, float* values_out, nm_stream stream);
 
 /*
+ * sddmm_nm_dt -- sddmm_nm that also writes the transpose of the output
+ * gradient, Dt[t][r] = D[r][t], which the input gradient's product then reads
+ * K-contiguous (spmm_nm_t of the re-pruned transposed weight; "Success story:
+ * ESPLAG", Research Topic: the kernels of the sparse training step).  The
+ * SDDMM stages every tile of D through LDS, so the transpose costs no extra
+ * read of D.
+ *   D, X, meta, values_out as for sddmm_nm; Dt [T][lddt] bf16 output
+ *   (lddt >= R), not overlapping any input.
+ * bf16 only (NM_ERR_UNSUPPORTED otherwise).  Outputs are those of sddmm_nm and
+ * nm_transpose(D); without the pipelined SDDMM's conditions the call runs the
+ * two.  Errors as for the two calls.
+ */
+nm_status sddmm_nm_dt(nm_dtype dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R,
+                      int64_t Kc, int64_t T, const uint8_t* meta, float* values_out, void* Dt,
+                      int64_t lddt, nm_stream stream);
+
+/*
  * nm_sizes -- host-only helper: element count of values, bytes of meta and of
  * colsel for an R x K matrix in N:M form (V > 0: V:N:M form with N = 2, where
  * N is ignored).  NULL outputs are skipped.

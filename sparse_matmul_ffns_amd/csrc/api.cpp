@@ -149,6 +149,16 @@ nm_status sddmm_nm(nm_dtype dt, const void* D, int64_t ldd, const void* X, int64
   return hip_status(nms::launch_sddmm_nm(dt, D, ldd, X, ldx, R, Kc, T, meta, values_out, hs(stream)));
 }
 
+nm_status sddmm_nm_dt(nm_dtype dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
+                      int64_t T, const uint8_t* meta, float* values_out, void* Dt, int64_t lddt, nm_stream stream) {
+  if (!D || !X || !meta || !values_out || !Dt) return NM_ERR_NULL;
+  if (dt != NM_BF16) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || Kc <= 0 || T <= 0 || Kc % 4 != 0 || ldd < T || ldx < T || lddt < R) return NM_ERR_SHAPE;
+  if (!aligned(D, esize(dt)) || !aligned(X, esize(dt)) || !aligned(values_out, 4) || !aligned(Dt, esize(dt)))
+    return NM_ERR_ALIGN;
+  return hip_status(nms::launch_sddmm_nm_dt(dt, D, ldd, X, ldx, R, Kc, T, meta, values_out, Dt, lddt, hs(stream)));
+}
+
 void nm_sizes(int64_t R, int64_t K, int N, int M, int V, int64_t* n_values, int64_t* meta_bytes,
               int64_t* colsel_bytes) {
   if (M <= 0) M = 4;

@@ -52,6 +52,8 @@ hipError_t launch_spmm_nm_nt_dma(const void* values, const uint8_t* meta, int64_
                                  int64_t ldbt, int64_t Nc, float* C, int64_t ldc, hipStream_t s);
 hipError_t launch_nm_transpose(int dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst, int64_t ldd,
                                hipStream_t s);
+hipError_t launch_sddmm_nm_dt(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
+                              int64_t Tn, const uint8_t* meta, float* out, void* Dt, int64_t lddt, hipStream_t s);
 hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R,
                            int64_t Kc, int64_t T, const uint8_t* meta, float* out, hipStream_t s);
 

@@ -247,10 +247,15 @@ struct SdCfg {
   static_assert(STAGES == 2 && STAGE * STAGES <= 160 * 1024, "two LDS buffers");
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+// WRITE_DT: the kernel also writes Dt[t][r] = D[r][t].  Every 64-t stage of a 256-row panel of D
+// passes through the LDS of all the panel's column tiles; the one with column tile
+// tn == kt % (number of column tiles) transposes stage kt from LDS -- waves 0-3, one 8 x 8 block
+// per lane (eight 16-byte LDS reads, v_perm, eight 16-byte stores; the 8 lanes of a t row write
+// 128 contiguous bytes) -- so each stage is written once and the work is spread evenly.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool WRITE_DT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
     const uint16_t* __restrict__ D, int64_t ldd, const uint16_t* __restrict__ X, int64_t ldx, int64_t R, int64_t Kc,
-    int64_t Tn, const uint8_t* __restrict__ meta, float* __restrict__ out) {
+    int64_t Tn, const uint8_t* __restrict__ meta, float* __restrict__ out, uint16_t* __restrict__ Dt, int64_t lddt) {
   using Cfg = SdCfg<BM, BN, WAVES_M, WAVES_N, STAGES>;
   constexpr int FM = Cfg::FM;
   extern __shared__ __align__(1024) unsigned char smem[];
@@ -336,14 +341,54 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
     }
   };
 
+  // Dt: stage kt of this row panel is written by the workgroup whose column tile is kt % ntn
+  constexpr int kDtStores = 8;   // 16-byte stores per lane of a transposing wave and stage
+  auto transpose_stage = [&](int kt) {
+    // waves 0-3: 32 row blocks x 8 t blocks of 8 x 8; the 8 lanes of a row block read the 8
+    // chunks of each of its rows (the whole 128-byte LDS row: no bank conflicts among them)
+    const int tb = lane & 7, rb = 8 * wave + (lane >> 3);
+    const unsigned char* st = smem + (kt % STAGES) * Cfg::STAGE;
+    u32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * rb + i;
+      v[i] = *reinterpret_cast<const u32x4*>(st + r * (TK * 2) + ((tb ^ sd_swz(r)) << 4));
+    }
+    const int64_t col = m0 + 8 * rb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 d;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[j] = __builtin_amdgcn_perm(v[2 * j + 1][e >> 1], v[2 * j][e >> 1], sel);
+      uint16_t* dst = Dt + ((int64_t)kt * TK + 8 * tb + e) * lddt + col;
+      if (col + 8 <= R) {
+        *reinterpret_cast<u32x4*>(dst) = d;
+      } else {
+        // rows past R (a partial last panel) are never written
+        for (int q = 0; q < 8; ++q)
+          if (col + q < R) dst[q] = (uint16_t)(d[q >> 1] >> (16 * (q & 1)));
+      }
+    }
+  };
+
   // two buffers: the loads of stage kt+1 are in flight while stage kt runs on the matrix cores
   if (KT > 0) issue(0);
+  bool wrote = false;   // this wave stored a transposed stage during the previous step
   for (int kt = 0; kt < KT; ++kt) {
-    wait_vmcnt<0>();   // this wave's loads of stage kt have landed
+    // this wave's loads of stage kt have landed (after a transposing step the stores of that step,
+    // which are younger than those loads, may still be in flight)
+    if (WRITE_DT && wrote) wait_vmcnt<kDtStores>(); else wait_vmcnt<0>();
     lds_barrier();     // ... every wave's; and every wave is done reading stage kt-1 (the other buffer)
     if (kt + 1 < KT) issue(kt + 1);
     compute(kt);
+    wrote = false;
+    if (WRITE_DT && kt % ntn == tn && wave < 4) {
+      transpose_stage(kt);
+      wrote = true;
+    }
   }
+  if (WRITE_DT) wait_vmcnt<0>();
 
   // epilogue: lane l32 holds columns 4*l32 .. +3 of the wave's 128 = 2:4 group gq
   const int64_t G = Kc / 4, mrow = (Kc + 7) / 8;
@@ -378,16 +423,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool WRITE_DT>
 static hipError_t run_sddmm_dma(const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
-                                int64_t Tn, const uint8_t* meta, float* out, hipStream_t s) {
+                                int64_t Tn, const uint8_t* meta, float* out, void* Dt, int64_t lddt, hipStream_t s) {
   using Cfg = SdCfg<BM, BN, WAVES_M, WAVES_N, STAGES>;
   const size_t lds = (size_t)Cfg::STAGE * STAGES;
-  auto kern = sddmm_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES>;
+  auto kern = sddmm_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, WRITE_DT>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int64_t ntiles = ((R + BM - 1) / BM) * ((Kc + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg::NT), lds, s, (const uint16_t*)D, ldd, (const uint16_t*)X,
-                     ldx, R, Kc, Tn, meta, out);
+                     ldx, R, Kc, Tn, meta, out, (uint16_t*)Dt, lddt);
   return hipGetLastError();
 }
 
@@ -412,7 +457,7 @@ hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, in
   const bool staged = tier && tier[0] == '1';
   if (dt == DT_BF16 && !force && !staged && Tn % TK == 0 && ldd % 8 == 0 && ldx % 8 == 0 && (uintptr_t)D % 16 == 0 &&
       (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0)
-    return run_sddmm_dma<256, 256, 4, 2, 2>(D, ldd, X, ldx, R, Kc, Tn, meta, out, s);
+    return run_sddmm_dma<256, 256, 4, 2, 2, false>(D, ldd, X, ldx, R, Kc, Tn, meta, out, nullptr, 0, s);
   if (dt == DT_BF16 && !force && Tn % 8 == 0 && ldd % 8 == 0 && ldx % 8 == 0 && (uintptr_t)D % 16 == 0 &&
       (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0)
     return run_sddmm_mfma<256, 128, 128, 64>(D, ldd, X, ldx, R, Kc, Tn, meta, out, s);
@@ -424,6 +469,19 @@ hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, in
     hipLaunchKernelGGL(sddmm_generic_kernel<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)D, ldd,
                        (const uint32_t*)X, ldx, R, Kc, Tn, meta, out);
   return hipGetLastError();
+}
+
+// sddmm_nm that also writes Dt = D^T [Tn][lddt]: one kernel on the pipelined path, otherwise the
+// SDDMM followed by the transpose.
+hipError_t launch_sddmm_nm_dt(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
+                              int64_t Tn, const uint8_t* meta, float* out, void* Dt, int64_t lddt, hipStream_t s) {
+  if (dt == DT_BF16 && !force_generic() && !env_is_one("NMSPARSE_SPMM_TIER") && Tn % TK == 0 && ldd % 8 == 0 &&
+      ldx % 8 == 0 && (uintptr_t)D % 16 == 0 && (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0 &&
+      (uintptr_t)Dt % 16 == 0 && lddt % 8 == 0)
+    return run_sddmm_dma<256, 256, 4, 2, 2, true>(D, ldd, X, ldx, R, Kc, Tn, meta, out, Dt, lddt, s);
+  const hipError_t e = launch_sddmm_nm(dt, D, ldd, X, ldx, R, Kc, Tn, meta, out, s);
+  if (e != hipSuccess) return e;
+  return launch_nm_transpose(dt, D, ldd, R, Tn, Dt, lddt, s);
 }
 
 }  // namespace nms

@@ -41,6 +41,7 @@ _SIGNATURES = {
     "spmm_venom": [_int, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
     "nm_reprune_t": [_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp],
     "sddmm_nm": [_int, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp],
+    "sddmm_nm_dt": [_int, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp],
 }
 
 _lib = None
@@ -308,8 +309,10 @@ def nm_reprune_t(values: torch.Tensor, meta: torch.Tensor, R: int, K: int, value
     return values_t, meta_t
 
 
-def sddmm_nm(D: torch.Tensor, X: torch.Tensor, meta: torch.Tensor, out=None) -> torch.Tensor:
-    _dev(D, X, meta, out)
+def sddmm_nm(D: torch.Tensor, X: torch.Tensor, meta: torch.Tensor, out=None, Dt=None):
+    """dW values of a 2:4 layer; with `Dt` (a [T, R] tensor, bf16) the call is sddmm_nm_dt, which also
+    writes Dt = D^T, and returns (out, Dt)."""
+    _dev(D, X, meta, out, Dt)
     _flat(meta, "meta")
     if D.dtype != X.dtype:
         raise TypeError("D and X must share a dtype")
@@ -320,6 +323,12 @@ def sddmm_nm(D: torch.Tensor, X: torch.Tensor, meta: torch.Tensor, out=None) -> 
     if out is None:
         out = torch.empty((R, Kc // 2), dtype=torch.float32, device=D.device)
     _flat(out, "out")
+    if Dt is not None:
+        if Dt.shape != (T, R) or Dt.dtype != D.dtype:
+            raise ValueError("Dt must be [T, R] with D's dtype")
+        _check(lib().sddmm_nm_dt(_dt(D), _p(D), _rows(D, "D"), _p(X), _rows(X, "X"), R, Kc, T, _p(meta), _p(out),
+                                 _p(Dt), _rows(Dt, "Dt"), _stream()), "sddmm_nm_dt")
+        return out, Dt
     _check(lib().sddmm_nm(_dt(D), _p(D), _rows(D, "D"), _p(X), _rows(X, "X"), R, Kc, T, _p(meta), _p(out),
                           _stream()), "sddmm_nm")
     return out

@@ -231,3 +231,15 @@ def test_train_step_nm24_full():
     cols = (np.arange(dm // 4)[None, :, None] * 4 + pos).reshape(len(rows), dm // 2)
     got = host(dW[torch.as_tensor(rows, device=dW.device)])
     check_close(got, ref, np.take_along_axis(full_bound, cols, axis=1), "train dW rows")
+    del dW
+
+    # the benchmark's order: dW with sddmm_nm_dt (which also writes dY^T), then dX from that dY^T
+    dW, dYt = nm.sddmm_nm(dYd, Xd, meta, Dt=torch.empty((T, dff), dtype=torch.bfloat16, device="cuda"))
+    got = host(dW[torch.as_tensor(rows, device=dW.device)])
+    check_close(got, ref, np.take_along_axis(full_bound, cols, axis=1), "train dW rows (sddmm_nm_dt)")
+    del dW
+    assert np.array_equal(host(dYt), np.ascontiguousarray(dY.T))
+    dX = nm.spmm_nm_t(vt, mt, dff, dYt)
+    _finite(dX, "dX after sddmm_nm_dt")
+    xrows = _sample(dm, 24, 42)   # the rows Wt_rows holds
+    _check_rows(dX, Wt_rows, O.decode(dY, "bf16"), xrows, "train dX from sddmm_nm_dt's dY^T")

@@ -419,3 +419,48 @@ def test_sddmm_nm(R, Kc, T, kind, dtype, tier):
     pos = O.unpack_positions(meta, R, Kc, 2, 4)
     cols = (np.arange(Kc // 4)[None, :, None] * 4 + pos).reshape(R, Kc // 2)
     check_close(out, ref, np.take_along_axis(full_bound, cols, axis=1), f"sddmm {R}x{Kc}x{T}")
+
+
+SDDMM_DT_CASES = [
+    # (R, Kc, T, pad): T % 64 == 0 runs the pipelined kernel, which transposes each 64-t stage of D
+    # in the workgroup whose column tile is kt % (column tiles)
+    (520, 1032, 1024, 0),    # 3 row panels (the last partial), 5 column tiles (the last partial)
+    (256, 256, 512, 8),      # one column tile: it writes every stage
+    (300, 136, 256, 0),      # partial row panel of 44 rows
+    (260, 512, 128, 16),     # a last panel of 4 rows: no whole 8-row block
+    (300, 136, 200, 0),      # T % 64 != 0: sddmm_nm, then nm_transpose
+]
+
+
+@pytest.mark.parametrize("R,Kc,T,pad", SDDMM_DT_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SDDMM_DT_CASES])
+@pytest.mark.parametrize("kind", ["normal", "ints"])
+def test_sddmm_nm_dt(R, Kc, T, pad, kind, tier):
+    """sddmm_nm_dt: dW values as the oracle's SDDMM, Dt the exact transpose of D, the padding
+    columns of Dt untouched."""
+    D = _inputs(kind, (R, T), R + T, "bf16")
+    X = _inputs(kind, (Kc, T), Kc + T + 1, "bf16")
+    W = synth.normal((R, Kc), 77, dtype="bf16")
+    _, meta, _ = O.compress_nm(W, O.prune_nm(W, "bf16", 2, 4), 2, 4)
+    dt_buf = torch.full((T, R + pad), 5, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    out, Dt = nm.sddmm_nm(dev(D, "bf16", pad=pad), dev(X, "bf16"), dev(meta, "u8"), Dt=dt_buf[:, :R])
+    out = host(out)
+    ref = O.sddmm_nm(D, X, meta, R, Kc, "bf16")
+    if kind == "ints" and T <= 1024:
+        assert np.array_equal(out, ref)
+    full_bound = np.abs(O.decode(D, "bf16")) @ np.abs(O.decode(X, "bf16")).T
+    pos = O.unpack_positions(meta, R, Kc, 2, 4)
+    cols = (np.arange(Kc // 4)[None, :, None] * 4 + pos).reshape(R, Kc // 2)
+    check_close(out, ref, np.take_along_axis(full_bound, cols, axis=1), f"sddmm_nm_dt {R}x{Kc}x{T}")
+    assert np.array_equal(host(Dt), np.ascontiguousarray(D.T))
+    if pad:
+        assert bool((dt_buf.view(torch.int16)[:, R:] == 5).all())
+
+
+def test_sddmm_nm_dt_rejects_bad_arguments():
+    D = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    X = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    meta = torch.zeros((8, 1), dtype=torch.uint8, device="cuda")
+    with pytest.raises(nm.NmError):            # fp32: NM_ERR_UNSUPPORTED
+        nm.sddmm_nm(D.float(), X.float(), meta, Dt=torch.zeros((64, 8), device="cuda"))
+    with pytest.raises(ValueError):            # Dt of the wrong shape
+        nm.sddmm_nm(D, X, meta, Dt=torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda"))
