@@ -23,7 +23,9 @@ of the step's dominant kernel, timed with HIP events on the stream it runs on,
 and the fp64 CPU oracle timed on the host (rank 0, N = 1 only).
 
 Warm-up: the W untimed steps are repeated until at least one second of them
-has run, so that the timed steps see settled GPU clocks.
+has run, so that the timed steps see settled GPU clocks.  `cold` reports, beside
+`value`, the median of five single steps each run after 512 MiB have been
+written over a scratch buffer (operands evicted from L2 and the last-level cache).
 """
 
 from __future__ import annotations
@@ -256,8 +258,10 @@ def _src_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload, kernel):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None."""
+def recorded_counter(workload, kernel, key):
+    """A per-launch figure (`hbm_bytes_per_launch`, `mfma_busy_pct`) from the committed rocprofv3
+    --pmc summary of the kernel on the workload, or None when there is none or the kernel's
+    sources have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -269,9 +273,13 @@ def recorded_traffic(workload, kernel):
     if fields.get("source_sha256_16") != _src_hash(kernel):
         return None
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields[key])
     except (KeyError, ValueError):
         return None
+
+
+COLD_RUNS = 5
+COLD_FLUSH_BYTES = 512 << 20
 
 
 def main():
@@ -327,6 +335,22 @@ def main():
     torch.cuda.synchronize()
     per_kernel_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
                      for i, n in enumerate(names)}
+
+    # cold steps (reported beside, not as `value`): before each, 512 MiB written over a scratch
+    # buffer push the step's operands out of L2 and the 256 MB last-level cache; the step is then
+    # timed alone between two events
+    flush = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    cold_ms = []
+    for i in range(COLD_RUNS):
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _, fn in steps:
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold_ms.append(e0.elapsed_time(e1))
+    del flush
     ms_per_step = elapsed * 1e3 / args.steps
     total_flops = sum(flops.values())
     value = total_flops / (ms_per_step * 1e-3) / 1e12
@@ -360,7 +384,11 @@ def main():
         "per_kernel_us": {n: round(v * 1e3, 2) for n, v in per_kernel_ms.items()},
         "roofline": {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": recorded_traffic(args.workload, dominant)},
+                     "traffic": recorded_counter(args.workload, dominant, "hbm_bytes_per_launch"),
+                     "mfma_busy_pct": recorded_counter(args.workload, dominant, "mfma_busy_pct")},
+        "cold": {"ms_per_step": round(float(np.median(cold_ms)), 5),
+                 "value": round(total_flops / (float(np.median(cold_ms)) * 1e-3) / 1e12, 2),
+                 "runs": COLD_RUNS, "flush_bytes": COLD_FLUSH_BYTES},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.workload)
