@@ -171,6 +171,19 @@ nm_status spmm_nm_t(nm_dtype dt, const void* values, const uint8_t* meta, int64_
                     const void* Bt, int64_t ldbt, int64_t Nc, float* C, int64_t ldc, nm_stream stream);
 
 /*
+ * spmm_nm_t_out_bf16 -- spmm_nm_t with a bf16 result: each fp32 sum is rounded
+ * to the nearest bf16, ties to even, as it is stored.  The output an FFN's
+ * up-projection hands to the next step in bf16 (the activations that
+ * prune_act_venom selects from; "To 2:4 Sparsity and Beyond", abstract).
+ *   values, meta, Bt as for spmm_nm_t (dtype dt, bf16 or fp32 products);
+ *   C [R][ldc] bf16 output (uint16 bit patterns), C[r][n] for n < Nc.
+ * Errors as for spmm_nm_t (C aligned to 2 bytes).
+ */
+nm_status spmm_nm_t_out_bf16(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R,
+                             int64_t K, const void* Bt, int64_t ldbt, int64_t Nc, void* C,
+                             int64_t ldc, nm_stream stream);
+
+/*
  * nm_transpose -- dst[c][r] = src[r][c] for an R x Cn matrix: turns a row-major
  * dense operand B [K][Nc] into the K-contiguous form spmm_nm_t takes.
  *   src [R][lds], dst [Cn][ldd] (ldd >= R), dtype dt; dst must not overlap src.

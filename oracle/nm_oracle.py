@@ -72,6 +72,25 @@ def decode(raw: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def encode_bf16(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of float64 values, rounded to the nearest bf16 with ties to even.
+
+    bf16 keeps fp32's sign and 8 exponent bits and 8 significant bits (7 stored).  For a finite
+    nonzero x = f * 2**e with 0.5 <= |f| < 1 (frexp), the bf16 numbers near x are the multiples of
+    2**(e - 8) (of 2**-133 below the normal range, where e - 8 < -133); x is divided by that step,
+    rounded half to even (numpy's rounding) and multiplied back, which is exact in float64.  A
+    result of 2**128 or more in magnitude is infinity.  Used for products stored in bf16.
+    """
+    x = np.asarray(x, np.float64)
+    _check_finite(x)
+    f, e = np.frexp(x)
+    step_exp = np.maximum(e - 8, -133)
+    y = np.round(np.ldexp(x, -step_exp)) * np.ldexp(1.0, step_exp)     # exact: |quotient| < 2**9
+    with np.errstate(over="ignore"):
+        y32 = np.where(np.abs(y) >= 2.0 ** 128, np.copysign(np.inf, y), y).astype(np.float32)
+    return (y32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 def zeros_raw(shape, dtype: str) -> np.ndarray:
     """+0.0 in the raw representation (all bits clear)."""
     return np.zeros(shape, np.uint16 if dtype == BF16 else np.float32)

@@ -100,6 +100,16 @@ nm_status spmm_nm_t(nm_dtype dt, const void* values, const uint8_t* meta, int64_
   return hip_status(nms::launch_spmm_nm_t(dt, values, meta, R, K, Bt, ldbt, Nc, C, ldc, hs(stream)));
 }
 
+nm_status spmm_nm_t_out_bf16(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                             const void* Bt, int64_t ldbt, int64_t Nc, void* C, int64_t ldc, nm_stream stream) {
+  if (!values || !meta || !Bt || !C) return NM_ERR_NULL;
+  if (!dtype_ok(dt)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || Nc <= 0 || K % 4 != 0 || ldbt < K || ldc < Nc) return NM_ERR_SHAPE;
+  if (!aligned(values, esize(dt)) || !aligned(Bt, esize(dt)) || !aligned(C, 2)) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_spmm_nm_t_bf16out(dt, values, meta, R, K, Bt, ldbt, Nc, (uint16_t*)C, ldc,
+                                                  hs(stream)));
+}
+
 nm_status nm_transpose(nm_dtype dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst, int64_t ldd,
                        nm_stream stream) {
   if (!src || !dst) return NM_ERR_NULL;

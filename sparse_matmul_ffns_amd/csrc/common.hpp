@@ -105,6 +105,18 @@ __device__ inline int xcd_remap(int wg, int nwg) {
   return (wg % nx) * per + (wg / nx);
 }
 
+// fp32 -> bf16 with round to nearest, ties to even (the bf16 result keeps the fp32 sign and
+// exponent and the top 7 stored significand bits, rounded on the 16 dropped ones); NaN stays a
+// quiet NaN, values past the bf16 range round to infinity.
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+// One output element of a product: fp32 as is, bf16 rounded to nearest even.
+__device__ inline void store_out(float* p, float v) { *p = v; }
+__device__ inline void store_out(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
+
 // Host-side knob, read on every call: NMSPARSE_FORCE_GENERIC=1 makes every call take its
 // plain SIMT kernel instead of the tiled ones (the tests compare the two).
 inline bool env_is_one(const char* name) {

@@ -39,11 +39,11 @@ namespace nms {
 // generic path: fp32 or bf16, any K % 4 == 0 (2:4) or V:N:M, any alignment.
 // 64 x 64 tile, 256 lanes, 4 x 4 outputs per lane, A decompressed into LDS.
 // ---------------------------------------------------------------------------
-template <typename T, bool VENOM>
+template <typename T, bool VENOM, typename OutT>
 __global__ __launch_bounds__(256) void spmm_generic_kernel(const T* __restrict__ values, const uint8_t* __restrict__ meta,
                                                            const uint8_t* __restrict__ colsel, int64_t R, int64_t K,
                                                            int V, int M, const T* __restrict__ B, int64_t sbk,
-                                                           int64_t sbn, int64_t Nc, float* __restrict__ C,
+                                                           int64_t sbn, int64_t Nc, OutT* __restrict__ C,
                                                            int64_t ldc) {
   constexpr int TM = 64, TN = 64, KC = 32;
   __shared__ float As[KC][TM + 4];
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void spmm_generic_kernel(const T* __restrict__
     if (row >= R) continue;
     for (int j = 0; j < 4; ++j) {
       const int64_t n = n0 + tx * 4 + j;
-      if (n < Nc) C[row * ldc + n] = acc[i][j];
+      if (n < Nc) store_out(C + row * ldc + n, acc[i][j]);
     }
   }
 }
@@ -329,13 +329,13 @@ static hipError_t run_smfmac(const void* values, const uint8_t* meta, const uint
   return hipGetLastError();
 }
 
-template <typename T, bool VENOM>
+template <typename T, bool VENOM, typename OutT>
 static hipError_t run_generic(const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R, int64_t K,
-                              int V, int M, const void* B, int64_t sbk, int64_t sbn, int64_t Nc, float* C, int64_t ldc,
+                              int V, int M, const void* B, int64_t sbk, int64_t sbn, int64_t Nc, OutT* C, int64_t ldc,
                               hipStream_t s) {
   dim3 grid((unsigned)((Nc + 63) / 64), (unsigned)((R + 63) / 64));
-  hipLaunchKernelGGL((spmm_generic_kernel<T, VENOM>), grid, dim3(256), 0, s, (const T*)values, meta, colsel, R, K, V,
-                     M, (const T*)B, sbk, sbn, Nc, C, ldc);
+  hipLaunchKernelGGL((spmm_generic_kernel<T, VENOM, OutT>), grid, dim3(256), 0, s, (const T*)values, meta, colsel, R,
+                     K, V, M, (const T*)B, sbk, sbn, Nc, C, ldc);
   return hipGetLastError();
 }
 
@@ -366,6 +366,14 @@ hipError_t launch_spmm_nm_t(int dt, const void* values, const uint8_t* meta, int
                             int64_t ldbt, int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
   if (dt == DT_BF16 && !force_generic() && spmm_nt_ok(values, meta, Bt, ldbt, R, Nc, K))
     return launch_spmm_nm_nt_dma(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
+  return dt == DT_BF16 ? run_generic<uint16_t, false>(values, meta, nullptr, R, K, 4, 4, Bt, 1, ldbt, Nc, C, ldc, s)
+                       : run_generic<uint32_t, false>(values, meta, nullptr, R, K, 4, 4, Bt, 1, ldbt, Nc, C, ldc, s);
+}
+
+hipError_t launch_spmm_nm_t_bf16out(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                                   const void* Bt, int64_t ldbt, int64_t Nc, uint16_t* C, int64_t ldc, hipStream_t s) {
+  if (dt == DT_BF16 && !force_generic() && spmm_nt_ok(values, meta, Bt, ldbt, R, Nc, K))
+    return launch_spmm_nm_nt_dma_bf16out(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
   return dt == DT_BF16 ? run_generic<uint16_t, false>(values, meta, nullptr, R, K, 4, 4, Bt, 1, ldbt, Nc, C, ldc, s)
                        : run_generic<uint32_t, false>(values, meta, nullptr, R, K, 4, 4, Bt, 1, ldbt, Nc, C, ldc, s);
 }

@@ -58,10 +58,11 @@ struct NtCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+// OutT: float (fp32 C) or uint16_t (bf16 C, each fp32 sum rounded to nearest even).
+template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
     const uint16_t* __restrict__ values, const uint8_t* __restrict__ meta, int64_t R, int64_t Kd,
-    const uint16_t* __restrict__ Bt, int64_t ldbt, int64_t Nc, float* __restrict__ C, int64_t ldc) {
+    const uint16_t* __restrict__ Bt, int64_t ldbt, int64_t Nc, OutT* __restrict__ C, int64_t ldc) {
   using Cfg = NtCfg<BM, BN, WAVES_M, WAVES_N>;
   constexpr int FM = Cfg::FM, FN = Cfg::FN;
   extern __shared__ __align__(1024) unsigned char smem[];
@@ -225,17 +226,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t row = m0 + wm * Cfg::WM + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
-        if (row < R && col < Nc) __builtin_nontemporal_store(acc[i][j][e], C + row * ldc + col);
+        if (row < R && col < Nc) {
+          if constexpr (sizeof(OutT) == 4)
+            __builtin_nontemporal_store(acc[i][j][e], C + row * ldc + col);
+          else
+            __builtin_nontemporal_store(f32_to_bf16_rne(acc[i][j][e]), C + row * ldc + col);
+        }
       }
     }
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT>
 static hipError_t run_nt(const void* values, const uint8_t* meta, int64_t R, int64_t Kd, const void* Bt, int64_t ldbt,
-                         int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
+                         int64_t Nc, OutT* C, int64_t ldc, hipStream_t s) {
   using Cfg = NtCfg<BM, BN, WAVES_M, WAVES_N>;
-  auto kern = spmm_nt_kernel<BM, BN, WAVES_M, WAVES_N>;
+  auto kern = spmm_nt_kernel<BM, BN, WAVES_M, WAVES_N, OutT>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   const int64_t ntiles = ((R + BM - 1) / BM) * ((Nc + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg::NT), (size_t)Cfg::LDS, s, (const uint16_t*)values, meta,
@@ -253,6 +259,11 @@ bool spmm_nt_ok(const void* values, const uint8_t* meta, const void* Bt, int64_t
 
 hipError_t launch_spmm_nm_nt_dma(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
                                  int64_t ldbt, int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
+  return run_nt<256, 256, 2, 4>(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
+}
+
+hipError_t launch_spmm_nm_nt_dma_bf16out(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
+                                         int64_t ldbt, int64_t Nc, uint16_t* C, int64_t ldc, hipStream_t s) {
   return run_nt<256, 256, 2, 4>(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
 }
 

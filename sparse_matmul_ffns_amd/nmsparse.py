@@ -36,6 +36,7 @@ _SIGNATURES = {
     "nm_decompress": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _vp],
     "spmm_nm": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
+    "spmm_nm_t_out_bf16": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "nm_transpose": [_int, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "prune_act_venom": [_int, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _i64, _vp],
     "spmm_venom": [_int, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
@@ -230,8 +231,11 @@ def spmm_nm(values: torch.Tensor, meta: torch.Tensor, K: int, B: torch.Tensor, o
     return out
 
 
-def spmm_nm_t(values: torch.Tensor, meta: torch.Tensor, K: int, Bt: torch.Tensor, out=None) -> torch.Tensor:
-    """C = decompress(values, meta) @ Bt.T with Bt [Nc, K] (rows contiguous)."""
+def spmm_nm_t(values: torch.Tensor, meta: torch.Tensor, K: int, Bt: torch.Tensor, out=None,
+              out_dtype=None) -> torch.Tensor:
+    """C = decompress(values, meta) @ Bt.T with Bt [Nc, K] (rows contiguous).  C is fp32, or bf16
+    (each sum rounded to nearest even: spmm_nm_t_out_bf16) when `out` is bf16 or
+    out_dtype=torch.bfloat16."""
     _dev(values, meta, Bt, out)
     _flat(values, "values"), _flat(meta, "meta")
     if Bt.dtype != values.dtype:
@@ -241,7 +245,13 @@ def spmm_nm_t(values: torch.Tensor, meta: torch.Tensor, K: int, Bt: torch.Tensor
     if Bt.shape[1] != K:
         raise ValueError("Bt must have K columns")
     if out is None:
-        out = torch.empty((R, Nc), dtype=torch.float32, device=Bt.device)
+        out = torch.empty((R, Nc), dtype=out_dtype or torch.float32, device=Bt.device)
+    if out.dtype == torch.bfloat16:
+        _check(lib().spmm_nm_t_out_bf16(_dt(Bt), _p(values), _p(meta), R, K, _p(Bt), _rows(Bt, "Bt"), Nc, _p(out),
+                                        _rows(out, "out"), _stream()), "spmm_nm_t_out_bf16")
+        return out
+    if out.dtype != torch.float32:
+        raise TypeError("out must be fp32 or bf16")
     _check(lib().spmm_nm_t(_dt(Bt), _p(values), _p(meta), R, K, _p(Bt), _rows(Bt, "Bt"), Nc, _p(out),
                            _rows(out, "out"), _stream()), "spmm_nm_t")
     return out

@@ -293,6 +293,30 @@ def test_spmm_nm_t_many_tiles(kind):
     check_close(got_c, want_c, O.abs_bound(A64, B64[:, cols]), "spmm_nm_t many tiles columns")
 
 
+@pytest.mark.parametrize("R,K,Nc,pb,pc", SPMM_T_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in SPMM_T_CASES])
+@pytest.mark.parametrize("kind", ["normal", "ints"])
+def test_spmm_nm_t_out_bf16(R, K, Nc, pb, pc, kind, tier_t):
+    """bf16 C: every element within one bf16 unit in the last place of the exact product (plus the
+    fp32 summation's share); with small integers, where fp32 sums are exact, the bf16 bits equal
+    the oracle's rounding of the exact product."""
+    raw = _inputs(kind, (R, K), seed=R + K + 9, dtype="bf16")
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, "bf16", 2, 4), 2, 4)
+    Btraw = _inputs(kind, (Nc, K), seed=Nc + 11, dtype="bf16")
+    Cbuf = torch.full((R, Nc + pc), 3, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    C = host(nm.spmm_nm_t(dev(vals, "bf16"), dev(meta, "u8"), K, dev(Btraw, "bf16", pad=pb), out=Cbuf[:, :Nc]))
+    Braw = np.ascontiguousarray(Btraw.T)
+    exact = O.spmm_nm(vals, meta, R, K, Braw, "bf16")
+    if kind == "ints" and K <= 1024:
+        assert np.array_equal(C, O.encode_bf16(exact))
+    got = O.decode(C, "bf16")
+    ulp = np.abs(O.decode(O.encode_bf16(exact) | np.uint16(1), "bf16") - O.decode(O.encode_bf16(exact) & np.uint16(0xFFFE), "bf16"))
+    A64 = O.decode(O.decompress_nm(vals, meta, R, K, 2, 4), "bf16")
+    bound = ulp + 1e-4 * O.abs_bound(A64, O.decode(Braw, "bf16"))
+    assert np.all(np.abs(got - exact) <= bound), float(np.max(np.abs(got - exact) - bound))
+    if pc:
+        assert bool((Cbuf.view(torch.int16)[:, Nc:] == 3).all())
+
+
 TRANSPOSE_CASES = [(64, 64, 0), (2048, 520, 0), (300, 136, 8), (17, 40, 0), (13, 7, 3), (1, 96, 0), (520, 1, 0)]
 
 

@@ -96,6 +96,21 @@ def _prune_signed(raw, dtype, N, M):
     return O.nm_select(O.decode(raw, dtype), N, M)          # mistake: signed key, not magnitude
 
 
+_orig_encode = O.encode_bf16
+
+
+def _encode_half_up(x):
+    x = np.asarray(x, np.float64)
+    f, e = np.frexp(x)
+    step_exp = np.maximum(e - 8, -133)
+    y = np.floor(np.abs(np.ldexp(x, -step_exp)) + 0.5) * np.sign(x) * np.ldexp(1.0, step_exp)   # mistake: ties up
+    return (y.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _encode_truncate(x):
+    return (np.asarray(x, np.float64).astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)  # mistake: chops
+
+
 MUTATIONS = [
     ("nm_select", _select_tie_high, [lambda: P.test_nm_select_exhaustive_m4(2, "f32")]),
     ("nm_select", _select_no_ties, [lambda: P.test_prune_compress_invariants(2, 4, "bf16")]),
@@ -107,6 +122,10 @@ MUTATIONS = [
     ("relu_raw", _relu_keeps_negzero, [lambda: P.test_relu_venom()]),
     ("decompress_nm", _decompress_negzero, [lambda: P.test_prune_compress_invariants(2, 4, "f32")]),
     ("reprune_t", _reprune_no_transpose, [lambda: P.test_golden_reprune_t()]),
+    ("encode_bf16", _encode_half_up, [lambda: P.test_encode_bf16_known_values(),
+                                      lambda: P.test_encode_bf16_is_nearest_ties_even_brute()]),
+    ("encode_bf16", _encode_truncate, [lambda: P.test_encode_bf16_known_values(),
+                                       lambda: P.test_encode_bf16_matches_fp32_bit_rounding()]),
 ]
 
 

@@ -339,3 +339,56 @@ def test_decode_bf16():
     got = O.decode(bits, "bf16")
     assert got[:4].tolist() == [1.0, -1.0, 0.0, 0.0] and np.signbit(got[2])
     assert got[4] == 3.140625 and got[5] == 2.0 ** -133
+
+
+# ---------------------------------------------------------------------------
+# encode_bf16: float64 -> nearest bf16, ties to even (products stored in bf16)
+# ---------------------------------------------------------------------------
+
+def test_encode_bf16_known_values():
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -30, -2.5, 0.0, -0.0,
+                  (2 - 2.0 ** -7) * 2.0 ** 127, (2 - 2.0 ** -8) * 2.0 ** 127 * (1 - 2.0 ** -40), 3.4e38,
+                  2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135, 2.0 ** -126 - 2.0 ** -134])
+    want = [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020, 0x0000, 0x8000,
+            0x7F7F, 0x7F7F, 0x7F80,
+            0x0001, 0x0000, 0x0001, 0x0080]
+    assert O.encode_bf16(x).tolist() == want
+
+
+def test_encode_bf16_round_trips_every_finite_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    assert np.array_equal(O.encode_bf16(O.decode(bits[finite], "bf16")), bits[finite])
+
+
+def test_encode_bf16_is_nearest_ties_even_brute():
+    """Against the two neighbouring bf16 values found by search over all patterns."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(3000) * np.exp2(rng.integers(-140, 127, 3000))
+    x = np.concatenate([x, (O.decode(np.arange(0x0001, 0x7F7F, 97, dtype=np.uint16), "bf16")
+                            + O.decode(np.arange(0x0002, 0x7F80, 97, dtype=np.uint16), "bf16")) / 2])  # exact ties
+    pos = np.sort(O.decode(np.arange(0x0000, 0x7F80, dtype=np.uint16), "bf16"))   # all finite bf16 >= 0
+    got = O.decode(O.encode_bf16(x), "bf16")
+    for xi, gi in zip(x, got):
+        a = abs(xi)
+        i = np.searchsorted(pos, a, side="right") - 1          # pos[i] <= a < pos[i+1]
+        lo, hi = pos[i], (pos[i + 1] if i + 1 < len(pos) else np.inf)
+        if a - lo < hi - a:
+            want = lo
+        elif a - lo > hi - a:
+            want = hi
+        else:                                                 # tie: the even pattern
+            want = lo if (i % 2 == 0) else hi
+        assert abs(gi) == want and (gi == 0 or np.sign(gi) == np.sign(xi)), (xi, gi, want)
+
+
+def test_encode_bf16_matches_fp32_bit_rounding():
+    """For fp32 inputs, the same result as rounding the fp32 bit pattern (add 0x7FFF plus the
+    lowest kept bit, drop the low 16 bits)."""
+    rng = np.random.default_rng(6)
+    u = rng.integers(0, 0x7F7F0000, 20000, dtype=np.uint64).astype(np.uint32)
+    u |= (rng.integers(0, 2, 20000).astype(np.uint32) << np.uint32(31))
+    f = u.view(np.float32)
+    want = ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    assert np.array_equal(O.encode_bf16(f.astype(np.float64)), want)
+
