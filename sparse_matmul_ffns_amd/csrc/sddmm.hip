@@ -322,23 +322,44 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) b_row[j] = wn * 128 + 32 * j + l32;   // = sd_xrow(wn*128 + 4*l32 + j)
 
+  // A stage is four 16-k sub-steps of 4 x FM matrix instructions.  The operands of sub-step kk+1
+  // (FM A and 4 B fragments) are read into the second of two register sets while sub-step kk's
+  // instructions run, so the LDS latency is exposed once per stage (after the barrier) instead of
+  // before every group of instructions.
+  auto read_ops = [&](const unsigned char* st, int kk, bf16x8 (&a)[FM], bf16x8 (&b)[4]) {
+    const int c = 2 * kk + aa;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = *reinterpret_cast<const bf16x8*>(st + Cfg::A_BYTES + b_row[j] * (TK * 2) + ((c ^ sd_swz(b_row[j])) << 4));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(st + a_row[i] * (TK * 2) + ((c ^ sd_swz(a_row[i])) << 4));
+  };
+  auto mma = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
   auto compute = [&](int kt) {
     const unsigned char* st = smem + (kt % STAGES) * Cfg::STAGE;
-#pragma unroll
-    for (int kk = 0; kk < TK / 16; ++kk) {
-      const int c = 2 * kk + aa;
-      bf16x8 a[FM];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(st + a_row[i] * (TK * 2) + ((c ^ sd_swz(a_row[i])) << 4));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(st + Cfg::A_BYTES + b_row[j] * (TK * 2) +
-                                                           ((c ^ sd_swz(b_row[j])) << 4));
-#pragma unroll
-        for (int i = 0; i < FM; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][j], 0, 0, 0);
-      }
-    }
+    bf16x8 a0[FM], b0[4], a1[FM], b1[4];
+    // the scheduling barriers keep each group of reads ahead of the instructions before it
+    // (the scheduler would otherwise sink every read next to its first use)
+    read_ops(st, 0, a0, b0);
+    read_ops(st, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_ops(st, 2, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_ops(st, 3, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
   };
 
   // Dt: stage kt of this row panel is written by the workgroup whose column tile is kt % ntn
