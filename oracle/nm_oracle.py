@@ -15,7 +15,8 @@ Sources (page title, section):
             pruning, the VENOM compressed storage format, the Spatha SpMM
             library; the three figures are missing from the page).
   [SLOPE]   NSF PAR award 2340011 listing, SLOPE abstract (double-pruned
-            backward pass: the transposed weight is re-pruned with N:M).
+            backward pass: the transposed weight is re-pruned with N:M; lazy
+            low-rank adapters added to the sparse weight late in training).
   [2:4+]    "To 2:4 Sparsity and Beyond: Neuron-level Activation Function to
             Accelerate LLM Pre-Training", abstract (2:4 weights and v:n:m
             (Venom) activations in every FFN matmul).
@@ -40,6 +41,9 @@ Readings taken where the pages are silent (all of them listed in the design doc):
   * the double-pruned transpose re-prunes the already pruned weight W_s;
   * a compress call whose mask keeps a count other than N in a group stores
     +0.0 values at positions 0..N-1 for that group and counts the group.
+  * the low-rank adapter is a pair of dense factors U [R, r], Vt [r, K] in the
+    weight's dtype; the adapted layer computes W_s @ B + U @ (Vt @ B), with the
+    adapter's inner activations Vt @ B formed first and returned as well.
 """
 
 from __future__ import annotations
@@ -371,6 +375,31 @@ def sddmm_nm_rows(D_raw, X_raw, meta, rows, Kc, dtype):
     pos = unpack_positions(meta[rows], len(rows), Kc, 2, 4)
     cols = (np.arange(Kc // 4)[None, :, None] * 4 + pos).reshape(len(rows), Kc // 2)
     return np.take_along_axis(full, cols, axis=1)
+
+
+# ---------------------------------------------------------------------------
+# sparse plus low-rank  [SLOPE abstract: low-rank adapters joined to the sparse
+# weight for the last iterations of pre-training, at little extra cost]
+# ---------------------------------------------------------------------------
+
+def spmm_nm_lowrank(values, meta, R, K, B_raw, U_raw, Vt_raw, dtype):
+    """Sparse weight plus a low-rank adapter, applied lazily, in float64.
+
+    The adapted weight is W_s + U @ Vt (U [R, r], Vt [r, K]); it is never formed.
+    The adapter's inner activations T = Vt @ B [r, Nc] are computed first, then
+    C = decompress(values, meta) @ B + U @ T.  Returns (C, T).
+    """
+    T = decode(Vt_raw, dtype) @ decode(B_raw, dtype)
+    C = spmm_nm(values, meta, R, K, B_raw, dtype) + decode(U_raw, dtype) @ T
+    return C, T
+
+
+def spmm_nm_lowrank_rows(values, meta, rows, K, B_raw, U_raw, Vt_raw, dtype):
+    """spmm_nm_lowrank restricted to the given rows of the output (sampled checks at full size)."""
+    A = decode(decompress_nm(values[rows], meta[rows], len(rows), K, 2, 4), dtype)
+    B = decode(B_raw, dtype)
+    T = decode(Vt_raw, dtype) @ B
+    return A @ B + decode(U_raw[rows], dtype) @ T
 
 
 # ---------------------------------------------------------------------------

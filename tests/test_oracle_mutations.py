@@ -111,6 +111,29 @@ def _encode_truncate(x):
     return (np.asarray(x, np.float64).astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)  # mistake: chops
 
 
+_orig_spmm = O.spmm_nm
+
+
+def _lowrank_dropped(values, meta, R, K, B_raw, U_raw, Vt_raw, dtype):
+    T = O.decode(Vt_raw, dtype) @ O.decode(B_raw, dtype)
+    return _orig_spmm(values, meta, R, K, B_raw, dtype), T        # mistake: adapter term left out
+
+
+def _lowrank_minus(values, meta, R, K, B_raw, U_raw, Vt_raw, dtype):
+    T = O.decode(Vt_raw, dtype) @ O.decode(B_raw, dtype)
+    return _orig_spmm(values, meta, R, K, B_raw, dtype) - O.decode(U_raw, dtype) @ T, T   # mistake: sign
+
+
+def _lowrank_rows_reversed(values, meta, R, K, B_raw, U_raw, Vt_raw, dtype):
+    T = O.decode(Vt_raw, dtype) @ O.decode(B_raw, dtype)
+    return _orig_spmm(values, meta, R, K, B_raw, dtype) + O.decode(U_raw, dtype)[::-1] @ T, T  # mistake: U rows
+
+
+def _lowrank_k_reversed(values, meta, R, K, B_raw, U_raw, Vt_raw, dtype):
+    T = O.decode(Vt_raw, dtype)[:, ::-1] @ O.decode(B_raw, dtype)   # mistake: Vt index order
+    return _orig_spmm(values, meta, R, K, B_raw, dtype) + O.decode(U_raw, dtype) @ T, T
+
+
 MUTATIONS = [
     ("nm_select", _select_tie_high, [lambda: P.test_nm_select_exhaustive_m4(2, "f32")]),
     ("nm_select", _select_no_ties, [lambda: P.test_prune_compress_invariants(2, 4, "bf16")]),
@@ -126,6 +149,11 @@ MUTATIONS = [
                                       lambda: P.test_encode_bf16_is_nearest_ties_even_brute()]),
     ("encode_bf16", _encode_truncate, [lambda: P.test_encode_bf16_known_values(),
                                        lambda: P.test_encode_bf16_matches_fp32_bit_rounding()]),
+    ("spmm_nm_lowrank", _lowrank_dropped, [lambda: P.test_spmm_lowrank_exact_integers()]),
+    ("spmm_nm_lowrank", _lowrank_minus, [lambda: P.test_spmm_lowrank_is_the_adapted_weight_times_b()]),
+    ("spmm_nm_lowrank", _lowrank_rows_reversed, [lambda: P.test_spmm_lowrank_exact_integers(),
+                                                 lambda: P.test_spmm_lowrank_special_cases()]),
+    ("spmm_nm_lowrank", _lowrank_k_reversed, [lambda: P.test_spmm_lowrank_exact_integers()]),
 ]
 
 

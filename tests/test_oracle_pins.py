@@ -327,6 +327,70 @@ def test_sddmm_exact_rational():
     assert np.array_equal(O.sddmm_nm_rows(D, X, meta, rows, Kc, "bf16"), got[rows])
 
 
+# ---------------------------------------------------------------------------
+# sparse plus low-rank: exact integer sums, the adapted weight, special cases
+# ---------------------------------------------------------------------------
+
+def _lowrank_case(R, K, Nc, r, seed, ints):
+    gen = synth.small_ints if ints else synth.normal
+    raw, vals, meta = _compressed(R, K, seed, "bf16", ints=ints)
+    B = gen((K, Nc), seed + 1, dtype="bf16")
+    U = gen((R, r), seed + 2, dtype="bf16")
+    Vt = gen((r, K), seed + 3, dtype="bf16")
+    return raw, vals, meta, B, U, Vt
+
+
+def test_spmm_lowrank_exact_integers():
+    # small integers: every sum is an integer far below 2**53, so the float64 result must equal
+    # the integer arithmetic done here element by element
+    R, K, Nc, r = 6, 16, 5, 3
+    raw, vals, meta, B, U, Vt = _lowrank_case(R, K, Nc, r, 80, ints=True)
+    C, T = O.spmm_nm_lowrank(vals, meta, R, K, B, U, Vt, "bf16")
+    mask = O.prune_nm(raw, "bf16", 2, 4)
+    a = [[int(v) for v in row] for row in synth.bf16_bits_to_f32(raw)]
+    b = [[int(v) for v in row] for row in synth.bf16_bits_to_f32(B)]
+    u = [[int(v) for v in row] for row in synth.bf16_bits_to_f32(U)]
+    vt = [[int(v) for v in row] for row in synth.bf16_bits_to_f32(Vt)]
+    for j in range(r):
+        for n in range(Nc):
+            assert T[j, n] == sum(vt[j][k] * b[k][n] for k in range(K))
+    for i in range(R):
+        for n in range(Nc):
+            sparse = sum(a[i][k] * b[k][n] for k in range(K) if mask[i, k])
+            adapter = sum(u[i][j] * sum(vt[j][k] * b[k][n] for k in range(K)) for j in range(r))
+            assert C[i, n] == sparse + adapter
+
+
+def test_spmm_lowrank_is_the_adapted_weight_times_b():
+    # (W_s + U Vt) B, formed densely, is the same product evaluated in another order
+    R, K, Nc, r = 12, 32, 7, 4
+    _, vals, meta, B, U, Vt = _lowrank_case(R, K, Nc, r, 84, ints=False)
+    C, _ = O.spmm_nm_lowrank(vals, meta, R, K, B, U, Vt, "bf16")
+    W = O.decode(O.decompress_nm(vals, meta, R, K, 2, 4), "bf16") + O.decode(U, "bf16") @ O.decode(Vt, "bf16")
+    assert np.allclose(C, W @ O.decode(B, "bf16"), rtol=1e-12, atol=1e-12)
+
+
+def test_spmm_lowrank_special_cases():
+    R, K, Nc, r = 8, 16, 6, 2
+    _, vals, meta, B, U, Vt = _lowrank_case(R, K, Nc, r, 88, ints=True)
+    zeroU = np.zeros_like(U)
+    C, T = O.spmm_nm_lowrank(vals, meta, R, K, B, zeroU, Vt, "bf16")
+    assert np.array_equal(C, O.spmm_nm(vals, meta, R, K, B, "bf16"))
+    # one-hot factors: the adapter adds row k = 5 of B to output row i = 3 (and nothing else)
+    one = synth.f32_to_bf16_bits(np.float32([1.0]))[0]
+    Ue = np.zeros_like(U)
+    Ue[3, 1] = one
+    Ve = np.zeros_like(Vt)
+    Ve[1, 5] = one
+    C, T = O.spmm_nm_lowrank(vals, meta, R, K, B, Ue, Ve, "bf16")
+    want = O.spmm_nm(vals, meta, R, K, B, "bf16")
+    want[3] += O.decode(B, "bf16")[5]
+    assert np.array_equal(C, want)
+    assert np.array_equal(T[1], O.decode(B, "bf16")[5]) and not T[0].any()
+    rows = np.array([6, 0, 3])
+    assert np.array_equal(O.spmm_nm_lowrank_rows(vals, meta, rows, K, B, Ue, Ve, "bf16"), C[rows])
+
+
 def test_tolerance_check():
     ref = np.array([[1.0, -2.0]])
     bound = np.array([[1.0, 2.0]])
