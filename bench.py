@@ -118,6 +118,35 @@ def _w_nm(w, dtype):
     return steps, flops, algo, kernel
 
 
+def _w_lowrank(w):
+    import torch
+    import sparse_matmul_ffns_amd as nm
+    from sparse_matmul_ffns_amd import synth
+    R, K, Nc, r = w["R"], w["K"], w["Nc"], w["rank"]
+    A = _dev(synth.normal((R, K), w["A"]["seed"], w["A"]["mean"], w["A"]["std"]))
+    B = _dev(synth.normal((K, Nc), w["B"]["seed"], w["B"]["mean"], w["B"]["std"]))
+    U = _dev(synth.normal((R, r), w["U"]["seed"], w["U"]["mean"], w["U"]["std"]))
+    Vt = _dev(synth.normal((r, K), w["Vt"]["seed"], w["Vt"]["mean"], w["Vt"]["std"]))
+    mask = torch.empty((R, K), dtype=torch.uint8, device="cuda")
+    nv, mb, _ = nm.sizes(R, K, 2, 4)
+    vals = torch.empty((R, nv // R), dtype=A.dtype, device="cuda")
+    meta = torch.empty((R, mb // R), dtype=torch.uint8, device="cuda")
+    Bt = torch.empty((Nc, K), dtype=B.dtype, device="cuda")
+    C = torch.empty((R, Nc), dtype=torch.float32, device="cuda")
+    Tt = torch.empty((Nc, r), dtype=torch.float32, device="cuda")
+    # the 2:4 step with a low-rank adapter: the adapter's inner activations (one launch), then the
+    # SpMM with the adapter term added to its accumulators
+    steps = [
+        ("nm_prune_compress_transpose",
+         lambda: nm.nm_prune_compress_transpose(A, B, 2, 4, mask=mask, values=vals, meta=meta, Bt=Bt)),
+        ("spmm_nm_t_lowrank", lambda: nm.spmm_nm_t_lowrank(vals, meta, K, Bt, U, Vt, out=C, Tt=Tt)),
+    ]
+    # dense-equivalent flops of the adapted layer: those of the dense [R x K] weight it stands for
+    flops = {"spmm_nm_t_lowrank": 2.0 * R * K * Nc}
+    algo = {"spmm_nm_t_lowrank": ("mfma", R * (K // 2) * Nc * 2.0 + 2.0 * r * K * Nc + 2.0 * R * r * Nc)}
+    return steps, flops, algo, "spmm_nm_t_lowrank"
+
+
 def _w_venom(w, relu):
     import torch
     import sparse_matmul_ffns_amd as nm
@@ -182,6 +211,8 @@ def build_workload(name):
     w = synth.WORKLOADS[name]
     if w["kind"] == "spmm_nm":
         return _w_nm(w, w["dtype"])
+    if w["kind"] == "spmm_nm_lowrank":
+        return _w_lowrank(w)
     if w["kind"] == "spmm_venom":
         return _w_venom(w, relu=False)
     if w["kind"] == "act_venom":
@@ -214,6 +245,19 @@ def cpu_baseline(name):
         dt = time.perf_counter() - t0
         fl = 2.0 * rows * K * Nc
         sample = f"whole workload, one step: prune + compress of the [{R}x{K}] weight, fp64 decompress-and-dgemm with the [{K}x{Nc}] operand"
+    elif w["kind"] == "spmm_nm_lowrank":
+        R, K, Nc, r = w["R"], w["K"], w["Nc"], w["rank"]
+        A = synth.normal((R, K), w["A"]["seed"], w["A"]["mean"], w["A"]["std"])
+        B = synth.normal((K, Nc), w["B"]["seed"], w["B"]["mean"], w["B"]["std"])
+        U = synth.normal((R, r), w["U"]["seed"], w["U"]["mean"], w["U"]["std"])
+        Vt = synth.normal((r, K), w["Vt"]["seed"], w["Vt"]["mean"], w["Vt"]["std"])
+        t0 = time.perf_counter()
+        v, m, _ = O.compress_nm(A, O.prune_nm(A, "bf16", 2, 4), 2, 4)
+        O.spmm_nm_lowrank(v, m, R, K, B, U, Vt, "bf16")
+        dt = time.perf_counter() - t0
+        fl = 2.0 * R * K * Nc
+        sample = (f"whole workload, one step: prune + compress of the [{R}x{K}] weight, fp64 decompress-and-dgemm "
+                  f"with the [{K}x{Nc}] operand plus the rank-{r} adapter")
     else:
         R, K, Nc, V, M = w["R"], w["K"], w["Nc"], w["V"], w["M"]
         rows = min(R, 4 * V)
@@ -240,6 +284,7 @@ def cpu_baseline(name):
 _KERNEL_SOURCES = {
     "spmm_nm": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp"],
     "spmm_nm_t": ["spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
+    "spmm_nm_t_lowrank": ["lowrank.hip", "spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
     "spmm_venom": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp"],
     "sddmm_nm": ["sddmm.hip", "common.hpp", "dma.hpp"],
     "sddmm_nm_dt": ["sddmm.hip", "common.hpp", "dma.hpp"],

@@ -184,6 +184,35 @@ nm_status spmm_nm_t_out_bf16(nm_dtype dt, const void* values, const uint8_t* met
                              int64_t ldc, nm_stream stream);
 
 /*
+ * spmm_nm_t_lowrank -- spmm_nm_t of a 2:4 weight plus a low-rank adapter,
+ * applied lazily (SLOPE abstract, NSF PAR award 2340011: low-rank adapters
+ * joined to the sparse weight late in pre-training).  The adapted weight
+ * W_s + U Vt is never formed:
+ *   Tt[n][j] = sum_k Bt[n][k] * Vt[j][k]                   (adapter's inner activations)
+ *   C[r][n]  = sum_k decompress(values, meta)[r][k] * Bt[n][k] + sum_j U[r][j] * Tt[n][j]
+ *   values, meta, Bt as for spmm_nm_t (dtype dt)
+ *   U      [R][ldu] dense, dtype dt, ldu >= rank
+ *   Vt     [rank][ldvt] dense, dtype dt, ldvt >= K
+ *   Tt     [Nc][rank] fp32 output, contiguous (row n holds the rank inner
+ *          activations of column n of B; caller-allocated, kept for the
+ *          adapter's backward)
+ *   C      [R][ldc] fp32 output, C[r][n] for n < Nc
+ * Two launches on the stream.  K must be a multiple of 4 and 0 < rank <= 2^20;
+ * no output may overlap an input or the other output.  Errors as for
+ * spmm_nm_t (U and Vt aligned to their element size, Tt and C to 4 bytes).
+ * With bf16, rank % 16 == 0, rank <= 128, K % 16 == 0, ldbt, ldvt and ldu
+ * multiples of 8 and Bt, Vt, U and Tt 16-byte aligned, Tt comes from matrix
+ * instructions and the adapter term is added inside the pipelined SpMM (when
+ * that kernel's own conditions hold); each Tt value then enters that term as
+ * two bf16 parts (about 16 significant bits).  Other calls take plain fp32
+ * kernels after the SpMM.
+ */
+nm_status spmm_nm_t_lowrank(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R,
+                            int64_t K, const void* Bt, int64_t ldbt, int64_t Nc, const void* U,
+                            int64_t ldu, const void* Vt, int64_t ldvt, int64_t rank, float* Tt,
+                            float* C, int64_t ldc, nm_stream stream);
+
+/*
  * nm_transpose -- dst[c][r] = src[r][c] for an R x Cn matrix: turns a row-major
  * dense operand B [K][Nc] into the K-contiguous form spmm_nm_t takes.
  *   src [R][lds], dst [Cn][ldd] (ldd >= R), dtype dt; dst must not overlap src.

@@ -20,6 +20,7 @@ from .nmsparse import (  # noqa: F401
     sizes,
     spmm_nm,
     spmm_nm_t,
+    spmm_nm_t_lowrank,
     spmm_venom,
     transpose,
 )

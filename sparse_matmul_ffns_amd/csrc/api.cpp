@@ -110,6 +110,21 @@ nm_status spmm_nm_t_out_bf16(nm_dtype dt, const void* values, const uint8_t* met
                                                   hs(stream)));
 }
 
+nm_status spmm_nm_t_lowrank(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                            const void* Bt, int64_t ldbt, int64_t Nc, const void* U, int64_t ldu, const void* Vt,
+                            int64_t ldvt, int64_t rank, float* Tt, float* C, int64_t ldc, nm_stream stream) {
+  if (!values || !meta || !Bt || !U || !Vt || !Tt || !C) return NM_ERR_NULL;
+  if (!dtype_ok(dt)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || Nc <= 0 || rank <= 0 || rank > (1 << 20) || K % 4 != 0 || ldbt < K || ldc < Nc ||
+      ldu < rank || ldvt < K)
+    return NM_ERR_SHAPE;
+  if (!aligned(values, esize(dt)) || !aligned(Bt, esize(dt)) || !aligned(U, esize(dt)) || !aligned(Vt, esize(dt)) ||
+      !aligned(Tt, 4) || !aligned(C, 4))
+    return NM_ERR_ALIGN;
+  return hip_status(nms::launch_spmm_nm_t_lowrank(dt, values, meta, R, K, Bt, ldbt, Nc, U, ldu, Vt, ldvt, rank, Tt, C,
+                                                  ldc, hs(stream)));
+}
+
 nm_status nm_transpose(nm_dtype dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst, int64_t ldd,
                        nm_stream stream) {
   if (!src || !dst) return NM_ERR_NULL;

@@ -113,6 +113,24 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
+// Eight fp32 values (a, then b) as two bf16x8 parts: hi holds the top 16 bits of each value (the
+// value truncated), lo the remainder rounded to nearest even, so hi + lo keeps about 16
+// significant bits of a finite value.  Products of bf16 operands with both parts, summed in fp32,
+// carry an fp32 operand through bf16 matrix instructions.
+__device__ inline void split_bf16x8(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  u32x4 h, l;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t b0 = __float_as_uint(v[2 * q]), b1 = __float_as_uint(v[2 * q + 1]);
+    const uint32_t t0 = b0 & 0xFFFF0000u, t1 = b1 & 0xFFFF0000u;
+    h[q] = (b0 >> 16) | t1;
+    l[q] = (uint32_t)f32_to_bf16_rne(v[2 * q] - __uint_as_float(t0)) |
+           ((uint32_t)f32_to_bf16_rne(v[2 * q + 1] - __uint_as_float(t1)) << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
 // One output element of a product: fp32 as is, bf16 rounded to nearest even.
 __device__ inline void store_out(float* p, float v) { *p = v; }
 __device__ inline void store_out(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }

@@ -54,6 +54,13 @@ hipError_t launch_spmm_nm_nt_dma_bf16out(const void* values, const uint8_t* meta
                                          int64_t ldbt, int64_t Nc, uint16_t* C, int64_t ldc, hipStream_t s);
 hipError_t launch_spmm_nm_t_bf16out(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
                                    const void* Bt, int64_t ldbt, int64_t Nc, uint16_t* C, int64_t ldc, hipStream_t s);
+hipError_t launch_spmm_nm_nt_dma_lowrank(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
+                                         int64_t ldbt, int64_t Nc, const void* U, int64_t ldu, const float* Tt,
+                                         int rank, float* C, int64_t ldc, hipStream_t s);
+hipError_t launch_spmm_nm_t_lowrank(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                                    const void* Bt, int64_t ldbt, int64_t Nc, const void* U, int64_t ldu,
+                                    const void* Vt, int64_t ldvt, int64_t rank, float* Tt, float* C, int64_t ldc,
+                                    hipStream_t s);
 hipError_t launch_nm_transpose(int dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst, int64_t ldd,
                                hipStream_t s);
 hipError_t launch_sddmm_nm_dt(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,

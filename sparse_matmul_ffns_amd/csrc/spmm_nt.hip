@@ -59,10 +59,13 @@ struct NtCfg {
 };
 
 // OutT: float (fp32 C) or uint16_t (bf16 C, each fp32 sum rounded to nearest even).
-template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT>
+// LR: add a low-rank adapter term U Tt^T to the accumulators before they are stored (U [R][ldu]
+// bf16, Tt [Nc][rank] fp32, rank a multiple of 16; unused otherwise).
+template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT, bool LR>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
     const uint16_t* __restrict__ values, const uint8_t* __restrict__ meta, int64_t R, int64_t Kd,
-    const uint16_t* __restrict__ Bt, int64_t ldbt, int64_t Nc, OutT* __restrict__ C, int64_t ldc) {
+    const uint16_t* __restrict__ Bt, int64_t ldbt, int64_t Nc, OutT* __restrict__ C, int64_t ldc,
+    const uint16_t* __restrict__ U, int64_t ldu, const float* __restrict__ Tt, int rank) {
   using Cfg = NtCfg<BM, BN, WAVES_M, WAVES_N>;
   constexpr int FM = Cfg::FM, FN = Cfg::FN;
   extern __shared__ __align__(1024) unsigned char smem[];
@@ -201,14 +204,57 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
   issue_a(0, 0);
   issue_m(0, 0);
   issue_b(0, 0);
+  // Low-rank adapter operands (LR): U in 64-column stages through the values buffers, Tt in
+  // 32-column fp32 stages through the Bt buffers, rows of 128 bytes with the same swizzles.  Chunks
+  // past the adapter's width repeat its last chunk (never read as operands).
+  auto issue_u = [&](int buf, int u) {
+    const uint32_t st = smem_base + Cfg::OFF_A + buf * Cfg::SA;
+    const int nch = (rank - 64 * u) / 8 < 8 ? (rank - 64 * u) / 8 : 8;
+#pragma unroll
+    for (int t = 0; t < Cfg::A_INSTR; ++t) {
+      const int r = 8 * (wave * Cfg::A_INSTR + t) + (lane >> 3);
+      int64_t row = m0 + r;
+      row = row < R ? row : R - 1;
+      int c = nt_apos(r, lane & 7);
+      c = c < nch ? c : nch - 1;
+      dma16s((uint32_t)(2 * (row * ldu + 64 * u + 8 * c)), U, uniform(st + (wave * Cfg::A_INSTR + t) * 1024));
+    }
+  };
+  auto issue_tt = [&](int buf, int s) {
+    const uint32_t st = smem_base + Cfg::OFF_B + buf * Cfg::SB;
+    const int nch = (rank - 32 * s) / 4 < 8 ? (rank - 32 * s) / 4 : 8;
+#pragma unroll
+    for (int t = 0; t < Cfg::B_INSTR; ++t) {
+      const int n = 8 * (wave * Cfg::B_INSTR + t) + (lane >> 3);
+      int64_t col = n0 + n;
+      col = col < Nc ? col : Nc - 1;
+      int c = nt_bpos(n, lane & 7);
+      c = c < nch ? c : nch - 1;
+      dma16s((uint32_t)(4 * (col * rank + 32 * s + 4 * c)), Tt, uniform(st + (wave * Cfg::B_INSTR + t) * 1024));
+    }
+  };
   auto body = [&](int kt, auto wait) {
     wait();
     lds_barrier();   // step kt's operands are in LDS for every wave; every wave is done with step kt-1
     auto am = [&] {
-      if ((kt & 1) == 0) issue_a(((kt >> 1) + 1) & 1, (kt >> 1) + 1 <= jlast ? (kt >> 1) + 1 : jlast);
+      if constexpr (LR) {
+        // the first adapter stage of U takes the place of the repeated last values super-stage
+        if ((kt & 1) == 0 && (kt >> 1) + 1 > jlast) issue_u(((kt >> 1) + 1) & 1, 0);
+        else if ((kt & 1) == 0) issue_a(((kt >> 1) + 1) & 1, (kt >> 1) + 1);
+      } else {
+        if ((kt & 1) == 0) issue_a(((kt >> 1) + 1) & 1, (kt >> 1) + 1 <= jlast ? (kt >> 1) + 1 : jlast);
+      }
       if ((kt & 3) == 0) issue_m(((kt >> 2) + 1) & 1, (kt >> 2) + 1 <= clast ? (kt >> 2) + 1 : clast);
     };
-    step(kt, [&] { issue_b((kt + 1) & 1, kt + 1 < KT ? kt + 1 : KT - 1); }, am);
+    step(kt, [&] {
+      if constexpr (LR) {
+        if (kt + 1 == KT) {   // the first Tt stage takes the place of the repeated last Bt step
+          issue_tt(KT & 1, 0);
+          return;
+        }
+      }
+      issue_b((kt + 1) & 1, kt + 1 < KT ? kt + 1 : KT - 1);
+    }, am);
   };
   for (int kt = 0; kt < KT; kt += 4) {
     body(kt, [] { wait_vmcnt<0>(); });
@@ -217,6 +263,52 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
     body(kt + 3, [] { wait_vmcnt<Cfg::A_INSTR>(); });
   }
   wait_vmcnt<0>();   // drain: no load may land in LDS after the workgroup ends
+
+  if constexpr (LR) {
+    // Adapter steps s = 0 .. ceil(rank/32)-1 after the sparse ones: acc[i][j] += U[rows of
+    // fragment i][32s..32s+31] . Tt[columns of fragment j][32s..32s+31], one 16-wide slice at a
+    // time by v_mfma_f32_32x32x16_bf16 (A operand: U row l%32, k = 8*(l/32)..+7; B operand: Tt row
+    // l%32, the same k; the result layout is the accumulators' own).  Tt stage s sits in Bt buffer
+    // (KT + s) % 2 and U stage s/2 in values buffer (jlast + 1 + s/2) % 2; each step issues the
+    // next stages after its barrier, as the sparse steps do.  Tt is fp32: each value enters as two
+    // bf16 parts (its top 16 bits, then the remainder rounded to nearest even), about 16
+    // significant bits in all.  Rows and columns past the matrix read the last one; their sums are
+    // never stored.
+    const int S = (rank + 31) / 32, NU = (rank + 63) / 64;
+    for (int s = 0; s < S; ++s) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (s + 1 < S) issue_tt((KT + s + 1) & 1, s + 1);
+      if ((s & 1) == 0 && (s >> 1) + 1 < NU) issue_u((jlast + 2 + (s >> 1)) & 1, (s >> 1) + 1);
+      const unsigned char* Us = smem + Cfg::OFF_A + ((jlast + 1 + (s >> 1)) & 1) * Cfg::SA;
+      const unsigned char* Ts = smem + Cfg::OFF_B + ((KT + s) & 1) * Cfg::SB;
+      const int nh = rank - 32 * s >= 32 ? 2 : 1;
+      for (int h = 0; h < nh; ++h) {
+        const int hu = 2 * (s & 1) + h;   // 16-wide slice within the U stage
+        bf16x8 ua[FM], th[FN], tl[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int r = (wm * FM + i) * 32 + l32;
+          ua[i] = *reinterpret_cast<const bf16x8*>(Us + r * 128 + (nt_apos(r, 2 * hu + aa) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int n = wn * Cfg::WN + 32 * j + l32;
+          const unsigned char* row = Ts + n * 128;
+          split_bf16x8(*reinterpret_cast<const f32x4*>(row + (nt_bpos(n, 4 * h + 2 * aa) << 4)),
+                       *reinterpret_cast<const f32x4*>(row + (nt_bpos(n, 4 * h + 2 * aa + 1) << 4)), th[j], tl[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[i], th[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[i], tl[j], acc[i][j], 0, 0, 0);
+          }
+      }
+    }
+    wait_vmcnt<0>();
+  }
 
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -237,15 +329,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT>
+template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT, bool LR = false>
 static hipError_t run_nt(const void* values, const uint8_t* meta, int64_t R, int64_t Kd, const void* Bt, int64_t ldbt,
-                         int64_t Nc, OutT* C, int64_t ldc, hipStream_t s) {
+                         int64_t Nc, OutT* C, int64_t ldc, hipStream_t s, const void* U = nullptr, int64_t ldu = 0,
+                         const float* Tt = nullptr, int rank = 0) {
   using Cfg = NtCfg<BM, BN, WAVES_M, WAVES_N>;
-  auto kern = spmm_nt_kernel<BM, BN, WAVES_M, WAVES_N, OutT>;
+  auto kern = spmm_nt_kernel<BM, BN, WAVES_M, WAVES_N, OutT, LR>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   const int64_t ntiles = ((R + BM - 1) / BM) * ((Nc + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg::NT), (size_t)Cfg::LDS, s, (const uint16_t*)values, meta,
-                     R, Kd, (const uint16_t*)Bt, ldbt, Nc, C, ldc);
+                     R, Kd, (const uint16_t*)Bt, ldbt, Nc, C, ldc, (const uint16_t*)U, ldu, Tt, rank);
   return hipGetLastError();
 }
 
@@ -265,6 +358,12 @@ hipError_t launch_spmm_nm_nt_dma(const void* values, const uint8_t* meta, int64_
 hipError_t launch_spmm_nm_nt_dma_bf16out(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
                                          int64_t ldbt, int64_t Nc, uint16_t* C, int64_t ldc, hipStream_t s) {
   return run_nt<256, 256, 2, 4>(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
+}
+
+hipError_t launch_spmm_nm_nt_dma_lowrank(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
+                                         int64_t ldbt, int64_t Nc, const void* U, int64_t ldu, const float* Tt,
+                                         int rank, float* C, int64_t ldc, hipStream_t s) {
+  return run_nt<256, 256, 2, 4, float, true>(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s, U, ldu, Tt, rank);
 }
 
 // ---------------------------------------------------------------------------

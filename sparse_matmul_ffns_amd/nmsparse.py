@@ -37,6 +37,8 @@ _SIGNATURES = {
     "spmm_nm": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t_out_bf16": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
+    "spmm_nm_t_lowrank": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
+                          _vp],
     "nm_transpose": [_int, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "prune_act_venom": [_int, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _i64, _vp],
     "spmm_venom": [_int, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
@@ -255,6 +257,35 @@ def spmm_nm_t(values: torch.Tensor, meta: torch.Tensor, K: int, Bt: torch.Tensor
     _check(lib().spmm_nm_t(_dt(Bt), _p(values), _p(meta), R, K, _p(Bt), _rows(Bt, "Bt"), Nc, _p(out),
                            _rows(out, "out"), _stream()), "spmm_nm_t")
     return out
+
+
+def spmm_nm_t_lowrank(values: torch.Tensor, meta: torch.Tensor, K: int, Bt: torch.Tensor, U: torch.Tensor,
+                      Vt: torch.Tensor, out=None, Tt=None):
+    """A 2:4 weight plus a low-rank adapter, applied lazily: Tt = Bt @ Vt.T ([Nc, rank], fp32) and
+    C = decompress(values, meta) @ Bt.T + U @ Tt.T ([R, Nc], fp32).  Returns (C, Tt)."""
+    _dev(values, meta, Bt, U, Vt, out, Tt)
+    _flat(values, "values"), _flat(meta, "meta")
+    if not (Bt.dtype == values.dtype == U.dtype == Vt.dtype):
+        raise TypeError("values, Bt, U and Vt must share a dtype")
+    R = values.shape[0]
+    Nc = Bt.shape[0]
+    rank = U.shape[1]
+    if Bt.shape[1] != K or Vt.shape[1] != K:
+        raise ValueError("Bt and Vt must have K columns")
+    if U.shape[0] != R or Vt.shape[0] != rank:
+        raise ValueError("U must be [R, rank] and Vt [rank, K]")
+    if out is None:
+        out = torch.empty((R, Nc), dtype=torch.float32, device=Bt.device)
+    if Tt is None:
+        Tt = torch.empty((Nc, rank), dtype=torch.float32, device=Bt.device)
+    if out.dtype != torch.float32 or Tt.dtype != torch.float32:
+        raise TypeError("out and Tt must be fp32")
+    if tuple(Tt.shape) != (Nc, rank) or not Tt.is_contiguous():
+        raise ValueError("Tt must be a contiguous [Nc, rank] tensor")
+    _check(lib().spmm_nm_t_lowrank(_dt(Bt), _p(values), _p(meta), R, K, _p(Bt), _rows(Bt, "Bt"), Nc, _p(U),
+                                   _rows(U, "U"), _p(Vt), _rows(Vt, "Vt"), rank, _p(Tt), _p(out), _rows(out, "out"),
+                                   _stream()), "spmm_nm_t_lowrank")
+    return out, Tt
 
 
 def transpose(X: torch.Tensor, out=None) -> torch.Tensor:

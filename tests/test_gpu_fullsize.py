@@ -110,6 +110,33 @@ def test_ffn_up_nm24_full():
 
 
 # ---------------------------------------------------------------------------
+# 2:4 up-projection with a rank-64 adapter: nm_prune_compress_transpose -> spmm_nm_t_lowrank,
+# W [8192 x 2048], X [2048 x 4096], U [8192 x 64], Vt [64 x 2048]
+# ---------------------------------------------------------------------------
+
+def test_ffn_up_nm24_lowrank64_full():
+    w = synth.WORKLOADS["ffn_up_nm24_lowrank64_8192x2048x4096"]
+    R, K, Nc, r = w["R"], w["K"], w["Nc"], w["rank"]
+    W, X = _gen(w["A"], (R, K)), _gen(w["B"], (K, Nc))
+    U, Vt = _gen(w["U"], (R, r)), _gen(w["Vt"], (r, K))
+    _, fvals, fmeta, fXt = nm.nm_prune_compress_transpose(dev(W, "bf16"), dev(X, "bf16"))
+    C, Tt = nm.spmm_nm_t_lowrank(fvals, fmeta, K, fXt, dev(U, "bf16"), dev(Vt, "bf16"))
+    _finite(C, "spmm_nm_t_lowrank")
+    wv, wm, _ = O.compress_nm(W, O.prune_nm(W, "bf16", 2, 4), 2, 4)
+    assert host(fvals).tobytes() == wv.tobytes() and np.array_equal(host(fmeta), wm)
+    X64, U64, Vt64 = O.decode(X, "bf16"), O.decode(U, "bf16"), O.decode(Vt, "bf16")
+    T64 = Vt64 @ X64                                           # [r, Nc], the oracle's inner activations
+    Tbound = O.abs_bound(Vt64, X64)
+    check_close(host(Tt), T64.T, Tbound.T, "lowrank Tt")
+    rows = _sample(R, 48, 13)
+    want = O.spmm_nm_lowrank_rows(wv, wm, rows, K, X, U, Vt, "bf16")
+    A64r = O.decode(O.decompress_nm(wv[rows], wm[rows], len(rows), K, 2, 4), "bf16")
+    bound = O.abs_bound(A64r, X64) + O.abs_bound(U64[rows], Tbound)
+    got = host(C[torch.as_tensor(rows, device=C.device)])
+    check_close(got, want, bound, "ffn_up lowrank rows")
+
+
+# ---------------------------------------------------------------------------
 # V:N:M (V=64, M=8) down-projection: prune_act_venom -> spmm_venom,
 # W [2048 x 8192], X [8192 x 4096]
 # ---------------------------------------------------------------------------

@@ -317,6 +317,83 @@ def test_spmm_nm_t_out_bf16(R, K, Nc, pb, pc, kind, tier_t):
         assert bool((Cbuf.view(torch.int16)[:, Nc:] == 3).all())
 
 
+LOWRANK_CASES = [
+    # R, K, Nc, rank, pb (Bt and Vt row padding), pc (C padding), pu (U padding)
+    (640, 512, 544, 64, 0, 0, 0),
+    (256, 256, 256, 16, 0, 0, 0),
+    (384, 768, 320, 48, 8, 4, 8),
+    (520, 1024, 264, 128, 0, 0, 0),
+    (256, 512, 200, 96, 0, 0, 0),
+    (64, 256, 40, 32, 0, 0, 0),
+    (200, 256, 72, 8, 0, 0, 0),       # rank % 16 != 0: SIMT adapter kernels
+    (300, 520, 130, 24, 0, 0, 0),     # K % 16 != 0: SIMT everywhere
+]
+
+
+@pytest.mark.parametrize("R,K,Nc,rank,pb,pc,pu", LOWRANK_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}r{c[3]}" for c in LOWRANK_CASES])
+@pytest.mark.parametrize("kind", ["normal", "ints"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_spmm_nm_t_lowrank(R, K, Nc, rank, pb, pc, pu, kind, dtype, tier_t):
+    """C = W_s B + U (Vt B) and Tt = (Vt B)^T against the oracle; bit-exact with small integers
+    while every partial sum stays an exact fp32 integer and every Tt value has at most 16
+    significant bits (the two bf16 parts of the matrix-instruction path)."""
+    raw = _inputs(kind, (R, K), seed=R + K + 21, dtype=dtype)
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, dtype, 2, 4), 2, 4)
+    Btraw = _inputs(kind, (Nc, K), seed=Nc + 23, dtype=dtype)
+    Uraw = _inputs(kind, (R, rank), seed=rank + 25, dtype=dtype)
+    Vtraw = _inputs(kind, (rank, K), seed=rank + K + 27, dtype=dtype)
+    Cbuf = torch.full((R, Nc + pc), float("nan"), dtype=torch.float32, device="cuda")
+    Tt = torch.full((Nc, rank), float("nan"), dtype=torch.float32, device="cuda")
+    C, Tt = nm.spmm_nm_t_lowrank(dev(vals, dtype), dev(meta, "u8"), K, dev(Btraw, dtype, pad=pb), dev(Uraw, dtype, pad=pu),
+                                 dev(Vtraw, dtype, pad=pb), out=Cbuf[:, :Nc], Tt=Tt)
+    C, Tt = host(C), host(Tt)
+    Braw = np.ascontiguousarray(Btraw.T)
+    Cref, Tref = O.spmm_nm_lowrank(vals, meta, R, K, Braw, Uraw, Vtraw, dtype)
+    A64, B64 = O.decode(O.decompress_nm(vals, meta, R, K, 2, 4), dtype), O.decode(Braw, dtype)
+    U64, Vt64 = O.decode(Uraw, dtype), O.decode(Vtraw, dtype)
+    Tbound = O.abs_bound(Vt64, B64)                                  # [rank, Nc]
+    Cbound = O.abs_bound(A64, B64) + O.abs_bound(U64, Tbound)
+    if kind == "ints" and Tbound.max() < 2 ** 16 and Cbound.max() < 2 ** 24:
+        assert np.array_equal(Tt, Tref.T) and np.array_equal(C, Cref)
+    check_close(Tt, Tref.T, Tbound.T, f"lowrank Tt {Nc}x{rank}")
+    check_close(C, Cref, Cbound, f"spmm_nm_t_lowrank {R}x{K}x{Nc} rank {rank}")
+    if pc:
+        assert torch.isnan(Cbuf[:, Nc:]).all()
+
+
+def test_spmm_nm_t_lowrank_dominant_adapter():
+    """An adapter term ten times the sparse one (large U): the two-part bf16 form of Tt keeps the
+    result within tolerance where a single bf16 rounding of Tt would not."""
+    R, K, Nc, rank = 512, 1024, 384, 64
+    raw = synth.normal((R, K), 31, dtype="bf16")
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, "bf16", 2, 4), 2, 4)
+    Btraw = synth.normal((Nc, K), 32, dtype="bf16")
+    Uraw = synth.normal((R, rank), 33, std=10.0, dtype="bf16")
+    Vtraw = synth.normal((rank, K), 34, dtype="bf16")
+    C, Tt = nm.spmm_nm_t_lowrank(dev(vals, "bf16"), dev(meta, "u8"), K, dev(Btraw, "bf16"), dev(Uraw, "bf16"),
+                                 dev(Vtraw, "bf16"))
+    Braw = np.ascontiguousarray(Btraw.T)
+    Cref, Tref = O.spmm_nm_lowrank(vals, meta, R, K, Braw, Uraw, Vtraw, "bf16")
+    U64 = O.decode(Uraw, "bf16")
+    bound = O.abs_bound(O.decode(O.decompress_nm(vals, meta, R, K, 2, 4), "bf16"), O.decode(Braw, "bf16")) + \
+        O.abs_bound(U64, O.abs_bound(O.decode(Vtraw, "bf16"), O.decode(Braw, "bf16")))
+    fro = check_close(host(C), Cref, bound, "dominant adapter")
+    assert fro < 1e-5, fro
+
+
+def test_spmm_nm_t_lowrank_rejects_bad_arguments():
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt, device="cuda")   # noqa: E731
+    m = torch.zeros((8, 2), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):            # U must be [R, rank]
+        nm.spmm_nm_t_lowrank(z(8, 8), m, 16, z(8, 16), z(4, 16), z(16, 16))
+    with pytest.raises(ValueError):            # Tt must be [Nc, rank]
+        nm.spmm_nm_t_lowrank(z(8, 8), m, 16, z(8, 16), z(8, 16), z(16, 16), Tt=z(16, 8, dt=torch.float32))
+    with pytest.raises(TypeError):             # one dtype for every operand
+        nm.spmm_nm_t_lowrank(z(8, 8), m, 16, z(8, 16), z(8, 16, dt=torch.float32), z(16, 16))
+    with pytest.raises(nm.NmError):            # K % 4 != 0: NM_ERR_SHAPE from the C ABI
+        nm.spmm_nm_t_lowrank(z(8, 7), m, 14, z(8, 14), z(8, 16), z(16, 14))
+
+
 TRANSPOSE_CASES = [(64, 64, 0), (2048, 520, 0), (300, 136, 8), (17, 40, 0), (13, 7, 3), (1, 96, 0), (520, 1, 0)]
 
 
