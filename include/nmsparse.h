@@ -200,12 +200,12 @@ nm_status spmm_nm_t_out_bf16(nm_dtype dt, const void* values, const uint8_t* met
  * Two launches on the stream.  K must be a multiple of 4 and 0 < rank <= 2^20;
  * no output may overlap an input or the other output.  Errors as for
  * spmm_nm_t (U and Vt aligned to their element size, Tt and C to 4 bytes).
- * With bf16, rank % 16 == 0, rank <= 128, K % 16 == 0, ldbt, ldvt and ldu
- * multiples of 8 and Bt, Vt, U and Tt 16-byte aligned, Tt comes from matrix
- * instructions and the adapter term is added inside the pipelined SpMM (when
- * that kernel's own conditions hold); each Tt value then enters that term as
- * two bf16 parts (about 16 significant bits).  Other calls take plain fp32
- * kernels after the SpMM.
+ * With bf16, rank % 16 == 0, K % 16 == 0, ldbt, ldvt and ldu multiples of 8
+ * and Bt, Vt, U and Tt 16-byte aligned, Tt comes from matrix instructions and
+ * the adapter term is added inside the pipelined SpMM (when that kernel's own
+ * conditions hold) as extra steps after the sparse ones; each Tt value then
+ * enters that term as two bf16 parts (about 16 significant bits).  Other calls
+ * take plain fp32 kernels after the SpMM.
  */
 nm_status spmm_nm_t_lowrank(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R,
                             int64_t K, const void* Bt, int64_t ldbt, int64_t Nc, const void* U,

@@ -16,9 +16,9 @@ namespace nms {
 
 // Tt[n][j] = sum_k Bt[n][k] Vt[j][k] with bf16 operands and fp32 sums.  One workgroup per
 // 32 x 32 block of Tt (32 rows of Bt, 32 rows of Vt), eight waves.  Both row blocks go to LDS by
-// direct loads of whole 128-byte lines, in stages of 256 k (512-byte rows), four stages per round
-// trip; the 16-byte chunk c of LDS row r holds source chunk c ^ (r % 16), so the operand reads of
-// 16 consecutive rows hit distinct banks.  Wave w multiplies slices 2w and 2w+1 (16 k each) of
+// direct loads of whole 128-byte lines, in stages of 256 k (512-byte rows) through a ring of four
+// buffers; the 16-byte chunk c of LDS row r holds source chunk c ^ (r % 16), so the operand reads
+// of 16 consecutive rows hit distinct banks.  Wave w multiplies slices 2w and 2w+1 (16 k each) of
 // every stage with v_mfma_f32_32x32x16_bf16 (A: Bt row n0 + l%32, k = 8*(l/32)..+7 of the slice;
 // B: Vt row j0 + l%32, the same k).  The eight partial blocks are then added in LDS in a fixed
 // tree order, so results do not depend on timing.
@@ -66,26 +66,30 @@ __global__ __launch_bounds__(512) void lowrank_inner_kernel(const uint16_t* __re
   f32x16 acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-  for (int64_t kb = 0; kb < K; kb += kInnerStages * kInnerStageK) {
-    const int64_t left = (K - kb + kInnerStageK - 1) / kInnerStageK;
-    const int ns = left < kInnerStages ? (int)left : kInnerStages;
-    for (int st = 0; st < ns; ++st) issue_stage(st, kb + st * kInnerStageK);
-    wait_vmcnt<0>();
-    lds_barrier();   // every wave's stages are in LDS
-    for (int st = 0; st < ns; ++st) {
-      const unsigned char* S = smem + st * kInnerStageBytes;
+  // a ring of four stage buffers: stage s is in buffer s % 4; while it is multiplied, the next
+  // two are in flight and stage s + 3 is issued into the buffer stage s - 1 has left
+  const int nst = (int)((K + kInnerStageK - 1) / kInnerStageK);
+  for (int st = 0; st < 3 && st < nst; ++st) issue_stage(st, (int64_t)st * kInnerStageK);
+  for (int st = 0; st < nst; ++st) {
+    const int later = nst - 1 - st < 2 ? nst - 1 - st : 2;   // stages issued after this one
+    if (later == 2) wait_vmcnt<8>();
+    else if (later == 1) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    lds_barrier();   // stage st is in LDS for every wave; every wave is done with stage st - 1
+    if (st + 3 < nst) issue_stage((st + 3) % kInnerStages, (int64_t)(st + 3) * kInnerStageK);
+    const unsigned char* S = smem + (st % kInnerStages) * kInnerStageBytes;
+    const int64_t k0 = (int64_t)st * kInnerStageK;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int sl = 2 * wave + h;
-        if (kb + st * kInnerStageK + 16 * sl >= K) continue;
-        const int c = 2 * sl + aa;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(S + l32 * 512 + (inner_pos(l32, c) << 4));
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(S + 16384 + l32 * 512 + (inner_pos(l32, c) << 4));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int sl = 2 * wave + h;
+      if (k0 + 16 * sl >= K) continue;
+      const int c = 2 * sl + aa;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(S + l32 * 512 + (inner_pos(l32, c) << 4));
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(S + 16384 + l32 * 512 + (inner_pos(l32, c) << 4));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
     }
-    lds_barrier();   // every wave is done reading before the next round's loads land
   }
+  lds_barrier();   // every wave is done reading the stages before LDS is reused below
 
   // waves 4..7 hand their blocks to waves 0..3, then 2..3 to 0..1, then 1 to 0
   float* red = reinterpret_cast<float*>(smem);   // [4 slots][16 elements][64 lanes]
