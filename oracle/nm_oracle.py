@@ -336,6 +336,31 @@ def spmm_nm_loop(values, meta, R, K, B_raw, dtype):
     return C
 
 
+def spmm_nm_general(values, meta, R, K, N, M, B_raw, dtype):
+    """C = decompress(values, meta) @ B in float64 for any N:M compressed matrix."""
+    A = decode(decompress_nm(values, meta, R, K, N, M), dtype)
+    return A @ decode(B_raw, dtype)
+
+
+def spmm_nm_general_loop(values, meta, R, K, N, M, B_raw, dtype):
+    """Same product by the explicit gather loop (small inputs only).
+
+    C[r, n] = sum over groups g and slots s of values[r, N*g+s] * B[M*g + p_s, n].
+    """
+    pos = unpack_positions(meta, R, K, N, M)
+    v = decode(values, dtype)
+    B = decode(B_raw, dtype)
+    C = np.zeros((R, B.shape[1]))
+    for r in range(R):
+        for n in range(B.shape[1]):
+            acc = 0.0
+            for g in range(K // M):
+                for s in range(N):
+                    acc += v[r, N * g + s] * B[M * g + pos[r, g, s], n]
+            C[r, n] = acc
+    return C
+
+
 def spmm_venom(values, meta, colsel, R, K, V, M, B_raw, dtype):
     """C = decompress_venom(...) @ B in float64."""
     A = decode(decompress_venom(values, meta, colsel, R, K, V, M), dtype)

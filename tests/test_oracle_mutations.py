@@ -134,6 +134,14 @@ def _lowrank_k_reversed(values, meta, R, K, B_raw, U_raw, Vt_raw, dtype):
     return _orig_spmm(values, meta, R, K, B_raw, dtype) + O.decode(U_raw, dtype) @ T, T
 
 
+def _general_slot_shift(values, meta, R, K, N, M, B_raw, dtype):
+    pos = O.unpack_positions(meta, R, K, N, M)
+    v = O.decode(values, dtype).reshape(R, K // M, N)
+    A = np.zeros((R, K // M, M))
+    np.put_along_axis(A, pos, np.roll(v, 1, axis=2), axis=2)   # mistake: values paired with the wrong slot
+    return A.reshape(R, K) @ O.decode(B_raw, dtype)
+
+
 MUTATIONS = [
     ("nm_select", _select_tie_high, [lambda: P.test_nm_select_exhaustive_m4(2, "f32")]),
     ("nm_select", _select_no_ties, [lambda: P.test_prune_compress_invariants(2, 4, "bf16")]),
@@ -154,6 +162,7 @@ MUTATIONS = [
     ("spmm_nm_lowrank", _lowrank_rows_reversed, [lambda: P.test_spmm_lowrank_exact_integers(),
                                                  lambda: P.test_spmm_lowrank_special_cases()]),
     ("spmm_nm_lowrank", _lowrank_k_reversed, [lambda: P.test_spmm_lowrank_exact_integers()]),
+    ("spmm_nm_general", _general_slot_shift, [lambda: P.test_spmm_general_gather_loop_and_exact_integers(2, 8)]),
 ]
 
 

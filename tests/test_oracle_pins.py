@@ -300,6 +300,28 @@ def test_spmm_identity_and_linearity():
                           O.spmm_nm(vals, meta, R, K, B1, "bf16") + O.spmm_nm(vals, meta, R, K, B2, "bf16"))
 
 
+@pytest.mark.parametrize("N,M", [(1, 4), (2, 8), (4, 8), (3, 8), (4, 16)])
+def test_spmm_general_gather_loop_and_exact_integers(N, M):
+    R, K, Nc = 5, 4 * M, 4
+    raw = synth.small_ints((R, K), 90 + N + M, dtype="bf16")
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, "bf16", N, M), N, M)
+    B = synth.small_ints((K, Nc), 91 + N + M, dtype="bf16")
+    C = O.spmm_nm_general(vals, meta, R, K, N, M, B, "bf16")
+    assert np.array_equal(C, O.spmm_nm_general_loop(vals, meta, R, K, N, M, B, "bf16"))
+    # exact integer sums over the kept positions, straight from the mask
+    mask = O.prune_nm(raw, "bf16", N, M)
+    a = synth.bf16_bits_to_f32(raw).astype(np.int64) * mask
+    b = synth.bf16_bits_to_f32(B).astype(np.int64)
+    assert np.array_equal(C, (a @ b).astype(np.float64))
+
+
+def test_spmm_general_2of4_is_spmm_nm():
+    R, K = 6, 32
+    _, vals, meta = _compressed(R, K, 95, "bf16")
+    B = synth.normal((K, 3), 96, dtype="bf16")
+    assert np.array_equal(O.spmm_nm_general(vals, meta, R, K, 2, 4, B, "bf16"), O.spmm_nm(vals, meta, R, K, B, "bf16"))
+
+
 def test_spmm_venom_gather_loop_equals_dgemm():
     R, K, V, M, Nc = 8, 32, 4, 8, 5
     raw = synth.normal((R, K), 60, dtype="bf16")
