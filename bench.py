@@ -147,6 +147,32 @@ def _w_lowrank(w):
     return steps, flops, algo, "spmm_nm_t_lowrank"
 
 
+def _w_general(w):
+    import torch
+    import sparse_matmul_ffns_amd as nm
+    from sparse_matmul_ffns_amd import synth
+    R, K, Nc, N, M = w["R"], w["K"], w["Nc"], w["N"], w["M"]
+    A = _dev(synth.normal((R, K), w["A"]["seed"], w["A"]["mean"], w["A"]["std"]))
+    B = _dev(synth.normal((K, Nc), w["B"]["seed"], w["B"]["mean"], w["B"]["std"]))
+    mask = torch.empty((R, K), dtype=torch.uint8, device="cuda")
+    nv, mb, _ = nm.sizes(R, K, N, M)
+    vals = torch.empty((R, nv // R), dtype=A.dtype, device="cuda")
+    meta = torch.empty((R, mb // R), dtype=torch.uint8, device="cuda")
+    Bt = torch.empty((Nc, K), dtype=B.dtype, device="cuda")
+    C = torch.empty((R, Nc), dtype=torch.float32, device="cuda")
+    work = torch.empty(nm.general_work_bytes(A.dtype, R, K, N, M), dtype=torch.uint8, device="cuda")
+    # prune + compress to N:M and the activations' transpose, then the product (for N <= 2 the
+    # matrix is rewritten in 2:4 form in `work` and multiplied by the 2:4 SpMM)
+    steps = [
+        ("nm_prune_compress_transpose",
+         lambda: nm.nm_prune_compress_transpose(A, B, N, M, mask=mask, values=vals, meta=meta, Bt=Bt)),
+        ("spmm_nm_general", lambda: nm.spmm_nm_general(vals, meta, K, N, M, Bt, out=C, work=work)),
+    ]
+    flops = {"spmm_nm_general": 2.0 * R * K * Nc}
+    algo = {"spmm_nm_general": ("mfma", 2.0 * R * (K // M * N) * Nc)}
+    return steps, flops, algo, "spmm_nm_general"
+
+
 def _w_venom(w, relu):
     import torch
     import sparse_matmul_ffns_amd as nm
@@ -213,6 +239,8 @@ def build_workload(name):
         return _w_nm(w, w["dtype"])
     if w["kind"] == "spmm_nm_lowrank":
         return _w_lowrank(w)
+    if w["kind"] == "spmm_nm_general":
+        return _w_general(w)
     if w["kind"] == "spmm_venom":
         return _w_venom(w, relu=False)
     if w["kind"] == "act_venom":
@@ -245,6 +273,17 @@ def cpu_baseline(name):
         dt = time.perf_counter() - t0
         fl = 2.0 * rows * K * Nc
         sample = f"whole workload, one step: prune + compress of the [{R}x{K}] weight, fp64 decompress-and-dgemm with the [{K}x{Nc}] operand"
+    elif w["kind"] == "spmm_nm_general":
+        R, K, Nc, N, M = w["R"], w["K"], w["Nc"], w["N"], w["M"]
+        A = synth.normal((R, K), w["A"]["seed"], w["A"]["mean"], w["A"]["std"])
+        B = synth.normal((K, Nc), w["B"]["seed"], w["B"]["mean"], w["B"]["std"])
+        t0 = time.perf_counter()
+        v, m, _ = O.compress_nm(A, O.prune_nm(A, "bf16", N, M), N, M)
+        O.spmm_nm_general(v, m, R, K, N, M, B, "bf16")
+        dt = time.perf_counter() - t0
+        fl = 2.0 * R * K * Nc
+        sample = (f"whole workload, one step: {N}:{M} prune + compress of the [{R}x{K}] weight, fp64 "
+                  f"decompress-and-dgemm with the [{K}x{Nc}] operand")
     elif w["kind"] == "spmm_nm_lowrank":
         R, K, Nc, r = w["R"], w["K"], w["Nc"], w["rank"]
         A = synth.normal((R, K), w["A"]["seed"], w["A"]["mean"], w["A"]["std"])
@@ -285,6 +324,7 @@ _KERNEL_SOURCES = {
     "spmm_nm": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp"],
     "spmm_nm_t": ["spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
     "spmm_nm_t_lowrank": ["lowrank.hip", "spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
+    "spmm_nm_general": ["general.hip", "spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
     "spmm_venom": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp"],
     "sddmm_nm": ["sddmm.hip", "common.hpp", "dma.hpp"],
     "sddmm_nm_dt": ["sddmm.hip", "common.hpp", "dma.hpp"],

@@ -213,6 +213,36 @@ nm_status spmm_nm_t_lowrank(nm_dtype dt, const void* values, const uint8_t* meta
                             float* C, int64_t ldc, nm_stream stream);
 
 /*
+ * spmm_nm_general -- spmm_nm_t for any N:M form nm_compress writes ("Success
+ * story: ESPLAG", Solution: N:M patterns beyond 2:4):
+ * C[r][n] = sum_k decompress(values, meta, N, M)[r][k] * Bt[n][k]
+ *   values [R][(K/M)*N], meta [R][ceil((K/M)*N*ceil(log2 M)/8)] (the layout of
+ *          nm_compress), dtype dt
+ *   Bt     [Nc][ldbt] dense, dtype dt (K-contiguous, as for spmm_nm_t)
+ *   C      [R][ldc] fp32 output
+ *   work   optional device memory of work_bytes bytes, 16-byte aligned, that
+ *          must not overlap any other argument (NULL allowed)
+ * M in {4, 8, 16}, 1 <= N < M, K % M == 0.  When N <= 2 every aligned run of
+ * 4 columns holds at most two survivors: with work of at least
+ * nm_general_work_bytes(dt, R, K, N, M) bytes the matrix is rewritten there
+ * in 2:4 form (runs padded with +0.0) and spmm_nm_t computes the product; 2:4
+ * itself goes to spmm_nm_t directly.  Other patterns, and N <= 2 without
+ * enough work memory, take a plain SIMT kernel.  Errors as for spmm_nm_t, plus
+ * NM_ERR_UNSUPPORTED for an N:M outside the set above and NM_ERR_SHAPE for
+ * K % M != 0 or work_bytes < 0.
+ */
+nm_status spmm_nm_general(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R,
+                          int64_t K, int N, int M, const void* Bt, int64_t ldbt, int64_t Nc,
+                          float* C, int64_t ldc, void* work, int64_t work_bytes,
+                          nm_stream stream);
+
+/*
+ * nm_general_work_bytes -- host only: the work bytes spmm_nm_general uses for
+ * an R x K matrix in N:M form (0 when it uses none, or for invalid arguments).
+ */
+int64_t nm_general_work_bytes(nm_dtype dt, int64_t R, int64_t K, int N, int M);
+
+/*
  * nm_transpose -- dst[c][r] = src[r][c] for an R x Cn matrix: turns a row-major
  * dense operand B [K][Nc] into the K-contiguous form spmm_nm_t takes.
  *   src [R][lds], dst [Cn][ldd] (ldd >= R), dtype dt; dst must not overlap src.

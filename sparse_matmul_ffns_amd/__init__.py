@@ -19,6 +19,8 @@ from .nmsparse import (  # noqa: F401
     sddmm_nm,
     sizes,
     spmm_nm,
+    spmm_nm_general,
+    general_work_bytes,
     spmm_nm_t,
     spmm_nm_t_lowrank,
     spmm_venom,

@@ -125,6 +125,22 @@ nm_status spmm_nm_t_lowrank(nm_dtype dt, const void* values, const uint8_t* meta
                                                   ldc, hs(stream)));
 }
 
+nm_status spmm_nm_general(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, int N, int M,
+                          const void* Bt, int64_t ldbt, int64_t Nc, float* C, int64_t ldc, void* work,
+                          int64_t work_bytes, nm_stream stream) {
+  if (!values || !meta || !Bt || !C) return NM_ERR_NULL;
+  if (!dtype_ok(dt) || !nm_ok(N, M)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || Nc <= 0 || K % M != 0 || ldbt < K || ldc < Nc || work_bytes < 0) return NM_ERR_SHAPE;
+  if (!aligned(values, esize(dt)) || !aligned(Bt, esize(dt)) || !aligned(C, 4)) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_spmm_nm_general(dt, values, meta, R, K, N, M, Bt, ldbt, Nc, C, ldc, work, work_bytes,
+                                                hs(stream)));
+}
+
+int64_t nm_general_work_bytes(nm_dtype dt, int64_t R, int64_t K, int N, int M) {
+  if (!dtype_ok(dt) || !nm_ok(N, M) || R <= 0 || K <= 0 || K % M != 0) return 0;
+  return nms::general_work_bytes(esize(dt), R, K, N, M);
+}
+
 nm_status nm_transpose(nm_dtype dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst, int64_t ldd,
                        nm_stream stream) {
   if (!src || !dst) return NM_ERR_NULL;

@@ -1,0 +1,173 @@
+// General N:M SpMM with the dense operand K-contiguous: C = decompress(values, meta) Bt^T for any
+// N:M form nm_compress writes (M in {4, 8, 16}, 1 <= N < M; "Success story: ESPLAG", Solution:
+// N:M patterns beyond 2:4 in the VENOM format's family).
+//
+// When N <= 2 every aligned run of 4 columns holds at most two survivors, so the matrix is also a
+// 2:4 matrix once each run is padded to two slots with +0.0: nm_to24_kernel rewrites the compressed
+// form that way (into caller memory) and the 2:4 SMFMAC SpMM does the product at the 2:4 rate.
+// Other patterns (and calls without that memory) take a plain SIMT kernel that decodes the
+// position stream directly.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nms {
+
+// b-bit field at bit offset bo of an LSB-first stream (the field never runs past its row).
+__device__ inline uint32_t nm_field(const uint8_t* row, int64_t bo, int b) {
+  const int64_t byte = bo >> 3;
+  const int sh = (int)(bo & 7);
+  uint32_t w = row[byte];
+  if (sh + b > 8) w |= (uint32_t)row[byte + 1] << 8;
+  return (w >> sh) & ((1u << b) - 1u);
+}
+
+// One thread per (row, output metadata byte): 2:4 runs q = 2t and 2t + 1 (dense columns 4q ..
+// 4q+3) collect the survivors of their N:M group that fall inside them (at most two, in ascending
+// position) and fill the remaining slots with +0.0 at the lowest free positions.
+template <typename T>
+__global__ __launch_bounds__(256) void nm_to24_kernel(const T* __restrict__ values, const uint8_t* __restrict__ meta,
+                                                      int64_t R, int64_t K, int N, int M, T* __restrict__ v24,
+                                                      uint8_t* __restrict__ m24) {
+  const int64_t tpr = (K + 7) / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= R * tpr) return;
+  const int64_t row = idx / tpr, t = idx % tpr;
+  const int b = ceil_log2(M);
+  const int64_t G = K / M;
+  const int64_t vrow = G * N, mrow = (G * N * b + 7) / 8;
+  const uint8_t* mr = meta + row * mrow;
+  uint32_t byte = 0;
+  for (int h = 0; h < 2; ++h) {
+    const int64_t q = 2 * t + h;
+    if (4 * q >= K) break;
+    const int64_t g = (4 * q) / M;
+    const int o = (int)(4 * q - g * M);
+    uint32_t p[2] = {0u, 1u};
+    T v[2] = {T(0), T(0)};
+    int cnt = 0;
+    for (int s = 0; s < N; ++s) {
+      const int pos = (int)nm_field(mr, (g * N + s) * b, b);
+      if (pos >= o && pos < o + 4 && cnt < 2) {
+        p[cnt] = (uint32_t)(pos - o);
+        v[cnt] = values[row * vrow + g * N + s];
+        ++cnt;
+      }
+    }
+    if (cnt == 1) {   // one survivor: pair it with the lowest other position, holding +0.0
+      if (p[0] == 0u) {
+        p[1] = 1u;
+        v[1] = T(0);
+      } else {
+        p[1] = p[0];
+        v[1] = v[0];
+        p[0] = 0u;
+        v[0] = T(0);
+      }
+    }
+    v24[row * (K / 2) + 2 * q] = v[0];
+    v24[row * (K / 2) + 2 * q + 1] = v[1];
+    byte |= (p[0] | (p[1] << 2)) << (4 * h);
+  }
+  m24[row * tpr + t] = (uint8_t)byte;
+}
+
+// Plain SIMT product for any N:M (64 x 64 tiles, 32-k chunks staged densely in LDS): the kept
+// values of each (row, group) are scattered to their dense columns by the decoded positions.
+template <typename T>
+__global__ __launch_bounds__(256) void spmm_general_generic_kernel(const T* __restrict__ values,
+                                                                   const uint8_t* __restrict__ meta, int64_t R,
+                                                                   int64_t K, int N, int M, const T* __restrict__ Bt,
+                                                                   int64_t ldbt, int64_t Nc, float* __restrict__ C,
+                                                                   int64_t ldc) {
+  constexpr int TM = 64, TN = 64, KC = 32;
+  __shared__ float As[KC][TM + 4];
+  __shared__ float Bs[KC][TN + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  const int64_t m0 = (int64_t)blockIdx.y * TM, n0 = (int64_t)blockIdx.x * TN;
+  const int b = ceil_log2(M);
+  const int64_t G = K / M;
+  const int64_t vrow = G * N, mrow = (G * N * b + 7) / 8;
+  float acc[4][4] = {};
+  for (int64_t k0 = 0; k0 < K; k0 += KC) {
+    for (int i = tid; i < KC * TM; i += 256) As[i / TM][i % TM] = 0.f;
+    __syncthreads();
+    const int gpc = KC / M;   // M divides KC
+    for (int u = tid; u < TM * gpc; u += 256) {
+      const int r = u / gpc, gi = u % gpc;
+      const int64_t row = m0 + r, g = k0 / M + gi;
+      if (row >= R || g >= G) continue;
+      for (int s = 0; s < N; ++s) {
+        const uint32_t p = nm_field(meta + row * mrow, (g * N + s) * b, b) & (uint32_t)(M - 1);
+        As[gi * M + p][r] = Elem<T>::to_f32(values[row * vrow + g * N + s]);
+      }
+    }
+    for (int i = tid; i < KC * TN; i += 256) {
+      const int kk = i % KC, nn = i / KC;
+      const int64_t k = k0 + kk, n = n0 + nn;
+      Bs[kk][nn] = (k < K && n < Nc) ? Elem<T>::to_f32(Bt[n * ldbt + k]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < KC; ++kk) {
+      float a[4], bb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bb[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], bb[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = m0 + ty * 4 + i;
+    if (row >= R) continue;
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + tx * 4 + j;
+      if (n < Nc) C[row * ldc + n] = acc[i][j];
+    }
+  }
+}
+
+// Bytes of caller memory the 2:4 route needs (values [R][K/2], then metadata [R][ceil(K/8)] at the
+// next 16-byte boundary); 0 when the pattern does not take that route.
+int64_t general_work_bytes(int esz, int64_t R, int64_t K, int N, int M) {
+  if (N > 2 || (N == 2 && M == 4)) return 0;
+  const int64_t vbytes = (R * (K / 2) * esz + 15) / 16 * 16;
+  return vbytes + R * ((K + 7) / 8);
+}
+
+hipError_t launch_spmm_nm_general(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, int N, int M,
+                                  const void* Bt, int64_t ldbt, int64_t Nc, float* C, int64_t ldc, void* work,
+                                  int64_t work_bytes, hipStream_t s) {
+  if (N == 2 && M == 4) return launch_spmm_nm_t(dt, values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
+  const int esz = dt == DT_BF16 ? 2 : 4;
+  const int64_t need = general_work_bytes(esz, R, K, N, M);
+  if (need > 0 && work && work_bytes >= need && (uintptr_t)work % 16 == 0 && !force_generic()) {
+    unsigned char* w = (unsigned char*)work;
+    uint8_t* m24 = w + (R * (K / 2) * esz + 15) / 16 * 16;
+    const unsigned blocks = (unsigned)((R * ((K + 7) / 8) + 255) / 256);
+    if (dt == DT_BF16)
+      hipLaunchKernelGGL(nm_to24_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, (const uint16_t*)values, meta, R, K,
+                         N, M, (uint16_t*)w, m24);
+    else
+      hipLaunchKernelGGL(nm_to24_kernel<uint32_t>, dim3(blocks), dim3(256), 0, s, (const uint32_t*)values, meta, R, K,
+                         N, M, (uint32_t*)w, m24);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_spmm_nm_t(dt, w, m24, R, K, Bt, ldbt, Nc, C, ldc, s);
+  }
+  const dim3 grid((unsigned)((Nc + 63) / 64), (unsigned)((R + 63) / 64));
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(spmm_general_generic_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)values, meta, R,
+                       K, N, M, (const uint16_t*)Bt, ldbt, Nc, C, ldc);
+  else
+    hipLaunchKernelGGL(spmm_general_generic_kernel<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)values, meta, R,
+                       K, N, M, (const uint32_t*)Bt, ldbt, Nc, C, ldc);
+  return hipGetLastError();
+}
+
+}  // namespace nms

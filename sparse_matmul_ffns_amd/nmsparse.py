@@ -39,6 +39,7 @@ _SIGNATURES = {
     "spmm_nm_t_out_bf16": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t_lowrank": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
                           _vp],
+    "spmm_nm_general": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp],
     "nm_transpose": [_int, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "prune_act_venom": [_int, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _i64, _vp],
     "spmm_venom": [_int, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.nm_sizes.argtypes = [_i64, _i64, _int, _int, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
                                ctypes.POINTER(_i64)]
         L.nm_sizes.restype = None
+        L.nm_general_work_bytes.argtypes = [_int, _i64, _i64, _int, _int]
+        L.nm_general_work_bytes.restype = _i64
         L.nm_status_str.argtypes = [_int]
         L.nm_status_str.restype = ctypes.c_char_p
         L.nm_last_hip_error.argtypes = []
@@ -286,6 +289,41 @@ def spmm_nm_t_lowrank(values: torch.Tensor, meta: torch.Tensor, K: int, Bt: torc
                                    _rows(U, "U"), _p(Vt), _rows(Vt, "Vt"), rank, _p(Tt), _p(out), _rows(out, "out"),
                                    _stream()), "spmm_nm_t_lowrank")
     return out, Tt
+
+
+def general_work_bytes(dtype: torch.dtype, R: int, K: int, N: int, M: int) -> int:
+    """Bytes of work memory spmm_nm_general uses for an R x K matrix in N:M form (0: none)."""
+    return int(lib().nm_general_work_bytes(NM_BF16 if dtype == torch.bfloat16 else NM_F32, R, K, N, M))
+
+
+def spmm_nm_general(values: torch.Tensor, meta: torch.Tensor, K: int, N: int, M: int, Bt: torch.Tensor, out=None,
+                    work="auto"):
+    """C = decompress(values, meta) @ Bt.T for any N:M compressed matrix (fp32 C).  `work`: a uint8
+    device tensor of at least general_work_bytes(...) bytes, None for none, or "auto" to allocate
+    one with torch when the pattern uses it."""
+    _dev(values, meta, Bt, out)
+    _flat(values, "values"), _flat(meta, "meta")
+    if Bt.dtype != values.dtype:
+        raise TypeError("values and Bt must share a dtype")
+    R = values.shape[0]
+    Nc = Bt.shape[0]
+    if Bt.shape[1] != K:
+        raise ValueError("Bt must have K columns")
+    if out is None:
+        out = torch.empty((R, Nc), dtype=torch.float32, device=Bt.device)
+    if isinstance(work, str):
+        if work != "auto":
+            raise ValueError("work must be a tensor, None or 'auto'")
+        nbytes = general_work_bytes(values.dtype, R, K, N, M)
+        work = torch.empty(nbytes, dtype=torch.uint8, device=Bt.device) if nbytes else None
+    if work is not None:
+        _dev(work)
+        _flat(work, "work")
+    _check(lib().spmm_nm_general(_dt(Bt), _p(values), _p(meta), R, K, N, M, _p(Bt), _rows(Bt, "Bt"), Nc, _p(out),
+                                 _rows(out, "out"), _p(work) if work is not None else None,
+                                 work.numel() * work.element_size() if work is not None else 0, _stream()),
+           "spmm_nm_general")
+    return out
 
 
 def transpose(X: torch.Tensor, out=None) -> torch.Tensor:

@@ -137,6 +137,31 @@ def test_ffn_up_nm24_lowrank64_full():
 
 
 # ---------------------------------------------------------------------------
+# 2:8 up-projection: nm_prune_compress_transpose (N:M) -> spmm_nm_general (2:4 form in work memory),
+# W [8192 x 2048], X [2048 x 4096]
+# ---------------------------------------------------------------------------
+
+def test_ffn_up_nm28_full():
+    w = synth.WORKLOADS["ffn_up_nm28_8192x2048x4096"]
+    R, K, Nc, N, M = w["R"], w["K"], w["Nc"], w["N"], w["M"]
+    W, X = _gen(w["A"], (R, K)), _gen(w["B"], (K, Nc))
+    fmask, fvals, fmeta, fXt = nm.nm_prune_compress_transpose(dev(W, "bf16"), dev(X, "bf16"), N, M)
+    want_mask = O.prune_nm(W, "bf16", N, M)
+    assert np.array_equal(host(fmask), want_mask)
+    wv, wm, _ = O.compress_nm(W, want_mask, N, M)
+    assert host(fvals).tobytes() == wv.tobytes() and np.array_equal(host(fmeta), wm)
+    work = torch.empty(nm.general_work_bytes(torch.bfloat16, R, K, N, M), dtype=torch.uint8, device="cuda")
+    C = nm.spmm_nm_general(fvals, fmeta, K, N, M, fXt, work=work)
+    _finite(C, "spmm_nm_general")
+    A64 = O.decode(O.decompress_nm(wv, wm, R, K, N, M), "bf16")
+    X64 = O.decode(X, "bf16")
+    rows = _sample(R, 48, 17)
+    _check_rows(C, A64[rows], X64, rows, "ffn_up 2:8 spmm_nm_general")
+    cols = _sample(Nc, 24, 18)
+    _check_cols(C, A64, X64[:, cols], cols, "ffn_up 2:8 spmm_nm_general")
+
+
+# ---------------------------------------------------------------------------
 # V:N:M (V=64, M=8) down-projection: prune_act_venom -> spmm_venom,
 # W [2048 x 8192], X [8192 x 4096]
 # ---------------------------------------------------------------------------

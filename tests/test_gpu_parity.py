@@ -394,6 +394,55 @@ def test_spmm_nm_t_lowrank_rejects_bad_arguments():
         nm.spmm_nm_t_lowrank(z(8, 7), m, 14, z(8, 14), z(8, 16), z(16, 14))
 
 
+GENERAL_CASES = [
+    # N, M, R, K, Nc
+    (1, 4, 300, 1024, 264),
+    (2, 8, 520, 2048, 136),
+    (1, 8, 256, 512, 96),
+    (2, 16, 384, 1024, 520),
+    (1, 16, 64, 256, 40),
+    (1, 4, 40, 36, 13),        # K % 8 == 4: a half-filled last metadata byte in 2:4 form
+    (2, 4, 256, 512, 256),     # 2:4 itself: spmm_nm_t
+    (4, 8, 200, 256, 72),      # N > 2: the SIMT kernel
+    (3, 8, 64, 128, 40),
+    (8, 16, 130, 512, 33),
+]
+
+
+@pytest.mark.parametrize("N,M,R,K,Nc", GENERAL_CASES, ids=[f"{c[0]}of{c[1]}_{c[2]}x{c[3]}x{c[4]}" for c in GENERAL_CASES])
+@pytest.mark.parametrize("kind", ["normal", "ints"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("work", ["auto", None])
+def test_spmm_nm_general(N, M, R, K, Nc, kind, dtype, work, tier_t):
+    """Any N:M against the oracle; N <= 2 with work memory goes through the 2:4 form (runs padded
+    with +0.0), without it through the SIMT kernel."""
+    raw = _inputs(kind, (R, K), seed=R + K + N + M, dtype=dtype)
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, dtype, N, M), N, M)
+    Btraw = _inputs(kind, (Nc, K), seed=Nc + N, dtype=dtype)
+    C = host(nm.spmm_nm_general(dev(vals, dtype), dev(meta, "u8"), K, N, M, dev(Btraw, dtype), work=work))
+    Braw = np.ascontiguousarray(Btraw.T)
+    Cref = O.spmm_nm_general(vals, meta, R, K, N, M, Braw, dtype)
+    if kind == "ints" and K <= 1024:
+        assert np.array_equal(C, Cref)
+    A64 = O.decode(O.decompress_nm(vals, meta, R, K, N, M), dtype)
+    check_close(C, Cref, O.abs_bound(A64, O.decode(Braw, dtype)), f"spmm_nm_general {N}:{M} {R}x{K}x{Nc}")
+
+
+def test_spmm_nm_general_work_bytes_and_errors():
+    assert nm.general_work_bytes(torch.bfloat16, 8, 64, 2, 8) == 8 * 32 * 2 + 8 * 8
+    assert nm.general_work_bytes(torch.bfloat16, 8, 64, 4, 8) == 0      # N > 2: no 2:4 form
+    assert nm.general_work_bytes(torch.bfloat16, 8, 64, 2, 4) == 0      # 2:4 itself
+    assert nm.general_work_bytes(torch.bfloat16, 8, 60, 2, 8) == 0      # K % M != 0
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt, device="cuda")   # noqa: E731
+    m = torch.zeros((8, 8), dtype=torch.uint8, device="cuda")
+    with pytest.raises(nm.NmError):            # 3:4 is fine, 2:5 is not an N:M the library knows
+        nm.spmm_nm_general(z(8, 26), m, 65, 2, 5, z(8, 65))
+    with pytest.raises(nm.NmError):            # K % M != 0: NM_ERR_SHAPE
+        nm.spmm_nm_general(z(8, 15), m, 60, 2, 8, z(8, 60))
+    with pytest.raises(ValueError):            # Bt must have K columns
+        nm.spmm_nm_general(z(8, 16), m, 64, 2, 8, z(8, 60))
+
+
 TRANSPOSE_CASES = [(64, 64, 0), (2048, 520, 0), (300, 136, 8), (17, 40, 0), (13, 7, 3), (1, 96, 0), (520, 1, 0)]
 
 
