@@ -28,20 +28,21 @@ template <typename T>
 __global__ __launch_bounds__(256) void nm_to24_kernel(const T* __restrict__ values, const uint8_t* __restrict__ meta,
                                                       int64_t R, int64_t K, int N, int M, T* __restrict__ v24,
                                                       uint8_t* __restrict__ m24) {
-  const int64_t tpr = (K + 7) / 8;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= R * tpr) return;
-  const int64_t row = idx / tpr, t = idx % tpr;
+  // 32-bit index arithmetic (the launch guarantees R * ceil(K/8) < 2^32); M is a power of two
+  const uint32_t tpr = (uint32_t)((K + 7) / 8);
+  const uint32_t idx = blockIdx.x * 256u + threadIdx.x;
+  if (idx >= (uint32_t)R * tpr) return;
+  const uint32_t row = idx / tpr, t = idx - row * tpr;
   const int b = ceil_log2(M);
-  const int64_t G = K / M;
+  const int64_t G = K >> b;
   const int64_t vrow = G * N, mrow = (G * N * b + 7) / 8;
   const uint8_t* mr = meta + row * mrow;
   uint32_t byte = 0;
   for (int h = 0; h < 2; ++h) {
-    const int64_t q = 2 * t + h;
+    const int64_t q = 2 * (int64_t)t + h;
     if (4 * q >= K) break;
-    const int64_t g = (4 * q) / M;
-    const int o = (int)(4 * q - g * M);
+    const int64_t g = (4 * q) >> b;
+    const int o = (int)(4 * q - (g << b));
     uint32_t p[2] = {0u, 1u};
     T v[2] = {T(0), T(0)};
     int cnt = 0;
@@ -64,11 +65,11 @@ __global__ __launch_bounds__(256) void nm_to24_kernel(const T* __restrict__ valu
         v[0] = T(0);
       }
     }
-    v24[row * (K / 2) + 2 * q] = v[0];
-    v24[row * (K / 2) + 2 * q + 1] = v[1];
+    v24[(int64_t)row * (K / 2) + 2 * q] = v[0];
+    v24[(int64_t)row * (K / 2) + 2 * q + 1] = v[1];
     byte |= (p[0] | (p[1] << 2)) << (4 * h);
   }
-  m24[row * tpr + t] = (uint8_t)byte;
+  m24[(int64_t)row * tpr + t] = (uint8_t)byte;
 }
 
 // Plain SIMT product for any N:M (64 x 64 tiles, 32-k chunks staged densely in LDS): the kept
@@ -146,7 +147,8 @@ hipError_t launch_spmm_nm_general(int dt, const void* values, const uint8_t* met
   if (N == 2 && M == 4) return launch_spmm_nm_t(dt, values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
   const int esz = dt == DT_BF16 ? 2 : 4;
   const int64_t need = general_work_bytes(esz, R, K, N, M);
-  if (need > 0 && work && work_bytes >= need && (uintptr_t)work % 16 == 0 && !force_generic()) {
+  if (need > 0 && work && work_bytes >= need && (uintptr_t)work % 16 == 0 && R * ((K + 7) / 8) < (int64_t(1) << 32) &&
+      !force_generic()) {
     unsigned char* w = (unsigned char*)work;
     uint8_t* m24 = w + (R * (K / 2) * esz + 15) / 16 * 16;
     const unsigned blocks = (unsigned)((R * ((K + 7) / 8) + 255) / 256);
