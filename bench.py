@@ -173,6 +173,40 @@ def _w_general(w):
     return steps, flops, algo, "spmm_nm_general"
 
 
+def _w_block(w):
+    import torch
+    import sparse_matmul_ffns_amd as nm
+    from sparse_matmul_ffns_amd import synth
+    dm, dff, T, V, M = w["d_model"], w["d_ff"], w["tokens"], w["V"], w["M"]
+    W = _dev(synth.normal((dff, dm), w["W"]["seed"], w["W"]["mean"], w["W"]["std"]))
+    Xt = _dev(synth.normal((T, dm), w["X"]["seed"], w["X"]["mean"], w["X"]["std"]))
+    Wd = _dev(synth.normal((dff, dm), w["W_down"]["seed"], w["W_down"]["mean"], w["W_down"]["std"]))
+    mask = torch.empty((dff, dm), dtype=torch.uint8, device="cuda")
+    vals = torch.empty((dff, dm // 2), dtype=W.dtype, device="cuda")
+    meta = torch.empty((dff, dm // 8), dtype=torch.uint8, device="cuda")
+    hT = torch.empty((dff, T), dtype=W.dtype, device="cuda")
+    h = torch.empty((T, dff), dtype=W.dtype, device="cuda")
+    nv, mb, cb = nm.sizes(T, dff, 2, M, V)
+    hv = torch.empty((T, nv // T), dtype=W.dtype, device="cuda")
+    hm = torch.empty((T, mb // T), dtype=torch.uint8, device="cuda")
+    hc = torch.empty((T // V, dff // M, 4), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((T, dm), dtype=torch.float32, device="cuda")
+    # the FFN block forward from its parts: the weight's 2:4 prune + compress, the up-projection
+    # (bf16 output, [d_ff x tokens]), the activations made token-major, ReLU + V:N:M prune, and the
+    # V:N:M down-projection
+    steps = [
+        ("nm_prune_compress", lambda: nm.nm_prune_compress(W, 2, 4, mask=mask, values=vals, meta=meta)),
+        ("spmm_nm_t_up", lambda: nm.spmm_nm_t(vals, meta, dm, Xt, out=hT)),
+        ("nm_transpose_h", lambda: nm.transpose(hT, out=h)),
+        ("prune_act_venom", lambda: nm.prune_act_venom(h, V, M, apply_relu=True, values=hv, meta=hm, colsel=hc)),
+        ("spmm_venom_down", lambda: nm.spmm_venom(hv, hm, hc, dff, V, M, Wd, out=Y)),
+    ]
+    g = 2.0 * dff * dm * T
+    flops = {"spmm_nm_t_up": g, "spmm_venom_down": g}
+    algo = {"spmm_nm_t_up": ("mfma", g / 2), "spmm_venom_down": ("mfma", g / 4)}
+    return steps, flops, algo, "spmm_venom_down"
+
+
 def _w_venom(w, relu):
     import torch
     import sparse_matmul_ffns_amd as nm
@@ -241,6 +275,8 @@ def build_workload(name):
         return _w_lowrank(w)
     if w["kind"] == "spmm_nm_general":
         return _w_general(w)
+    if w["kind"] == "ffn_block":
+        return _w_block(w)
     if w["kind"] == "spmm_venom":
         return _w_venom(w, relu=False)
     if w["kind"] == "act_venom":
@@ -284,6 +320,20 @@ def cpu_baseline(name):
         fl = 2.0 * R * K * Nc
         sample = (f"whole workload, one step: {N}:{M} prune + compress of the [{R}x{K}] weight, fp64 "
                   f"decompress-and-dgemm with the [{K}x{Nc}] operand")
+    elif w["kind"] == "ffn_block":
+        dm, dff, T, V, M = w["d_model"], w["d_ff"], w["tokens"], w["V"], w["M"]
+        W = synth.normal((dff, dm), w["W"]["seed"], w["W"]["mean"], w["W"]["std"])
+        Xt = synth.normal((V, dm), w["X"]["seed"], w["X"]["mean"], w["X"]["std"])   # the first V tokens
+        Wd = synth.normal((dff, dm), w["W_down"]["seed"], w["W_down"]["mean"], w["W_down"]["std"])
+        t0 = time.perf_counter()
+        v, m, _ = O.compress_nm(W, O.prune_nm(W, "bf16", 2, 4), 2, 4)
+        hT = O.spmm_nm(v, m, dff, dm, np.ascontiguousarray(Xt.T), "bf16")         # [d_ff x V] in fp64
+        hv, hm, hc, _, _ = O.prune_venom(O.encode_bf16(hT.T), "bf16", V, M, True)
+        O.spmm_venom(hv, hm, hc, V, dff, V, M, Wd, "bf16")
+        dt = time.perf_counter() - t0
+        fl = 2 * 2.0 * dff * dm * V
+        sample = (f"{V} of {T} tokens (one V-block): the weight's 2:4 prune + compress, the fp64 up-projection, "
+                  f"bf16 rounding, ReLU + V:N:M prune and the fp64 down-projection")
     elif w["kind"] == "spmm_nm_lowrank":
         R, K, Nc, r = w["R"], w["K"], w["Nc"], w["rank"]
         A = synth.normal((R, K), w["A"]["seed"], w["A"]["mean"], w["A"]["std"])

@@ -97,6 +97,10 @@ WORKLOADS = {
         kind="spmm_nm_lowrank", dtype="bf16", R=8192, K=2048, Nc=4096, rank=64,
         A=dict(seed=2000, mean=0.0, std=0.02), B=dict(seed=2001, mean=0.0, std=1.0),
         U=dict(seed=2002, mean=0.0, std=0.02), Vt=dict(seed=2003, mean=0.0, std=0.02)),
+    "ffn_block_fwd_nm24_vnm128_dmodel4096_dff16384_tok8192": dict(
+        kind="ffn_block", dtype="bf16", d_model=4096, d_ff=16384, tokens=8192, V=128, M=8,
+        W=dict(seed=7000, mean=0.0, std=0.02), X=dict(seed=7001, mean=0.0, std=1.0),
+        W_down=dict(seed=7002, mean=0.0, std=0.02)),
     "relu_act_vnm128_2_8_8192x16384x4096": dict(
         kind="act_venom", dtype="bf16", R=8192, K=16384, Nc=4096, V=128, M=8,
         Z=dict(seed=5000, mean=-0.5, std=1.0), W=dict(seed=5001, mean=0.0, std=0.02)),

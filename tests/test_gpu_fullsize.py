@@ -221,6 +221,46 @@ def test_relu_act_vnm128_full():
 
 
 # ---------------------------------------------------------------------------
+# the FFN block forward: 2:4 up-projection (bf16 output) -> token-major h -> ReLU + V:N:M (V=128,
+# M=8) -> V:N:M down-projection; d_model 4096, d_ff 16384, 8192 tokens
+# ---------------------------------------------------------------------------
+
+def test_ffn_block_fwd_full():
+    """Small-integer inputs, so that every up-projection sum is an exact fp32 integer and its bf16
+    rounding is the oracle's: the V:N:M selection of the activations is then compared bit for bit
+    on sampled V-blocks, and the down-projection on sampled tokens within tolerance."""
+    w = synth.WORKLOADS["ffn_block_fwd_nm24_vnm128_dmodel4096_dff16384_tok8192"]
+    dm, dff, T, V, M = w["d_model"], w["d_ff"], w["tokens"], w["V"], w["M"]
+    W = synth.small_ints((dff, dm), 71, dtype="bf16")
+    Xt = synth.small_ints((T, dm), 72, dtype="bf16")
+    Wd = synth.small_ints((dff, dm), 73, dtype="bf16")
+    _, vals, meta = nm.nm_prune_compress(dev(W, "bf16"))
+    hT = nm.spmm_nm_t(vals, meta, dm, dev(Xt, "bf16"), out_dtype=torch.bfloat16)
+    h = nm.transpose(hT)
+    del hT
+    hv, hm, hc = nm.prune_act_venom(h, V, M, apply_relu=True)
+    del h
+    Y = nm.spmm_venom(hv, hm, hc, dff, V, M, dev(Wd, "bf16"))
+    _finite(Y, "ffn block")
+    gv, gm, gc = host(hv), host(hm), host(hc)
+    wv, wm, _ = O.compress_nm(W, O.prune_nm(W, "bf16", 2, 4), 2, 4)
+    assert host(vals).tobytes() == wv.tobytes() and np.array_equal(host(meta), wm)
+    Ws64 = O.decode(O.decompress_nm(wv, wm, dff, dm, 2, 4), "bf16")
+    Wd64 = O.decode(Wd, "bf16")
+    rng = np.random.default_rng(74)
+    for b in sorted({0, T // V - 1} | set(rng.choice(T // V, 1, replace=False).tolist())):
+        ts = slice(b * V, (b + 1) * V)
+        Z = O.decode(Xt[ts], "bf16") @ Ws64.T                      # exact integers, [V, d_ff]
+        ov, om, oc, _, _ = O.prune_venom(O.encode_bf16(Z), "bf16", V, M, True)
+        assert np.array_equal(gc[b:b + 1], oc), f"colsel of block {b}"
+        assert gv[ts].tobytes() == ov.tobytes(), f"values of block {b}"
+        assert np.array_equal(gm[ts], om), f"metadata of block {b}"
+        H64 = O.decode(O.decompress_venom(ov, om, oc, V, dff, V, M), "bf16")
+        rows = np.array(sorted({0, V - 1} | set(rng.choice(V, 4, replace=False).tolist())))
+        _check_rows(Y, H64[rows], Wd64, b * V + rows, f"ffn block {b} down-projection")
+
+
+# ---------------------------------------------------------------------------
 # 2:4 double-pruned training step: d_model 4096, d_ff 16384, 8192 tokens
 #   Y = W_s X, W_ds^T = re-prune(W_s^T), dX = W_ds^T dY, dW = (dY X^T) at W_s's pattern
 # ---------------------------------------------------------------------------
