@@ -194,6 +194,19 @@ def _w_block(w):
     # the FFN block forward from its parts: the weight's 2:4 prune + compress, the up-projection
     # (bf16 output, [d_ff x tokens]), the activations made token-major, ReLU + V:N:M prune, and the
     # V:N:M down-projection
+    if w["kind"] == "ffn_block_fused":
+        # the up-projection prunes its activations in its epilogue: h is never stored
+        del hT, h
+        steps = [
+            ("nm_prune_compress", lambda: nm.nm_prune_compress(W, 2, 4, mask=mask, values=vals, meta=meta)),
+            ("spmm_nm_t_relu_venom", lambda: nm.spmm_nm_t_relu_venom(vals, meta, dm, Xt, V, M, h_values=hv,
+                                                                     h_meta=hm, h_colsel=hc)),
+            ("spmm_venom_down", lambda: nm.spmm_venom(hv, hm, hc, dff, V, M, Wd, out=Y)),
+        ]
+        g = 2.0 * dff * dm * T
+        flops = {"spmm_nm_t_relu_venom": g, "spmm_venom_down": g}
+        algo = {"spmm_nm_t_relu_venom": ("mfma", g / 2), "spmm_venom_down": ("mfma", g / 4)}
+        return steps, flops, algo, "spmm_venom_down"
     steps = [
         ("nm_prune_compress", lambda: nm.nm_prune_compress(W, 2, 4, mask=mask, values=vals, meta=meta)),
         ("spmm_nm_t_up", lambda: nm.spmm_nm_t(vals, meta, dm, Xt, out=hT)),
@@ -275,7 +288,7 @@ def build_workload(name):
         return _w_lowrank(w)
     if w["kind"] == "spmm_nm_general":
         return _w_general(w)
-    if w["kind"] == "ffn_block":
+    if w["kind"] in ("ffn_block", "ffn_block_fused"):
         return _w_block(w)
     if w["kind"] == "spmm_venom":
         return _w_venom(w, relu=False)
@@ -320,7 +333,7 @@ def cpu_baseline(name):
         fl = 2.0 * R * K * Nc
         sample = (f"whole workload, one step: {N}:{M} prune + compress of the [{R}x{K}] weight, fp64 "
                   f"decompress-and-dgemm with the [{K}x{Nc}] operand")
-    elif w["kind"] == "ffn_block":
+    elif w["kind"] in ("ffn_block", "ffn_block_fused"):
         dm, dff, T, V, M = w["d_model"], w["d_ff"], w["tokens"], w["V"], w["M"]
         W = synth.normal((dff, dm), w["W"]["seed"], w["W"]["mean"], w["W"]["std"])
         Xt = synth.normal((V, dm), w["X"]["seed"], w["X"]["mean"], w["X"]["std"])   # the first V tokens
@@ -375,6 +388,7 @@ _KERNEL_SOURCES = {
     "spmm_nm_t": ["spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
     "spmm_nm_t_lowrank": ["lowrank.hip", "spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
     "spmm_nm_general": ["general.hip", "spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
+    "spmm_venom_down": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp"],
     "spmm_venom": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp"],
     "sddmm_nm": ["sddmm.hip", "common.hpp", "dma.hpp"],
     "sddmm_nm_dt": ["sddmm.hip", "common.hpp", "dma.hpp"],

@@ -213,6 +213,31 @@ nm_status spmm_nm_t_lowrank(nm_dtype dt, const void* values, const uint8_t* meta
                             float* C, int64_t ldc, nm_stream stream);
 
 /*
+ * spmm_nm_t_relu_venom -- an FFN up-projection whose activations leave the
+ * kernel already pruned ("To 2:4 Sparsity and Beyond", abstract: 2:4 weights
+ * and v:n:m activations in the FFN; "Sparser, Faster, Lighter Transformer
+ * Language Models", Methodologie: ReLU).  With C = decompress(values, meta) Bt^T
+ * as in spmm_nm_t ([R][Nc]: R the FFN width, Nc the tokens), the activations
+ * h = ReLU(bf16(C))^T [Nc][R] (each fp32 sum rounded to nearest even, then
+ * every value <= 0 made +0.0) are pruned to V:N:M along R with V-blocks of
+ * tokens, exactly as prune_act_venom(h, V, M, apply_relu) would, and only the
+ * compressed form is written: h is never stored.
+ *   values, meta, Bt as for spmm_nm_t, bf16 only
+ *   h_values [Nc][(R/M)*2] bf16, h_meta [Nc][ceil((R/M)/2)], h_colsel
+ *            [Nc/V][R/M][4]: the outputs of prune_act_venom for h
+ * V = 128 and M = 8 only (NM_ERR_UNSUPPORTED otherwise, and for dtypes other
+ * than bf16); R % 256 == 0, Nc % 256 == 0, K % 256 == 0, ldbt % 8 == 0,
+ * values, meta and Bt 16-byte aligned, h_values 16-byte and h_meta, h_colsel
+ * 4-byte aligned (NM_ERR_UNSUPPORTED otherwise: compose spmm_nm_t_out_bf16,
+ * nm_transpose and prune_act_venom instead).  NM_ERR_SHAPE for non-positive
+ * sizes, K % 4 != 0, ldbt < K, R % M != 0 or Nc % V != 0.
+ */
+nm_status spmm_nm_t_relu_venom(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R,
+                               int64_t K, const void* Bt, int64_t ldbt, int64_t Nc, int V, int M,
+                               void* h_values, uint8_t* h_meta, uint8_t* h_colsel,
+                               nm_stream stream);
+
+/*
  * spmm_nm_general -- spmm_nm_t for any N:M form nm_compress writes ("Success
  * story: ESPLAG", Solution: N:M patterns beyond 2:4):
  * C[r][n] = sum_k decompress(values, meta, N, M)[r][k] * Bt[n][k]

@@ -23,6 +23,7 @@ from .nmsparse import (  # noqa: F401
     general_work_bytes,
     spmm_nm_t,
     spmm_nm_t_lowrank,
+    spmm_nm_t_relu_venom,
     spmm_venom,
     transpose,
 )

@@ -141,6 +141,19 @@ int64_t nm_general_work_bytes(nm_dtype dt, int64_t R, int64_t K, int N, int M) {
   return nms::general_work_bytes(esize(dt), R, K, N, M);
 }
 
+nm_status spmm_nm_t_relu_venom(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                               const void* Bt, int64_t ldbt, int64_t Nc, int V, int M, void* h_values,
+                               uint8_t* h_meta, uint8_t* h_colsel, nm_stream stream) {
+  if (!values || !meta || !Bt || !h_values || !h_meta || !h_colsel) return NM_ERR_NULL;
+  if (dt != NM_BF16 || V != 128 || M != 8) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || Nc <= 0 || K % 4 != 0 || ldbt < K || R % M != 0 || Nc % V != 0) return NM_ERR_SHAPE;
+  if (!aligned(values, 2) || !aligned(Bt, 2) || !aligned(h_values, 2)) return NM_ERR_ALIGN;
+  const hipError_t e = nms::launch_spmm_nm_t_relu_venom(values, meta, R, K, Bt, ldbt, Nc, V, M, h_values, h_meta,
+                                                        h_colsel, hs(stream));
+  if (e == hipErrorNotSupported) return NM_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
 nm_status nm_transpose(nm_dtype dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst, int64_t ldd,
                        nm_stream stream) {
   if (!src || !dst) return NM_ERR_NULL;

@@ -46,6 +46,18 @@ __device__ inline int rank_of(const uint32_t (&k)[M], int p) {
   return r;
 }
 
+// The same rank over fp64 keys (the V:N:M column norms).
+template <int M>
+__device__ inline int rank_f64(const double (&k)[M], int p) {
+  int r = 0;
+#pragma unroll
+  for (int q = 0; q < M; ++q) {
+    r += (k[q] > k[p]) ? 1 : 0;
+    r += (q < p && k[q] == k[p]) ? 1 : 0;
+  }
+  return r;
+}
+
 // 2:4 selection on four keys: returns the nibble p0 | p1 << 2 (p0 < p1) of the two positions
 // with rank < 2 under rank_of.  Each key is extended by its position, (k << 2) | (3 - p), so
 // that the extended keys are distinct and order exactly like rank_of (larger key first, then

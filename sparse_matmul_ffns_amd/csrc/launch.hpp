@@ -61,6 +61,9 @@ hipError_t launch_spmm_nm_t_lowrank(int dt, const void* values, const uint8_t* m
                                     const void* Bt, int64_t ldbt, int64_t Nc, const void* U, int64_t ldu,
                                     const void* Vt, int64_t ldvt, int64_t rank, float* Tt, float* C, int64_t ldc,
                                     hipStream_t s);
+hipError_t launch_spmm_nm_t_relu_venom(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
+                                      int64_t ldbt, int64_t Nc, int V, int M, void* hv, uint8_t* hm, uint8_t* hc,
+                                      hipStream_t s);
 int64_t general_work_bytes(int esz, int64_t R, int64_t K, int N, int M);
 hipError_t launch_spmm_nm_general(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, int N, int M,
                                   const void* Bt, int64_t ldbt, int64_t Nc, float* C, int64_t ldc, void* work,

@@ -22,17 +22,6 @@
 
 namespace nms {
 
-template <int M>
-__device__ inline int rank_f64(const double (&k)[M], int p) {
-  int r = 0;
-#pragma unroll
-  for (int q = 0; q < M; ++q) {
-    r += (k[q] > k[p]) ? 1 : 0;
-    r += (q < p && k[q] == k[p]) ? 1 : 0;
-  }
-  return r;
-}
-
 // Chunks of 16 bytes per thread and tile on the streaming path (a 64 KB tile, 256 threads).
 constexpr int kStreamChunks = 16;
 

@@ -39,6 +39,7 @@ _SIGNATURES = {
     "spmm_nm_t_out_bf16": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t_lowrank": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
                           _vp],
+    "spmm_nm_t_relu_venom": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp],
     "spmm_nm_general": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp],
     "nm_transpose": [_int, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "prune_act_venom": [_int, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _i64, _vp],
@@ -289,6 +290,35 @@ def spmm_nm_t_lowrank(values: torch.Tensor, meta: torch.Tensor, K: int, Bt: torc
                                    _rows(U, "U"), _p(Vt), _rows(Vt, "Vt"), rank, _p(Tt), _p(out), _rows(out, "out"),
                                    _stream()), "spmm_nm_t_lowrank")
     return out, Tt
+
+
+def spmm_nm_t_relu_venom(values: torch.Tensor, meta: torch.Tensor, K: int, Bt: torch.Tensor, V: int = 128, M: int = 8,
+                         h_values=None, h_meta=None, h_colsel=None):
+    """The up-projection C = decompress(values, meta) @ Bt.T ([R, Nc]) with its activations
+    h = ReLU(bf16(C)).T ([Nc, R]) pruned to V:N:M on the way out: returns (h_values, h_meta,
+    h_colsel), as prune_act_venom(h, V, M, apply_relu=True) would."""
+    _dev(values, meta, Bt, h_values, h_meta, h_colsel)
+    _flat(values, "values"), _flat(meta, "meta")
+    if Bt.dtype != values.dtype:
+        raise TypeError("values and Bt must share a dtype")
+    R = values.shape[0]
+    Nc = Bt.shape[0]
+    if Bt.shape[1] != K:
+        raise ValueError("Bt must have K columns")
+    nv, mb, cb = sizes(Nc, R, 2, M, V)
+    if h_values is None:
+        h_values = torch.empty((Nc, nv // Nc), dtype=Bt.dtype, device=Bt.device)
+    if h_meta is None:
+        h_meta = torch.empty((Nc, mb // Nc), dtype=torch.uint8, device=Bt.device)
+    if h_colsel is None:
+        h_colsel = torch.empty((Nc // V, R // M, 4), dtype=torch.uint8, device=Bt.device)
+    for t, n, name in ((h_values, nv, "h_values"), (h_meta, mb, "h_meta"), (h_colsel, cb, "h_colsel")):
+        _flat(t, name)
+        if t.numel() < n:
+            raise ValueError(f"{name} is too small")
+    _check(lib().spmm_nm_t_relu_venom(_dt(Bt), _p(values), _p(meta), R, K, _p(Bt), _rows(Bt, "Bt"), Nc, V, M,
+                                      _p(h_values), _p(h_meta), _p(h_colsel), _stream()), "spmm_nm_t_relu_venom")
+    return h_values, h_meta, h_colsel
 
 
 def general_work_bytes(dtype: torch.dtype, R: int, K: int, N: int, M: int) -> int:

@@ -101,6 +101,10 @@ WORKLOADS = {
         kind="ffn_block", dtype="bf16", d_model=4096, d_ff=16384, tokens=8192, V=128, M=8,
         W=dict(seed=7000, mean=0.0, std=0.02), X=dict(seed=7001, mean=0.0, std=1.0),
         W_down=dict(seed=7002, mean=0.0, std=0.02)),
+    "ffn_block_fwd_fused_nm24_vnm128_dmodel4096_dff16384_tok8192": dict(
+        kind="ffn_block_fused", dtype="bf16", d_model=4096, d_ff=16384, tokens=8192, V=128, M=8,
+        W=dict(seed=7000, mean=0.0, std=0.02), X=dict(seed=7001, mean=0.0, std=1.0),
+        W_down=dict(seed=7002, mean=0.0, std=0.02)),
     "relu_act_vnm128_2_8_8192x16384x4096": dict(
         kind="act_venom", dtype="bf16", R=8192, K=16384, Nc=4096, V=128, M=8,
         Z=dict(seed=5000, mean=-0.5, std=1.0), W=dict(seed=5001, mean=0.0, std=0.02)),

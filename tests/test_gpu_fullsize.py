@@ -242,6 +242,10 @@ def test_ffn_block_fwd_full():
     del h
     Y = nm.spmm_venom(hv, hm, hc, dff, V, M, dev(Wd, "bf16"))
     _finite(Y, "ffn block")
+    # the fused up-projection (ReLU + V:N:M in its epilogue) gives the same compressed activations
+    fv, fm, fc = nm.spmm_nm_t_relu_venom(vals, meta, dm, dev(Xt, "bf16"), V, M)
+    assert torch.equal(fc, hc) and torch.equal(fv.view(torch.int16), hv.view(torch.int16)) and torch.equal(fm, hm)
+    del fv, fm, fc
     gv, gm, gc = host(hv), host(hm), host(hc)
     wv, wm, _ = O.compress_nm(W, O.prune_nm(W, "bf16", 2, 4), 2, 4)
     assert host(vals).tobytes() == wv.tobytes() and np.array_equal(host(meta), wm)
