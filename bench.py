@@ -434,8 +434,8 @@ COLD_FLUSH_BYTES = 512 << 20
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU "
-              "component in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no multi-GPU "
+              "component", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

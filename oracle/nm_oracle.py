@@ -23,7 +23,7 @@ Sources (page title, section):
   [SFL]     "Sparser, Faster, Lighter Transformer Language Models",
             Methodologie, training strategy (ReLU instead of SiLU).
 
-Readings taken where the pages are silent (all of them listed in the design doc):
+Readings taken where the pages are silent:
   * groups are M consecutive elements along the reduction dimension K of the
     left (sparse) operand, starting at k = 0; partial groups are not allowed;
   * the magnitude key is |stored value| in the input dtype; ties go to the

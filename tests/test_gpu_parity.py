@@ -212,7 +212,7 @@ def test_spmm_nm_config1_fp32():
     assert host(gv).tobytes() == vals.tobytes() and np.array_equal(host(gm), meta)
     C = host(nm.spmm_nm(dev(vals, "f32"), dev(meta, "u8"), 512, dev(B, "f32")))
     A64 = O.decode(O.decompress_nm(vals, meta, 256, 512, 2, 4), "f32")
-    check_close(C, O.spmm_nm(vals, meta, 256, 512, B, "f32"), O.abs_bound(A64, B.astype(np.float64)), "cfg1")
+    check_close(C, O.spmm_nm(vals, meta, 256, 512, B, "f32"), O.abs_bound(A64, B.astype(np.float64)), "fp32 256x512x128")
 
 
 def test_spmm_nm_deterministic():
