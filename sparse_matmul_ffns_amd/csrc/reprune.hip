@@ -238,9 +238,11 @@ static hipError_t reprune_dispatch(const void* values, const uint8_t* meta, int6
   const int esz = sizeof(T);
   if (esz == 2 && R % RB_TILE == 0 && K % RB_TILE == 0 && (uintptr_t)values % 16 == 0 && (uintptr_t)meta % 2 == 0 &&
       (uintptr_t)values_t % 16 == 0 && (uintptr_t)meta_t % 2 == 0 && !force_generic()) {
-    // four 32 KB workgroups per CU
+    // one workgroup per tile (measured: 35.6 us against 37.6 with 1024 workgroups walking four
+    // tiles each at 16384 x 4096, 31.9 against 36.2 at 4096 x 16384); the walk only serves grids
+    // past 2^30 tiles
     const int64_t ntiles = (R / RB_TILE) * (K / RB_TILE);
-    const unsigned grid = (unsigned)(ntiles < 1024 ? ntiles : 1024);   // ntiles < 2^32: R, K < 2^31
+    const unsigned grid = (unsigned)(ntiles < (int64_t(1) << 30) ? ntiles : (int64_t(1) << 30));
     hipLaunchKernelGGL(reprune_t_bf16_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t*)values, meta, R, K,
                        (uint16_t*)values_t, meta_t);
     return hipGetLastError();
