@@ -13,7 +13,8 @@
  *       Accelerate LLM Pre-Training" -- abstract: 2:4 weights and v:n:m
  *       (Venom) activations in every FFN matmul.
  *   NSF PAR award 2340011 listing -- SLOPE abstract: the backward pass uses
- *       the transposed weight re-pruned with N:M ("double pruned").
+ *       the transposed weight re-pruned with N:M ("double pruned"); lazy
+ *       low-rank adapters join the sparse weight late in pre-training.
  *   "Sparser, Faster, Lighter Transformer Language Models" -- Methodologie:
  *       ReLU activations, the FFN as the dominant cost.
  *
@@ -47,7 +48,8 @@
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Every call
  *     is asynchronous on that stream; argument errors are returned before
  *     anything is launched.
- *   - Floating point: products accumulate in fp32 and are written as fp32.
+ *   - Floating point: products accumulate in fp32 and are written as fp32,
+ *     except where a call states a bf16 result (rounded to nearest even).
  *   - Errors: NM_ERR_NULL for a NULL required pointer, NM_ERR_SHAPE for
  *     non-positive sizes, sizes that are not multiples of the group/block, or
  *     a leading dimension below the row width, NM_ERR_UNSUPPORTED for a dtype
