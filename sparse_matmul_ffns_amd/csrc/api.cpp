@@ -145,7 +145,7 @@ nm_status spmm_nm_t_relu_venom(nm_dtype dt, const void* values, const uint8_t* m
                                const void* Bt, int64_t ldbt, int64_t Nc, int V, int M, void* h_values,
                                uint8_t* h_meta, uint8_t* h_colsel, nm_stream stream) {
   if (!values || !meta || !Bt || !h_values || !h_meta || !h_colsel) return NM_ERR_NULL;
-  if (dt != NM_BF16 || V != 128 || M != 8) return NM_ERR_UNSUPPORTED;
+  if (dt != NM_BF16 || (V != 64 && V != 128 && V != 256) || (M != 4 && M != 8 && M != 16)) return NM_ERR_UNSUPPORTED;
   if (R <= 0 || K <= 0 || Nc <= 0 || K % 4 != 0 || ldbt < K || R % M != 0 || Nc % V != 0) return NM_ERR_SHAPE;
   if (!aligned(values, 2) || !aligned(Bt, 2) || !aligned(h_values, 2)) return NM_ERR_ALIGN;
   const hipError_t e = nms::launch_spmm_nm_t_relu_venom(values, meta, R, K, Bt, ldbt, Nc, V, M, h_values, h_meta,

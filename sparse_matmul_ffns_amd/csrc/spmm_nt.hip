@@ -29,6 +29,8 @@
 // the operand reads of 16 (32) consecutive rows are free of bank conflicts.
 // 8 waves (two per SIMD) own 128 x 64 of the 256 x 256 tile each, 4 x 2
 // fragments with accumulators in VGPRs.
+#include <type_traits>
+
 #include "common.hpp"
 #include "dma.hpp"
 #include "launch.hpp"
@@ -61,15 +63,16 @@ struct NtCfg {
 // OutT: float (fp32 C) or uint16_t (bf16 C, each fp32 sum rounded to nearest even).
 // LR: add a low-rank adapter term U Tt^T to the accumulators before they are stored (U [R][ldu]
 // bf16, Tt [Nc][rank] fp32, rank a multiple of 16; unused otherwise).
-// VNM: instead of storing C, prune h = ReLU(bf16(C))^T (columns of C are tokens) to V:N:M with
-// V = 128 tokens and M = 8 rows of C, writing h's values, nibbles and column choices (hv, hm, hc in
-// the layout of prune_act_venom; R and Nc multiples of 256).
-template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT, bool LR, bool VNM = false>
+// VNM (= M, 0 for off): instead of storing C, prune h = ReLU(bf16(C))^T (columns of C are
+// tokens) to V:N:M with V = vnm_v tokens (64, 128 or 256) and M rows of C (4, 8 or 16), writing
+// h's values, nibbles and column choices (hv, hm, hc in the layout of prune_act_venom; R and Nc
+// multiples of 256).
+template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT, bool LR, int VNM = 0>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
     const uint16_t* __restrict__ values, const uint8_t* __restrict__ meta, int64_t R, int64_t Kd,
     const uint16_t* __restrict__ Bt, int64_t ldbt, int64_t Nc, OutT* __restrict__ C, int64_t ldc,
     const uint16_t* __restrict__ U, int64_t ldu, const float* __restrict__ Tt, int rank,
-    uint16_t* __restrict__ hv, uint8_t* __restrict__ hm, uint8_t* __restrict__ hc) {
+    uint16_t* __restrict__ hv, uint8_t* __restrict__ hm, uint8_t* __restrict__ hc, int vnm_v) {
   using Cfg = NtCfg<BM, BN, WAVES_M, WAVES_N>;
   constexpr int FM = Cfg::FM, FN = Cfg::FN;
   extern __shared__ __align__(1024) unsigned char smem[];
@@ -314,15 +317,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
     wait_vmcnt<0>();
   }
 
-  if constexpr (VNM) {
+  if constexpr (VNM > 0) {
     static_assert(BM == 256 && BN == 256 && !LR, "the V:N:M epilogue takes whole 256 x 256 tiles");
+    static_assert(VNM == 4 || VNM == 8 || VNM == 16, "M");
+    constexpr int M = VNM, NG = 256 / M;   // groups of the tile's 256 rows
+    const int V = vnm_v, NB = 256 / V;     // V-blocks of the tile's 256 tokens
     // 1. h = ReLU(bf16(acc)) into LDS, token-major: ht[n][r] for the tile's 256 tokens n and 256
     //    rows r of C, 260 elements per token (each lane's 8-byte writes of 32 tokens then fall on
     //    distinct banks)
     constexpr int HP = 260;
     uint16_t* ht = reinterpret_cast<uint16_t*>(smem);
-    double* l1 = reinterpret_cast<double*>(smem + 256 * HP * 2);
-    uint32_t* cs = reinterpret_cast<uint32_t*>(l1 + 512);
+    double* l1 = reinterpret_cast<double*>(smem + 256 * HP * 2);   // [NB][256]
+    uint32_t* cs = reinterpret_cast<uint32_t*>(l1 + 1024);          // [NB][NG]
     lds_barrier();   // every wave is done with the last step's operands
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -342,54 +348,55 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
         }
       }
     __syncthreads();
-    // 2. column norms: thread t adds h over the 128 tokens of V-block t / 256 for row t % 256, in
-    //    fp64 and token order (the sequence of additions of any sequential implementation)
-    {
-      const int vb = tid >> 8, r = tid & 255;
+    // 2. column norms: one lane per (V-block, row) adds h over the block's V tokens, in fp64 and
+    //    token order (the sequence of additions of any sequential implementation)
+    for (int u = tid; u < NB * 256; u += Cfg::NT) {
+      const int vb = u >> 8, r = u & 255;
       double acc1 = 0.0;
-      for (int n = 0; n < 128; ++n) acc1 += (double)Elem<uint16_t>::to_f32(ht[(vb * 128 + n) * HP + r]);
-      l1[tid] = acc1;
+      for (int n = 0; n < V; ++n) acc1 += (double)Elem<uint16_t>::to_f32(ht[(vb * V + n) * HP + r]);
+      l1[u] = acc1;
     }
     __syncthreads();
-    // 3. per (V-block, group of 8 rows): the 4 rows of largest norm, lower row on ties
-    const int64_t Gh = R / 8;   // groups per token of h
-    if (tid < 64) {
-      const int vb = tid >> 5, g = tid & 31;
-      double k[8];
+    // 3. per (V-block, group of M rows): the 4 rows of largest norm, lower row on ties
+    const int64_t Gh = R / M;   // groups per token of h
+    for (int u = tid; u < NB * NG; u += Cfg::NT) {
+      const int vb = u / NG, g = u % NG;
+      double k[M];
 #pragma unroll
-      for (int p = 0; p < 8; ++p) k[p] = l1[vb * 256 + 8 * g + p];
+      for (int p = 0; p < M; ++p) k[p] = l1[vb * 256 + M * g + p];
       uint32_t packed = 0;
       int c = 0;
 #pragma unroll
-      for (int p = 0; p < 8; ++p)
-        if (rank_f64<8>(k, p) < 4) {
+      for (int p = 0; p < M; ++p)
+        if (rank_f64<M>(k, p) < 4) {
           packed |= (uint32_t)p << (8 * c);
           ++c;
         }
-      cs[tid] = packed;
-      *reinterpret_cast<uint32_t*>(hc + ((n0 / 128 + vb) * Gh + m0 / 8 + g) * 4) = packed;
+      cs[u] = packed;
+      *reinterpret_cast<uint32_t*>(hc + ((n0 / V + vb) * Gh + m0 / M + g) * 4) = packed;
     }
     __syncthreads();
     // 4. per (token, 8 groups): 2 of the group's 4 chosen rows by magnitude (lower on ties);
-    //    32 bytes of values and 4 bytes of nibbles per token
-    for (int it = tid; it < 1024; it += Cfg::NT) {
-      const int n = it >> 2, g0 = (it & 3) * 8, vb = n >> 7;
+    //    32 bytes of values and 4 bytes of nibbles per token and octet of groups
+    constexpr int NO = NG / 8;   // octets of groups per token
+    for (int it = tid; it < 256 * NO; it += Cfg::NT) {
+      const int n = it / NO, g0 = (it % NO) * 8, vb = n / V;
       const uint16_t* trow = ht + n * HP;
       uint32_t out[8];
       uint32_t nibs = 0;
 #pragma unroll
       for (int gi = 0; gi < 8; ++gi) {
-        const uint32_t packed = cs[vb * 32 + g0 + gi];
+        const uint32_t packed = cs[vb * NG + g0 + gi];
         uint32_t x[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) x[jj] = trow[8 * (g0 + gi) + ((packed >> (8 * jj)) & 0xFF)];
+        for (int jj = 0; jj < 4; ++jj) x[jj] = trow[M * (g0 + gi) + ((packed >> (8 * jj)) & 0xFF)];
         const uint32_t nib = select24_bf16(x[0], x[1], x[2], x[3]);
         const uint32_t d01 = x[0] | (x[1] << 16), d23 = x[2] | (x[3] << 16);
         const uint32_t j0 = nib & 3, j1 = nib >> 2;
         out[gi] = __builtin_amdgcn_perm(d23, d01, (j0 * 0x202u + 0x100u) | ((j1 * 0x202u + 0x100u) << 16));
         nibs |= nib << (4 * gi);
       }
-      const int64_t tok = n0 + n, grp = m0 / 8 + g0;
+      const int64_t tok = n0 + n, grp = m0 / M + g0;
       u32x4* dv = reinterpret_cast<u32x4*>(hv + tok * (Gh * 2) + grp * 2);
       dv[0] = u32x4{out[0], out[1], out[2], out[3]};
       dv[1] = u32x4{out[4], out[5], out[6], out[7]};
@@ -417,17 +424,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT, bool LR = false, bool VNM = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT, bool LR = false, int VNM = 0>
 static hipError_t run_nt(const void* values, const uint8_t* meta, int64_t R, int64_t Kd, const void* Bt, int64_t ldbt,
                          int64_t Nc, OutT* C, int64_t ldc, hipStream_t s, const void* U = nullptr, int64_t ldu = 0,
                          const float* Tt = nullptr, int rank = 0, uint16_t* hv = nullptr, uint8_t* hm = nullptr,
-                         uint8_t* hc = nullptr) {
+                         uint8_t* hc = nullptr, int vnm_v = 0) {
   using Cfg = NtCfg<BM, BN, WAVES_M, WAVES_N>;
   auto kern = spmm_nt_kernel<BM, BN, WAVES_M, WAVES_N, OutT, LR, VNM>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   const int64_t ntiles = ((R + BM - 1) / BM) * ((Nc + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg::NT), (size_t)Cfg::LDS, s, (const uint16_t*)values, meta,
-                     R, Kd, (const uint16_t*)Bt, ldbt, Nc, C, ldc, (const uint16_t*)U, ldu, Tt, rank, hv, hm, hc);
+                     R, Kd, (const uint16_t*)Bt, ldbt, Nc, C, ldc, (const uint16_t*)U, ldu, Tt, rank, hv, hm, hc, vnm_v);
   return hipGetLastError();
 }
 
@@ -452,13 +459,20 @@ hipError_t launch_spmm_nm_nt_dma_bf16out(const void* values, const uint8_t* meta
 hipError_t launch_spmm_nm_t_relu_venom(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
                                       int64_t ldbt, int64_t Nc, int V, int M, void* hv, uint8_t* hm, uint8_t* hc,
                                       hipStream_t s) {
-  // the fused epilogue's conditions: V = 128 and M = 8 with whole 256 x 256 tiles, the pipelined
-  // SpMM's own conditions, 16-byte value rows and 4-byte metadata and column-choice words
-  if (V != 128 || M != 8 || R % 256 != 0 || Nc % 256 != 0 || !spmm_nt_ok(values, meta, Bt, ldbt, R, Nc, K) ||
-      (uintptr_t)hv % 16 != 0 || (uintptr_t)hm % 4 != 0 || (uintptr_t)hc % 4 != 0)
+  // the fused epilogue's conditions: V in {64, 128, 256} and M in {4, 8, 16} with whole 256 x 256
+  // tiles, the pipelined SpMM's own conditions, 16-byte value rows and 4-byte metadata and
+  // column-choice words
+  if ((V != 64 && V != 128 && V != 256) || (M != 4 && M != 8 && M != 16) || R % 256 != 0 || Nc % 256 != 0 ||
+      !spmm_nt_ok(values, meta, Bt, ldbt, R, Nc, K) || (uintptr_t)hv % 16 != 0 || (uintptr_t)hm % 4 != 0 ||
+      (uintptr_t)hc % 4 != 0)
     return hipErrorNotSupported;
-  return run_nt<256, 256, 2, 4, float, false, true>(values, meta, R, K, Bt, ldbt, Nc, (float*)nullptr, 0, s, nullptr, 0,
-                                                    nullptr, 0, (uint16_t*)hv, hm, hc);
+  auto go = [&](auto MM) {
+    return run_nt<256, 256, 2, 4, float, false, decltype(MM)::value>(values, meta, R, K, Bt, ldbt, Nc, (float*)nullptr,
+                                                                     0, s, nullptr, 0, nullptr, 0, (uint16_t*)hv, hm,
+                                                                     hc, V);
+  };
+  return M == 4 ? go(std::integral_constant<int, 4>{}) : M == 8 ? go(std::integral_constant<int, 8>{})
+                                                                : go(std::integral_constant<int, 16>{});
 }
 
 hipError_t launch_spmm_nm_nt_dma_lowrank(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,

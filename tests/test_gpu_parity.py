@@ -443,19 +443,20 @@ def test_spmm_nm_general_work_bytes_and_errors():
         nm.spmm_nm_general(z(8, 16), m, 64, 2, 8, z(8, 60))
 
 
-RELU_VNM_CASES = [(256, 256, 256), (512, 512, 768), (768, 1024, 512)]
+RELU_VNM_CASES = [(256, 256, 256, 128, 8), (512, 512, 768, 128, 8), (768, 1024, 512, 128, 8),
+                  (512, 256, 512, 64, 4), (256, 512, 768, 256, 16), (512, 256, 256, 64, 16), (256, 256, 512, 256, 4)]
 
 
-@pytest.mark.parametrize("R,K,Nc", RELU_VNM_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in RELU_VNM_CASES])
-def test_spmm_nm_t_relu_venom_exact(R, K, Nc):
+@pytest.mark.parametrize("R,K,Nc,V,M", RELU_VNM_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}_V{c[3]}M{c[4]}" for c in RELU_VNM_CASES])
+def test_spmm_nm_t_relu_venom_exact(R, K, Nc, V, M):
     """Small integers: every sum is an exact fp32 integer, so h = ReLU(bf16(C)) is the oracle's and
     the fused V:N:M output must equal the oracle's prune of it bit for bit."""
     raw = synth.small_ints((R, K), R + K + 41, dtype="bf16")
     vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, "bf16", 2, 4), 2, 4)
     Btraw = synth.small_ints((Nc, K), Nc + 43, dtype="bf16")
-    hv, hm, hc = nm.spmm_nm_t_relu_venom(dev(vals, "bf16"), dev(meta, "u8"), K, dev(Btraw, "bf16"))
+    hv, hm, hc = nm.spmm_nm_t_relu_venom(dev(vals, "bf16"), dev(meta, "u8"), K, dev(Btraw, "bf16"), V, M)
     C = O.spmm_nm(vals, meta, R, K, np.ascontiguousarray(Btraw.T), "bf16")
-    ov, om, oc, _, _ = O.prune_venom(O.encode_bf16(np.ascontiguousarray(C.T)), "bf16", 128, 8, True)
+    ov, om, oc, _, _ = O.prune_venom(O.encode_bf16(np.ascontiguousarray(C.T)), "bf16", V, M, True)
     assert np.array_equal(host(hc), oc)
     assert host(hv).tobytes() == ov.tobytes()
     assert np.array_equal(host(hm), om)
@@ -486,8 +487,8 @@ def test_spmm_nm_t_relu_venom_rejects():
     m = torch.zeros((264, 64), dtype=torch.uint8, device="cuda")
     with pytest.raises(nm.NmError):            # R % 256 != 0: no fused tile (NM_ERR_UNSUPPORTED)
         nm.spmm_nm_t_relu_venom(z(264, 256), m, 512, z(256, 512))
-    with pytest.raises(nm.NmError):            # V = 64 is not the fused form
-        nm.spmm_nm_t_relu_venom(z(256, 256), m[:256], 512, z(256, 512), V=64)
+    with pytest.raises(nm.NmError):            # V = 32 is not a fused form
+        nm.spmm_nm_t_relu_venom(z(256, 256), m[:256], 512, z(256, 512), V=32)
 
 
 TRANSPOSE_CASES = [(64, 64, 0), (2048, 520, 0), (300, 136, 8), (17, 40, 0), (13, 7, 3), (1, 96, 0), (520, 1, 0)]
