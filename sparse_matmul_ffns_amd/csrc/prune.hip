@@ -179,11 +179,42 @@ __global__ __launch_bounds__(256) void nm_compress_kernel(const T* __restrict__ 
                                                           const uint8_t* __restrict__ mask, int64_t ldmask,
                                                           int64_t R, int64_t G, int N, int CG,
                                                           T* __restrict__ values, uint8_t* __restrict__ meta,
-                                                          int64_t meta_row, int32_t* bad_groups) {
+                                                          int64_t meta_row, int32_t* bad_groups, int staged) {
+  extern __shared__ __align__(16) unsigned char cst[];
   const int64_t chunks_per_row = (G + CG - 1) / CG;
   const int64_t cid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = R * chunks_per_row;
+  // Staged loads (16-byte aligned rows): a thread's chunk is CG*M elements and CG*M mask bytes,
+  // whole 16-byte pieces; the 64 lanes of a wave load the pieces of the wave's 64 chunks in order,
+  // so that each load instruction covers whole lines, and hand them over through LDS.
+  const int PA = CG * M * (int)sizeof(T) / 16, PM = CG * M / 16, PS = PA + PM;
+  if (staged) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t K = G * M;
+    for (int q = lane; q < 64 * PS; q += 64) {
+      const int tl = q / PS, j = q % PS;
+      const int64_t c = (int64_t)blockIdx.x * blockDim.x + 64 * wave + tl;
+      int64_t rr = R - 1, gg = 0;
+      if (c < total) {
+        rr = c / chunks_per_row;
+        gg = (c - rr * chunks_per_row) * CG;
+      }
+      u32x4 d;
+      if (j < PA) {   // piece j of the chunk's elements; pieces past the row repeat its last one
+        int64_t off = gg * M + (int64_t)j * (16 / (int)sizeof(T));
+        if (off + 16 / (int)sizeof(T) > K) off = K - 16 / (int)sizeof(T);
+        d = *reinterpret_cast<const u32x4*>(A + rr * lda + off);
+      } else {        // piece j - PA of the chunk's mask bytes
+        int64_t off = gg * M + (int64_t)(j - PA) * 16;
+        if (off + 16 > K) off = K - 16;
+        d = *reinterpret_cast<const u32x4*>(mask + rr * ldmask + off);
+      }
+      *reinterpret_cast<u32x4*>(cst + ((size_t)(64 * wave + tl) * PS + j) * 16) = d;
+    }
+    __syncthreads();
+  }
   int bad = 0;
-  if (cid < R * chunks_per_row) {
+  if (cid < total) {
     const int64_t r = cid / chunks_per_row;
     const int64_t g0 = (cid - r * chunks_per_row) * CG;
     const int ng = (int)((G - g0) < CG ? (G - g0) : CG);
@@ -195,10 +226,16 @@ __global__ __launch_bounds__(256) void nm_compress_kernel(const T* __restrict__ 
     for (int gi = 0; gi < ng; ++gi) {
       uint8_t mm[M];
       T xx[M];
+      if (staged) {
+        const unsigned char* mine = cst + (size_t)threadIdx.x * PS * 16;
+        __builtin_memcpy(xx, mine + (size_t)gi * M * sizeof(T), sizeof(T) * M);
+        __builtin_memcpy(mm, mine + (size_t)PA * 16 + gi * M, M);
+      } else {
 #pragma unroll
-      for (int p = 0; p < M; ++p) {
-        mm[p] = mk[gi * M + p];
-        xx[p] = a[gi * M + p];
+        for (int p = 0; p < M; ++p) {
+          mm[p] = mk[gi * M + p];
+          xx[p] = a[gi * M + p];
+        }
       }
       int cnt = 0;
 #pragma unroll
@@ -402,18 +439,28 @@ static hipError_t compress_dispatch(const void* A, int64_t lda, const uint8_t* m
   const int CG = compress_chunk_groups(N, M);
   const int64_t meta_row = meta_row_bytes(K, N, M);
   const int64_t n = R * ((G + CG - 1) / CG);
+  // staged loads when rows are 16-byte aligned and whole 16-byte pieces (so is every clamped piece)
+  const int staged = K % 16 == 0 && (uintptr_t)A % 16 == 0 && ((int64_t)lda * (int64_t)sizeof(T)) % 16 == 0 &&
+                     (uintptr_t)mask % 16 == 0 && ldmask % 16 == 0 && !force_generic();
+  const size_t lds = staged ? (size_t)256 * (CG * M * sizeof(T) / 16 + CG * M / 16) * 16 : 0;
+  if (lds > 0) {
+    (void)hipFuncSetAttribute((const void*)nm_compress_kernel<T, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)nm_compress_kernel<T, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)nm_compress_kernel<T, 16>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+  }
   switch (M) {
     case 4:
-      hipLaunchKernelGGL((nm_compress_kernel<T, 4>), dim3(nblocks(n, 256)), dim3(256), 0, s, (const T*)A, lda,
-                         mask, ldmask, R, G, N, CG, (T*)values, meta, meta_row, bad);
+      hipLaunchKernelGGL((nm_compress_kernel<T, 4>), dim3(nblocks(n, 256)), dim3(256), lds, s, (const T*)A, lda,
+                         mask, ldmask, R, G, N, CG, (T*)values, meta, meta_row, bad, staged);
       break;
     case 8:
-      hipLaunchKernelGGL((nm_compress_kernel<T, 8>), dim3(nblocks(n, 256)), dim3(256), 0, s, (const T*)A, lda,
-                         mask, ldmask, R, G, N, CG, (T*)values, meta, meta_row, bad);
+      hipLaunchKernelGGL((nm_compress_kernel<T, 8>), dim3(nblocks(n, 256)), dim3(256), lds, s, (const T*)A, lda,
+                         mask, ldmask, R, G, N, CG, (T*)values, meta, meta_row, bad, staged);
       break;
     default:
-      hipLaunchKernelGGL((nm_compress_kernel<T, 16>), dim3(nblocks(n, 256)), dim3(256), 0, s, (const T*)A,
-                         lda, mask, ldmask, R, G, N, CG, (T*)values, meta, meta_row, bad);
+      hipLaunchKernelGGL((nm_compress_kernel<T, 16>), dim3(nblocks(n, 256)), dim3(256), lds, s, (const T*)A,
+                         lda, mask, ldmask, R, G, N, CG, (T*)values, meta, meta_row, bad, staged);
       break;
   }
   return hipGetLastError();
