@@ -229,8 +229,9 @@ nm_status spmm_nm_t_lowrank(nm_dtype dt, const void* values, const uint8_t* meta
  *            [Nc/V][R/M][4]: the outputs of prune_act_venom for h
  * V in {64, 128, 256} and M in {4, 8, 16} (NM_ERR_UNSUPPORTED otherwise, and
  * for dtypes other than bf16); R % 256 == 0, Nc % 256 == 0, K % 256 == 0, ldbt % 8 == 0,
- * values, meta and Bt 16-byte aligned, h_values 16-byte and h_meta, h_colsel
- * 4-byte aligned (NM_ERR_UNSUPPORTED otherwise: compose spmm_nm_t_out_bf16,
+ * values, meta and Bt 16-byte aligned, values and Bt each below 4 GiB,
+ * h_values 16-byte and h_meta, h_colsel 4-byte aligned (NM_ERR_UNSUPPORTED
+ * otherwise: compose spmm_nm_t_out_bf16,
  * nm_transpose and prune_act_venom instead).  NM_ERR_SHAPE for non-positive
  * sizes, K % 4 != 0, ldbt < K, R % M != 0 or Nc % V != 0.
  */
