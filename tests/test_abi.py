@@ -101,6 +101,38 @@ def test_venom_reprune_sddmm_errors(L):
     assert L.sddmm_nm(1, FAKE, 8, FAKE, 8, 4, 8, 8, FAKE, FAKE + 2, s) == nm.NM_ERR_ALIGN
 
 
+def test_lowrank_general_fused_errors(L):
+    s = None
+    # spmm_nm_t_lowrank(dt, values, meta, R, K, Bt, ldbt, Nc, U, ldu, Vt, ldvt, rank, Tt, C, ldc, stream)
+    assert L.spmm_nm_t_lowrank(1, FAKE, FAKE, 8, 16, FAKE, 16, 8, FAKE, 16, FAKE, 16, 16, None, FAKE, 8, s) == \
+        nm.NM_ERR_NULL
+    assert L.spmm_nm_t_lowrank(1, FAKE, FAKE, 8, 16, FAKE, 16, 8, FAKE, 8, FAKE, 16, 16, FAKE, FAKE, 8, s) == \
+        nm.NM_ERR_SHAPE                                                                      # ldu < rank
+    assert L.spmm_nm_t_lowrank(1, FAKE, FAKE, 8, 16, FAKE, 16, 8, FAKE, 16, FAKE, 16, 0, FAKE, FAKE, 8, s) == \
+        nm.NM_ERR_SHAPE                                                                      # rank 0
+    assert L.spmm_nm_t_lowrank(1, FAKE, FAKE, 8, 16, FAKE, 16, 8, FAKE + 1, 16, FAKE, 16, 16, FAKE, FAKE, 8, s) == \
+        nm.NM_ERR_ALIGN
+    # spmm_nm_general(dt, values, meta, R, K, N, M, Bt, ldbt, Nc, C, ldc, work, work_bytes, stream)
+    assert L.spmm_nm_general(1, FAKE, FAKE, 8, 16, 2, 5, FAKE, 16, 8, FAKE, 8, None, 0, s) == nm.NM_ERR_UNSUPPORTED
+    assert L.spmm_nm_general(1, FAKE, FAKE, 8, 12, 2, 8, FAKE, 16, 8, FAKE, 8, None, 0, s) == nm.NM_ERR_SHAPE
+    assert L.spmm_nm_general(1, FAKE, FAKE, 8, 16, 2, 8, FAKE, 16, 8, FAKE, 8, None, -1, s) == nm.NM_ERR_SHAPE
+    assert L.spmm_nm_general(1, None, FAKE, 8, 16, 2, 8, FAKE, 16, 8, FAKE, 8, None, 0, s) == nm.NM_ERR_NULL
+    assert L.nm_general_work_bytes(1, 8, 64, 2, 8) == 8 * 32 * 2 + 8 * 8
+    assert L.nm_general_work_bytes(0, 8, 64, 1, 4) == 8 * 32 * 4 + 8 * 8
+    assert L.nm_general_work_bytes(1, 8, 64, 3, 8) == 0
+    # spmm_nm_t_relu_venom(dt, values, meta, R, K, Bt, ldbt, Nc, V, M, hv, hm, hc, stream)
+    assert L.spmm_nm_t_relu_venom(1, FAKE, FAKE, 256, 256, FAKE, 256, 256, 128, 8, FAKE, None, FAKE, s) == \
+        nm.NM_ERR_NULL
+    assert L.spmm_nm_t_relu_venom(0, FAKE, FAKE, 256, 256, FAKE, 256, 256, 128, 8, FAKE, FAKE, FAKE, s) == \
+        nm.NM_ERR_UNSUPPORTED                                                                # fp32
+    assert L.spmm_nm_t_relu_venom(1, FAKE, FAKE, 256, 256, FAKE, 256, 256, 32, 8, FAKE, FAKE, FAKE, s) == \
+        nm.NM_ERR_UNSUPPORTED                                                                # V = 32
+    assert L.spmm_nm_t_relu_venom(1, FAKE, FAKE, 256, 256, FAKE, 256, 200, 128, 8, FAKE, FAKE, FAKE, s) == \
+        nm.NM_ERR_SHAPE                                                                      # Nc % V
+    assert L.spmm_nm_t_relu_venom(1, FAKE, FAKE, 264, 256, FAKE, 256, 256, 128, 8, FAKE, FAKE, FAKE, s) == \
+        nm.NM_ERR_UNSUPPORTED                                                                # R % 256: no fused tile
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
