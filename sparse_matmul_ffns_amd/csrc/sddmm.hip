@@ -397,7 +397,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
 
   // two buffers: the loads of stage kt+1 are in flight while stage kt runs on the matrix cores
   if (KT > 0) issue(0);
-  bool wrote = false;   // this wave stored a transposed stage during the previous step
+  // A transposing wave of a whole row panel issues exactly kDtStores stores (one 16-byte store
+  // per e, every lane in range), younger than its loads of the next stage, so waiting until only
+  // kDtStores operations are outstanding covers those loads.  In a partial last panel a wave may
+  // issue fewer stores (none at all when every one of its rows lies past R), so there every wait
+  // is for all outstanding operations.
+  const bool whole_panel = m0 + BM <= R;
+  bool wrote = false;   // this wave stored a transposed stage of a whole panel during the previous step
   for (int kt = 0; kt < KT; ++kt) {
     // this wave's loads of stage kt have landed (after a transposing step the stores of that step,
     // which are younger than those loads, may still be in flight)
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
     wrote = false;
     if (WRITE_DT && kt % ntn == tn && wave < 4) {
       transpose_stage(kt);
-      wrote = true;
+      wrote = whole_panel;
     }
   }
   if (WRITE_DT) wait_vmcnt<0>();
