@@ -6,8 +6,10 @@
 // completion to the kernel, which waits with an explicit vmcnt before the
 // barrier that publishes a stage (the compiler would otherwise wait for every
 // outstanding LDS DMA before any LDS read, serialising the pipeline).  The
-// kernels that use these helpers set M0 only here and never index register
-// arrays dynamically, so nothing else in them depends on M0.
+// helpers write M0, a register the compiler reserves and does not let inline
+// assembly clobber; the kernels that use them never index register arrays
+// dynamically, and a CPU test (test_codegen.py) checks the compiled code: no
+// instruction outside these helpers reads or writes M0.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,6 +19,19 @@ namespace nms {
 
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+// dma16 by the lanes below `lanes` only (1 <= lanes <= 64).  The other lanes are masked off in
+// EXEC inside the same assembly block, which restores EXEC before it ends: the wave issues exactly
+// one load whatever the lane count, with no branch around it, so every wave's count of
+// outstanding vector-memory operations is the same fixed number.
+__device__ __forceinline__ void dma16_lanes(const void* g, uint32_t lds, uint64_t lane_mask) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\ts_mov_b64 exec, %2\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lane_mask), "s"(lds)
+      : "memory");
 }
 // The same with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset: one VGPR
 // per source instead of two.
