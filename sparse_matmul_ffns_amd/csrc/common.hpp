@@ -117,6 +117,34 @@ __device__ inline int xcd_remap(int wg, int nwg) {
   return (wg % nx) * per + (wg / nx);
 }
 
+// Column-panel-major, XCD-aware tile order.  The dispatcher deals consecutive workgroup ids to
+// the 8 XCDs in turn, and each XCD's L2 serves only its own CUs.  When the ntn column panels
+// divide evenly among the XCDs, XCD x takes panels x*pp .. x*pp + pp - 1 (pp = ntn / 8) for every
+// row tile, so each column panel of the dense operand is fetched into one L2 only; its slots are
+// ordered in groups of gm row tiles x pp panels (the tiles that run together share both operands'
+// panels).  Otherwise the plain XCD-contiguous order grouped by gm row tiles.
+__device__ inline void panel_major_tile(int wg_hw, int ntm, int ntn, int gm, int& tm, int& tn) {
+  const int nx = 8;
+  if (ntn % nx == 0) {
+    const int pp = ntn / nx;
+    const int x = wg_hw % nx, slot = wg_hw / nx;
+    const int grp = slot / (gm * pp);
+    const int first_m = grp * gm;
+    const int gsz = (ntm - first_m) < gm ? (ntm - first_m) : gm;
+    const int within = slot - grp * gm * pp;
+    tm = first_m + within % gsz;
+    tn = x * pp + within / gsz;
+    return;
+  }
+  const int wg = xcd_remap(wg_hw, ntm * ntn);
+  const int grp = wg / (gm * ntn);
+  const int first_m = grp * gm;
+  const int gsz = (ntm - first_m) < gm ? (ntm - first_m) : gm;
+  const int within = wg - grp * gm * ntn;
+  tm = first_m + within % gsz;
+  tn = within / gsz;
+}
+
 // fp32 -> bf16 with round to nearest, ties to even (the bf16 result keeps the fp32 sign and
 // exponent and the top 7 stored significand bits, rounded on the 16 dropped ones); NaN stays a
 // quiet NaN, values past the bf16 range round to infinity.

@@ -44,6 +44,11 @@ hipError_t launch_spmm_nm_dma(const void* values, const uint8_t* meta, int64_t R
 hipError_t launch_spmm_venom_dma(const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R,
                                  int64_t Kd, int V, int M, int64_t G, const void* B, int64_t ldb, int64_t Nc,
                                  float* C, int64_t ldc, hipStream_t s);
+bool spmm_vnm_reg_ok(const uint8_t* colsel, int V, int M, int64_t G, int64_t Kd, int64_t ldb, int64_t Nc, const float* C,
+                     int64_t ldc);
+hipError_t launch_spmm_vnm_reg(const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R, int64_t Kd,
+                               int V, int M, int64_t G, const void* B, int64_t ldb, int64_t Nc, float* C, int64_t ldc,
+                               hipStream_t s);
 bool spmm_nt_ok(const void* values, const uint8_t* meta, const void* Bt, int64_t ldbt, int64_t R, int64_t Nc,
                 int64_t Kd);
 hipError_t launch_spmm_nm_t(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,

@@ -349,8 +349,13 @@ static bool fast_ok(const void* values, const uint8_t* meta, const void* B, int6
 
 // Kernel selection knob, read on every call (for A/B tests of the tiers):
 // NMSPARSE_SPMM_TIER=1 skips the pipelined DMA kernel (register-staged SMFMAC
-// kernel instead); NMSPARSE_FORCE_GENERIC (common.hpp) selects the SIMT kernel.
-static int kernel_tier() { return env_is_one("NMSPARSE_SPMM_TIER") ? 1 : 0; }
+// kernel instead); NMSPARSE_SPMM_TIER=2 skips the register-gather V:N:M kernel
+// (the pipelined DMA kernel instead); NMSPARSE_FORCE_GENERIC (common.hpp)
+// selects the SIMT kernel.
+static int kernel_tier() {
+  const char* e = getenv("NMSPARSE_SPMM_TIER");
+  return e && (e[0] == '1' || e[0] == '2') ? e[0] - '0' : 0;
+}
 
 hipError_t launch_spmm_nm(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* B,
                           int64_t ldb, int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
@@ -384,6 +389,9 @@ hipError_t launch_spmm_venom(int dt, const void* values, const uint8_t* meta, co
   const int64_t G = K / M;
   const int64_t Kd = G * 4;  // the 2:4 domain: 4 selected columns per group
   if (dt == DT_BF16 && !force_generic() && kernel_tier() == 0 && spmm_dma_ok(values, meta, B, ldb, Nc, Kd) &&
+      spmm_vnm_reg_ok(colsel, V, M, G, Kd, ldb, Nc, C, ldc))
+    return launch_spmm_vnm_reg(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
+  if (dt == DT_BF16 && !force_generic() && kernel_tier() != 1 && spmm_dma_ok(values, meta, B, ldb, Nc, Kd) &&
       (uintptr_t)colsel % 16 == 0 && V % 64 == 0)
     return launch_spmm_venom_dma(values, meta, colsel, R, Kd, V, M, G, B, ldb, Nc, C, ldc, s);
   if (dt == DT_BF16 && !force_generic() && fast_ok(values, meta, B, ldb, Nc, C, ldc, Kd) &&

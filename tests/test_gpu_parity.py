@@ -562,10 +562,23 @@ SPMM_VENOM_CASES = [(256, 1024, 264, 64, 8), (384, 512, 136, 128, 8), (48, 96, 4
                     (512, 2048, 512, 128, 8), (128, 256, 72, 64, 4), (64, 512, 256, 64, 16), (192, 1024, 1096, 64, 8)]
 
 
+VENOM_TIERS = {"reg": {}, "dma": {"NMSPARSE_SPMM_TIER": "2"}, "staged": {"NMSPARSE_SPMM_TIER": "1"},
+               "generic": {"NMSPARSE_FORCE_GENERIC": "1"}}
+
+
+@pytest.fixture(params=list(VENOM_TIERS))
+def venom_tier(request, monkeypatch):
+    """Kernel tier of the bf16 V:N:M SpMM: register gather, pipelined DMA, register-staged
+    SMFMAC, or SIMT."""
+    for k, v in VENOM_TIERS[request.param].items():
+        monkeypatch.setenv(k, v)
+    return request.param
+
+
 @pytest.mark.parametrize("R,K,Nc,V,M", SPMM_VENOM_CASES,
                          ids=[f"{c[0]}x{c[1]}x{c[2]}_V{c[3]}_M{c[4]}" for c in SPMM_VENOM_CASES])
 @pytest.mark.parametrize("kind", ["normal", "ints"])
-def test_spmm_venom(R, K, Nc, V, M, kind, tier):
+def test_spmm_venom(R, K, Nc, V, M, kind, venom_tier):
     dtype = "bf16"
     raw = _inputs(kind, (R, K), R * 3 + K, dtype)
     vals, meta, colsel, _, _ = O.prune_venom(raw, dtype, V, M, False)
