@@ -44,7 +44,9 @@
  *   - Device pointers: every array argument is device memory owned by the
  *     caller, naturally aligned for its element type.  Outputs are fully
  *     overwritten and must not overlap inputs.  The library allocates nothing
- *     and keeps no state: calls are reentrant and thread-safe.
+ *     and keeps no state: calls are reentrant and thread-safe -- except
+ *     spmm_nm_general_noalloc, whose calls share a fixed scratch buffer per
+ *     GPU (see there).
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Every call
  *     is asynchronous on that stream; argument errors are returned before
  *     anything is launched.
@@ -55,7 +57,8 @@
  *     a leading dimension below the row width, NM_ERR_UNSUPPORTED for a dtype
  *     or (N, M, V) the call does not implement, NM_ERR_ALIGN for a pointer
  *     that is not aligned to its element size, NM_ERR_HIP when the launch
- *     fails (nm_last_hip_error() names the HIP error).
+ *     fails (nm_last_hip_error() names the HIP error), NM_ERR_TOO_LARGE when
+ *     an operand does not fit a fixed scratch buffer (spmm_nm_general_noalloc).
  */
 #ifndef NMSPARSE_H
 #define NMSPARSE_H
@@ -72,7 +75,8 @@ typedef enum {
   NM_ERR_SHAPE = 2,
   NM_ERR_UNSUPPORTED = 3,
   NM_ERR_ALIGN = 4,
-  NM_ERR_HIP = 5
+  NM_ERR_HIP = 5,
+  NM_ERR_TOO_LARGE = 6
 } nm_status;
 
 typedef enum { NM_F32 = 0, NM_BF16 = 1 } nm_dtype;
@@ -263,6 +267,28 @@ nm_status spmm_nm_general(nm_dtype dt, const void* values, const uint8_t* meta, 
                           int64_t K, int N, int M, const void* Bt, int64_t ldbt, int64_t Nc,
                           float* C, int64_t ldc, void* work, int64_t work_bytes,
                           nm_stream stream);
+
+/*
+ * spmm_nm_general_noalloc -- spmm_nm_general for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation): the same product and kernels, with the 2:4 rewrite held
+ * in a fixed 64 MiB scratch buffer that the library keeps in each GPU's memory
+ * for the life of the process (nm_general_scratch_bytes() gives the size).
+ * The call allocates nothing and takes no work argument; the caller still
+ * passes inputs and outputs as for spmm_nm_general.  Every call on one GPU
+ * shares that buffer: calls that overlap on one GPU (two streams, or two host
+ * threads) race and must be serialised by the caller.  Nothing in the buffer
+ * needs clearing between calls.  Errors as for spmm_nm_general, plus
+ * NM_ERR_TOO_LARGE, returned before any launch, when the rewrite needs more
+ * than the buffer holds (nm_general_work_bytes(dt, R, K, N, M) >
+ * nm_general_scratch_bytes()).
+ */
+nm_status spmm_nm_general_noalloc(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R,
+                                  int64_t K, int N, int M, const void* Bt, int64_t ldbt, int64_t Nc,
+                                  float* C, int64_t ldc, nm_stream stream);
+
+/* Bytes of the fixed scratch buffer of spmm_nm_general_noalloc (host only). */
+int64_t nm_general_scratch_bytes(void);
 
 /*
  * nm_general_work_bytes -- host only: the work bytes spmm_nm_general uses for

@@ -7,6 +7,7 @@ is loaded on first use and must have been built with
 """
 
 from .nmsparse import (  # noqa: F401
+    NM_ERR_TOO_LARGE,
     NmError,
     lib,
     nm_compress,
@@ -21,6 +22,8 @@ from .nmsparse import (  # noqa: F401
     spmm_nm,
     spmm_nm_general,
     general_work_bytes,
+    general_scratch_bytes,
+    spmm_nm_general_noalloc,
     spmm_nm_t,
     spmm_nm_t_lowrank,
     spmm_nm_t_relu_venom,

@@ -136,6 +136,20 @@ nm_status spmm_nm_general(nm_dtype dt, const void* values, const uint8_t* meta, 
                                                 hs(stream)));
 }
 
+nm_status spmm_nm_general_noalloc(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, int N,
+                                  int M, const void* Bt, int64_t ldbt, int64_t Nc, float* C, int64_t ldc,
+                                  nm_stream stream) {
+  if (!values || !meta || !Bt || !C) return NM_ERR_NULL;
+  if (!dtype_ok(dt) || !nm_ok(N, M)) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || Nc <= 0 || K % M != 0 || ldbt < K || ldc < Nc) return NM_ERR_SHAPE;
+  if (!aligned(values, esize(dt)) || !aligned(Bt, esize(dt)) || !aligned(C, 4)) return NM_ERR_ALIGN;
+  if (nms::general_work_bytes(esize(dt), R, K, N, M) > nms::GENERAL_SCRATCH_BYTES) return NM_ERR_TOO_LARGE;
+  return hip_status(nms::launch_spmm_nm_general_noalloc(dt, values, meta, R, K, N, M, Bt, ldbt, Nc, C, ldc,
+                                                        hs(stream)));
+}
+
+int64_t nm_general_scratch_bytes(void) { return nms::GENERAL_SCRATCH_BYTES; }
+
 int64_t nm_general_work_bytes(nm_dtype dt, int64_t R, int64_t K, int N, int M) {
   if (!dtype_ok(dt) || !nm_ok(N, M) || R <= 0 || K <= 0 || K % M != 0) return 0;
   return nms::general_work_bytes(esize(dt), R, K, N, M);
@@ -236,6 +250,7 @@ const char* nm_status_str(nm_status status) {
     case NM_ERR_UNSUPPORTED: return "unsupported dtype, N:M pattern or block size";
     case NM_ERR_ALIGN: return "pointer not aligned to its element size";
     case NM_ERR_HIP: return "HIP launch failed";
+    case NM_ERR_TOO_LARGE: return "the operand needs more scratch memory than the library's fixed buffer holds";
   }
   return "unknown status";
 }

@@ -7,10 +7,18 @@
 // form that way (into caller memory) and the 2:4 SMFMAC SpMM does the product at the 2:4 rate.
 // Other patterns (and calls without that memory) take a plain SIMT kernel that decodes the
 // position stream directly.
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace nms {
+
+// Fixed scratch memory for spmm_nm_general_noalloc: the 2:4 rewrite of the sparse operand lives
+// here instead of in caller memory.  Each GPU the library runs on holds its own copy until the
+// process ends; every call on that GPU shares it.  In host code `scratch` is only a stand-in for
+// the device symbol: its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[GENERAL_SCRATCH_BYTES];
 
 // b-bit field at bit offset bo of an LSB-first stream (the field never runs past its row).
 __device__ inline uint32_t nm_field(const uint8_t* row, int64_t bo, int b) {
@@ -170,6 +178,44 @@ hipError_t launch_spmm_nm_general(int dt, const void* values, const uint8_t* met
     hipLaunchKernelGGL(spmm_general_generic_kernel<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)values, meta, R,
                        K, N, M, (const uint32_t*)Bt, ldbt, Nc, C, ldc);
   return hipGetLastError();
+}
+
+// Device address of `scratch` on the current device, looked up once per device (with that device
+// current) and cached.
+static hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+// spmm_nm_general with the 2:4 rewrite in `scratch`: the same kernels, no allocation.  Returns
+// hipErrorInvalidValue (before any launch) when the rewrite needs more than GENERAL_SCRATCH_BYTES;
+// the caller checks that first.  Nothing in `scratch` has to start at zero: the rewrite writes every
+// byte the product reads.
+hipError_t launch_spmm_nm_general_noalloc(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                                          int N, int M, const void* Bt, int64_t ldbt, int64_t Nc, float* C,
+                                          int64_t ldc, hipStream_t s) {
+  const int64_t need = general_work_bytes(dt == DT_BF16 ? 2 : 4, R, K, N, M);
+  if (need > GENERAL_SCRATCH_BYTES) return hipErrorInvalidValue;
+  void* ptr = nullptr;
+  if (need > 0) {
+    const hipError_t e = scratch_address(&ptr);
+    if (e != hipSuccess) return e;
+  }
+  return launch_spmm_nm_general(dt, values, meta, R, K, N, M, Bt, ldbt, Nc, C, ldc, ptr, need, s);
 }
 
 }  // namespace nms

@@ -70,6 +70,11 @@ hipError_t launch_spmm_nm_t_relu_venom(const void* values, const uint8_t* meta, 
                                       int64_t ldbt, int64_t Nc, int V, int M, void* hv, uint8_t* hm, uint8_t* hc,
                                       hipStream_t s);
 int64_t general_work_bytes(int esz, int64_t R, int64_t K, int N, int M);
+// Size of the fixed scratch memory of spmm_nm_general_noalloc (64 MiB per GPU).
+constexpr int64_t GENERAL_SCRATCH_BYTES = int64_t(64) << 20;
+hipError_t launch_spmm_nm_general_noalloc(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                                          int N, int M, const void* Bt, int64_t ldbt, int64_t Nc, float* C,
+                                          int64_t ldc, hipStream_t s);
 hipError_t launch_spmm_nm_general(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, int N, int M,
                                   const void* Bt, int64_t ldbt, int64_t Nc, float* C, int64_t ldc, void* work,
                                   int64_t work_bytes, hipStream_t s);

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnmsparse.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "nmsparse.h")
 
-NM_OK, NM_ERR_NULL, NM_ERR_SHAPE, NM_ERR_UNSUPPORTED, NM_ERR_ALIGN, NM_ERR_HIP = range(6)
+NM_OK, NM_ERR_NULL, NM_ERR_SHAPE, NM_ERR_UNSUPPORTED, NM_ERR_ALIGN, NM_ERR_HIP, NM_ERR_TOO_LARGE = range(7)
 NM_F32, NM_BF16 = 0, 1
 
 _i64 = ctypes.c_int64
@@ -41,6 +41,7 @@ _SIGNATURES = {
                           _vp],
     "spmm_nm_t_relu_venom": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp],
     "spmm_nm_general": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp],
+    "spmm_nm_general_noalloc": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
     "nm_transpose": [_int, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "prune_act_venom": [_int, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _i64, _vp],
     "spmm_venom": [_int, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.nm_sizes.restype = None
         L.nm_general_work_bytes.argtypes = [_int, _i64, _i64, _int, _int]
         L.nm_general_work_bytes.restype = _i64
+        L.nm_general_scratch_bytes.argtypes = []
+        L.nm_general_scratch_bytes.restype = _i64
         L.nm_status_str.argtypes = [_int]
         L.nm_status_str.restype = ctypes.c_char_p
         L.nm_last_hip_error.argtypes = []
@@ -93,7 +96,7 @@ def header_functions() -> list[str]:
     """Names of the functions include/nmsparse.h declares."""
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:nm_status|void|const char\*|int)\s+(\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:nm_status|void|const char\*|int|int64_t)\s+(\w+)\s*\(", text, flags=re.M)
 
 
 def _check(status: int, call: str) -> None:
@@ -354,6 +357,28 @@ def spmm_nm_general(values: torch.Tensor, meta: torch.Tensor, K: int, N: int, M:
                                  work.numel() * work.element_size() if work is not None else 0, _stream()),
            "spmm_nm_general")
     return out
+
+
+def spmm_nm_general_noalloc(values: torch.Tensor, meta: torch.Tensor, K: int, N: int, M: int, Bt: torch.Tensor,
+                            out: torch.Tensor) -> torch.Tensor:
+    """spmm_nm_general with the library's fixed scratch buffer instead of work memory: the call
+    allocates nothing (the caller passes `out`).  Calls that overlap on one GPU race."""
+    _dev(values, meta, Bt, out)
+    _flat(values, "values"), _flat(meta, "meta")
+    if Bt.dtype != values.dtype:
+        raise TypeError("values and Bt must share a dtype")
+    R = values.shape[0]
+    Nc = Bt.shape[0]
+    if Bt.shape[1] != K or tuple(out.shape) != (R, Nc) or out.dtype != torch.float32:
+        raise ValueError("Bt must have K columns and out must be an fp32 [R, Nc] tensor")
+    _check(lib().spmm_nm_general_noalloc(_dt(Bt), _p(values), _p(meta), R, K, N, M, _p(Bt), _rows(Bt, "Bt"), Nc,
+                                         _p(out), _rows(out, "out"), _stream()), "spmm_nm_general_noalloc")
+    return out
+
+
+def general_scratch_bytes() -> int:
+    """Bytes of the fixed scratch buffer spmm_nm_general_noalloc uses on each GPU."""
+    return int(lib().nm_general_scratch_bytes())
 
 
 def transpose(X: torch.Tensor, out=None) -> torch.Tensor:

@@ -24,13 +24,13 @@ def test_exports_every_header_function(L):
 
 
 def test_binding_covers_header():
-    assert set(nm._SIGNATURES) | {"nm_sizes", "nm_status_str", "nm_last_hip_error", "nm_version"} == \
-        set(nm.header_functions())
+    assert set(nm._SIGNATURES) | {"nm_sizes", "nm_status_str", "nm_last_hip_error", "nm_version",
+                                  "nm_general_work_bytes", "nm_general_scratch_bytes"} == set(nm.header_functions())
 
 
 def test_status_strings(L):
-    for s in range(6):
-        assert L.nm_status_str(s)
+    for s in range(7):
+        assert L.nm_status_str(s) and L.nm_status_str(s) != b"unknown status"
     assert L.nm_version() >= 100
     assert L.nm_last_hip_error() == b""
 
@@ -120,6 +120,16 @@ def test_lowrank_general_fused_errors(L):
     assert L.nm_general_work_bytes(1, 8, 64, 2, 8) == 8 * 32 * 2 + 8 * 8
     assert L.nm_general_work_bytes(0, 8, 64, 1, 4) == 8 * 32 * 4 + 8 * 8
     assert L.nm_general_work_bytes(1, 8, 64, 3, 8) == 0
+    # spmm_nm_general_noalloc(dt, values, meta, R, K, N, M, Bt, ldbt, Nc, C, ldc, stream)
+    assert L.nm_general_scratch_bytes() == 64 << 20
+    assert L.spmm_nm_general_noalloc(1, None, FAKE, 8, 16, 2, 8, FAKE, 16, 8, FAKE, 8, s) == nm.NM_ERR_NULL
+    assert L.spmm_nm_general_noalloc(1, FAKE, FAKE, 8, 16, 2, 5, FAKE, 16, 8, FAKE, 8, s) == nm.NM_ERR_UNSUPPORTED
+    assert L.spmm_nm_general_noalloc(1, FAKE, FAKE, 8, 12, 2, 8, FAKE, 16, 8, FAKE, 8, s) == nm.NM_ERR_SHAPE
+    # a 2:8 matrix whose 2:4 rewrite (R*K/2 bf16 + R*K/8 bytes) exceeds 64 MiB: rejected before any launch
+    big_r, big_k = 65536, 1024
+    assert L.nm_general_work_bytes(1, big_r, big_k, 2, 8) > L.nm_general_scratch_bytes()
+    assert L.spmm_nm_general_noalloc(1, FAKE, FAKE, big_r, big_k, 2, 8, FAKE, big_k, 8, FAKE, 8, s) == \
+        nm.NM_ERR_TOO_LARGE
     # spmm_nm_t_relu_venom(dt, values, meta, R, K, Bt, ldbt, Nc, V, M, hv, hm, hc, stream)
     assert L.spmm_nm_t_relu_venom(1, FAKE, FAKE, 256, 256, FAKE, 256, 256, 128, 8, FAKE, None, FAKE, s) == \
         nm.NM_ERR_NULL
