@@ -22,6 +22,12 @@ pruned zeros counted as if dense).  The JSON line also carries the roofline
 of the step's dominant kernel, timed with HIP events on the stream it runs on,
 and the fp64 CPU oracle timed on the host (rank 0, N = 1 only).
 
+Without --workload the headline is the 2:4 up-projection, and `configs` adds
+the same measurement (step time, dense-equivalent TFLOP/s, share of the bf16
+peak, per-kernel times, roofline of the dominant kernel, oracle sample) for the
+small fp32 case, the V:N:M down-projection, the double-pruned training step and
+the ReLU V:N:M step.
+
 Warm-up: the W untimed steps are repeated until at least one second of them
 has run, so that the timed steps see settled GPU clocks.  `cold` reports, beside
 `value`, the median of five single steps each run after 512 MiB have been
@@ -47,6 +53,10 @@ PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 WARMUP_MIN_S = 1.0            # minimum warm-up wall time (see main)
 METRIC = "dense-equivalent TFLOP/s of 2:4 & V:N:M SpMM at FFN shapes; % of bf16 MFMA peak"
+HEADLINE = "ffn_up_nm24_8192x2048x4096"
+# the other workloads of the metric, measured beside the headline in a default run
+CONFIGS = ["nm24_fp32_256x512x128", "ffn_down_vnm64_2_8_2048x8192x4096",
+           "train_step_nm24_dmodel4096_dff16384_tok8192", "relu_act_vnm128_2_8_8192x16384x4096"]
 
 
 def _parse():
@@ -54,8 +64,9 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="ffn_up_nm24_8192x2048x4096")
+    p.add_argument("--workload", default=None, help=f"one workload (default: {HEADLINE} plus `configs`)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--single", action="store_true", help="measure the headline workload only (no `configs`)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of known size (to scale rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return p.parse_args()
@@ -360,9 +371,29 @@ def cpu_baseline(name):
         fl = 2.0 * R * K * Nc
         sample = (f"whole workload, one step: prune + compress of the [{R}x{K}] weight, fp64 decompress-and-dgemm "
                   f"with the [{K}x{Nc}] operand plus the rank-{r} adapter")
+    elif w["kind"] == "train_step":
+        # a slice of the d_ff rows of the layer (whole 2:4 groups of W_s^T): W's prune + compress,
+        # Y for those rows, the re-pruned transpose of the slice and its share of dX, dW at the
+        # slice's survivors -- all three products of the step on 1/64 of the d_ff dimension
+        dm, dff, T = w["d_model"], w["d_ff"], w["tokens"]
+        rows = 1024
+        W = synth.normal((rows, dm), w["W"]["seed"], w["W"]["mean"], w["W"]["std"])
+        X = synth.normal((dm, T), w["X"]["seed"], w["X"]["mean"], w["X"]["std"])
+        dY = synth.normal((rows, T), w["dY"]["seed"], w["dY"]["mean"], w["dY"]["std"])
+        t0 = time.perf_counter()
+        v, m, _ = O.compress_nm(W, O.prune_nm(W, "bf16", 2, 4), 2, 4)
+        O.spmm_nm(v, m, rows, dm, X, "bf16")                                   # Y rows
+        vt, mt = O.reprune_t(v, m, rows, dm, "bf16")                             # W_ds^T [dm x rows]
+        O.spmm_nm(vt, mt, dm, rows, dY, "bf16")                                  # the slice's share of dX
+        O.sddmm_nm(dY, X, m, rows, dm, "bf16")                                   # dW at the survivors
+        dt = time.perf_counter() - t0
+        fl = 3 * 2.0 * rows * dm * T
+        sample = (f"{rows} of {dff} d_ff rows (the first rows of W and dY, the whole X): "
+                  f"2:4 prune + compress, fp64 Y, re-prune of the transposed slice and its share of dX, dW at the "
+                  f"survivors (1/{dff // rows} of each product)")
     else:
         R, K, Nc, V, M = w["R"], w["K"], w["Nc"], w["V"], w["M"]
-        rows = min(R, 4 * V)
+        rows = min(R, 2048)
         a = w.get("Z") or w.get("A")
         b = w.get("W") or w.get("B")
         A = synth.normal((rows, K), a["seed"], a["mean"], a["std"])
@@ -381,29 +412,18 @@ def cpu_baseline(name):
 # counters recorded with rocprofv3 (profiles/), valid while the kernel source is unchanged
 # ---------------------------------------------------------------------------
 
-# sources of each kernel and of the dispatch that chooses it: a change to any of them voids recorded
-# counters (launch.hpp only declares host launchers and is left out)
-_KERNEL_SOURCES = {
-    "spmm_nm": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp"],
-    "spmm_nm_t": ["spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
-    "spmm_nm_t_lowrank": ["lowrank.hip", "spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
-    "spmm_nm_general": ["general.hip", "spmm.hip", "spmm_nt.hip", "common.hpp", "dma.hpp"],
-    "spmm_venom_down": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp"],
-    "spmm_venom": ["spmm.hip", "spmm_dma.hip", "common.hpp", "dma.hpp"],
-    "sddmm_nm": ["sddmm.hip", "common.hpp", "dma.hpp"],
-    "sddmm_nm_dt": ["sddmm.hip", "common.hpp", "dma.hpp"],
-    "prune_act_venom": ["venom.hip", "common.hpp"],
-}
-
-
-def _src_hash(kernel):
-    srcs = _KERNEL_SOURCES.get(kernel)
-    if srcs is None:
-        return None
+def _src_hash(kernel=None):
+    """Hash of every source file of the library (kernels, headers, C ABI) and of the build flags:
+    recorded counters describe the code built from exactly these."""
+    from sparse_matmul_ffns_amd import build
     h = hashlib.sha256()
-    for name in srcs:
-        with open(os.path.join(ROOT, "sparse_matmul_ffns_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "sparse_matmul_ffns_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "nmsparse.h"), "rb") as f:
+        h.update(f.read())
+    h.update(" ".join(build.FLAGS).replace(build.ROOT, "<repo>").encode())
     return h.hexdigest()[:16]
 
 
@@ -431,21 +451,11 @@ COLD_RUNS = 5
 COLD_FLUSH_BYTES = 512 << 20
 
 
-def main():
-    args = _parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no multi-GPU "
-              "component", file=sys.stderr)
-        sys.exit(2)
+def measure(workload, steps_n, warmup_n, with_cpu):
+    """One workload: warm-up, K timed steps, K event-timed steps (per-kernel durations), cold steps,
+    and the oracle sample; returns the figures as a dict."""
     import torch
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    torch.cuda.set_device(0)
-    if args.copy_calibration:
-        copy_calibration(args.steps)
-        return
-    steps, flops, algo, dominant = build_workload(args.workload)
+    steps, flops, algo, dominant = build_workload(workload)
     torch.cuda.synchronize()
 
     # W untimed warm-up steps, continued until at least WARMUP_MIN_S of them have run: from idle the
@@ -453,7 +463,7 @@ def main():
     # earlier run up to 20% slower
     t_w = time.perf_counter()
     done = 0
-    while done < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+    while done < warmup_n or time.perf_counter() - t_w < WARMUP_MIN_S:
         for _, fn in steps:
             fn()
         done += 1
@@ -464,7 +474,7 @@ def main():
     # timed region: exactly K steps, launched back to back with nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps_n):
         for _, fn in steps:
             fn()
     torch.cuda.synchronize()
@@ -475,14 +485,14 @@ def main():
     # they stay out of the timed region)
     stream = torch.cuda.current_stream()
     names = [n for n, _ in steps]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        ev[s][0].record(stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(steps_n)]
+    for st in range(steps_n):
+        ev[st][0].record(stream)
         for i, (_, fn) in enumerate(steps):
             fn()
-            ev[s][i + 1].record(stream)
+            ev[st][i + 1].record(stream)
     torch.cuda.synchronize()
-    per_kernel_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+    per_kernel_ms = {n: float(np.mean([ev[st][i].elapsed_time(ev[st][i + 1]) for st in range(steps_n)]))
                      for i, n in enumerate(names)}
 
     # cold steps (reported beside, not as `value`): before each, 512 MiB written over a scratch
@@ -499,48 +509,90 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         cold_ms.append(e0.elapsed_time(e1))
-    del flush
-    ms_per_step = elapsed * 1e3 / args.steps
+    del flush, steps
+    torch.cuda.empty_cache()
+    ms_per_step = elapsed * 1e3 / steps_n
     total_flops = sum(flops.values())
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
+    from sparse_matmul_ffns_amd import synth
+    w = synth.WORKLOADS[workload]
     bound, per_launch = algo[dominant]
     t_dom = per_kernel_ms[dominant] * 1e-3
     if bound == "mfma":
-        achieved, peak, unit = per_launch / t_dom / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        achieved, unit = per_launch / t_dom / 1e12, "TFLOP/s"
+        peak = PEAK_FP32_MFMA_TFLOPS if w["dtype"] == "f32" else PEAK_BF16_TFLOPS
     else:
         achieved, peak, unit = per_launch / t_dom / 1e9, PEAK_HBM_GBS, "GB/s"
-    from sparse_matmul_ffns_amd import synth
-    w = synth.WORKLOADS[args.workload]
-    if w["dtype"] == "f32":
-        peak = PEAK_FP32_MFMA_TFLOPS
-    out = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "warmup_steps_run": done,
+    res = {
+        "workload": workload,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "value": round(value, 2),
+        "steps": steps_n,
+        "warmup_steps_run": done,
         "dtype": "bf16" if w["dtype"] == "bf16" else "f32",
-        "data": "synthetic (seeded normal inputs of the workload's shapes; no dataset or trained weights)",
-        "config": {"workload": args.workload, "kernels": names,
-                   "pct_of_bf16_peak_dense_equivalent": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "kernels": names,
+        "pct_of_bf16_peak_dense_equivalent": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "per_kernel_us": {n: round(v * 1e3, 2) for n, v in per_kernel_ms.items()},
         "roofline": {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": recorded_counter(args.workload, dominant, "hbm_bytes_per_launch"),
-                     "mfma_busy_pct": recorded_counter(args.workload, dominant, "mfma_busy_pct")},
+                     "traffic": recorded_counter(workload, dominant, "hbm_bytes_per_launch"),
+                     "mfma_busy_pct": recorded_counter(workload, dominant, "mfma_busy_pct"),
+                     "counters": "recorded: rocprofv3 --pmc of the same sources and build flags "
+                                 f"(profiles/{dominant}_{workload}_pmc.txt); null when they differ"},
         "cold": {"ms_per_step": round(float(np.median(cold_ms)), 5),
                  "value": round(total_flops / (float(np.median(cold_ms)) * 1e-3) / 1e12, 2),
                  "runs": COLD_RUNS, "flush_bytes": COLD_FLUSH_BYTES},
     }
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(args.workload)
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(workload)
+    return res
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no multi-GPU "
+              "component", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
+    workload = args.workload or HEADLINE
+    head = measure(workload, args.steps, args.warmup, not args.no_cpu)
+    out = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "warmup_steps_run": head["warmup_steps_run"],
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic (seeded normal inputs of the workload's shapes; no dataset or trained weights)",
+        "config": {"workload": workload, "kernels": head["kernels"],
+                   "pct_of_bf16_peak_dense_equivalent": head["pct_of_bf16_peak_dense_equivalent"]},
+        "per_kernel_us": head["per_kernel_us"],
+        "roofline": head["roofline"],
+        "cold": head["cold"],
+    }
+    if "cpu_baseline" in head:
+        out["cpu_baseline"] = head["cpu_baseline"]
+    if args.workload is None and not args.single:
+        out["configs"] = {}
+        for name in CONFIGS:
+            r = measure(name, args.steps, args.warmup, not args.no_cpu)
+            r.pop("workload")
+            out["configs"][name] = r
     print(json.dumps(out))
 
 
