@@ -403,6 +403,73 @@ def sddmm_nm_rows(D_raw, X_raw, meta, rows, Kc, dtype):
 
 
 # ---------------------------------------------------------------------------
+# backward of the V:N:M down-projection  [2:4+ abstract: v:n:m activations in
+# every FFN matmul; SFL Methodologie: ReLU activations]
+#
+# Forward: Y = h_s @ W_down, h_s = the V:N:M form of h = ReLU(z) [T, F] (V-row
+# blocks of tokens, groups of M along F).  Readings (the pages give only the
+# forward idea): the gradient reaches z only through the entries the forward
+# kept, times ReLU's derivative (1 where the kept activation is > 0, 0 where it
+# is +0.0, i.e. z <= 0); the weight gradient is dW_down = h_s^T @ dY.
+# ---------------------------------------------------------------------------
+
+def venom_kept_columns(meta, colsel, T, F, V, M):
+    """Dense column index [T, (F/M)*2] of every kept entry: g*M + colsel[t//V, g, j_s]."""
+    G = F // M
+    pos = unpack_positions(meta, T, G * VNM_KEEP_COLS, 2, VNM_KEEP_COLS)          # [T, G, 2] = j_s
+    sel = np.repeat(colsel.astype(np.int64), V, axis=0)                           # [T, G, 4]
+    cols = np.arange(G)[None, :, None] * M + np.take_along_axis(sel, pos, axis=2)  # [T, G, 2]
+    return cols.reshape(T, G * 2)
+
+
+def sddmm_venom(dY_raw, Wd_raw, h_values, h_meta, h_colsel, T, F, V, M, dtype, relu):
+    """dZ values [T, (F/M)*2], aligned with h_s's values: (dY @ W_down^T) in float64 read at
+    h_s's kept positions, times ReLU's derivative at them when relu."""
+    full = decode(dY_raw, dtype) @ decode(Wd_raw, dtype).T                        # [T, F]
+    out = np.take_along_axis(full, venom_kept_columns(h_meta, h_colsel, T, F, V, M), axis=1)
+    if relu:
+        out = np.where(decode(h_values, dtype) > 0, out, 0.0)
+    return out
+
+
+def sddmm_venom_loop(dY_raw, Wd_raw, h_values, h_meta, h_colsel, T, F, V, M, dtype, relu):
+    """sddmm_venom element by element (small inputs)."""
+    G = F // M
+    pos = unpack_positions(h_meta, T, G * VNM_KEEP_COLS, 2, VNM_KEEP_COLS)
+    dY, Wd, hv = decode(dY_raw, dtype), decode(Wd_raw, dtype), decode(h_values, dtype)
+    out = np.zeros((T, 2 * G))
+    for t in range(T):
+        for g in range(G):
+            for s in range(2):
+                col = g * M + int(h_colsel[t // V, g, pos[t, g, s]])
+                acc = 0.0
+                for c in range(dY.shape[1]):
+                    acc += dY[t, c] * Wd[col, c]
+                out[t, 2 * g + s] = acc if (not relu or hv[t, 2 * g + s] > 0) else 0.0
+    return out
+
+
+def spmm_venom_tn(h_values, h_meta, h_colsel, T, F, V, M, dY_raw, dtype):
+    """dW_down [F, Nc] = decompress_venom(h_s)^T @ dY in float64."""
+    H = decode(decompress_venom(h_values, h_meta, h_colsel, T, F, V, M), dtype)
+    return H.T @ decode(dY_raw, dtype)
+
+
+def spmm_venom_tn_loop(h_values, h_meta, h_colsel, T, F, V, M, dY_raw, dtype):
+    """dW_down[col] += h_s[t, 2g+s] * dY[t] for every kept entry (small inputs)."""
+    G = F // M
+    pos = unpack_positions(h_meta, T, G * VNM_KEEP_COLS, 2, VNM_KEEP_COLS)
+    hv, dY = decode(h_values, dtype), decode(dY_raw, dtype)
+    out = np.zeros((F, dY.shape[1]))
+    for t in range(T):
+        for g in range(G):
+            for s in range(2):
+                col = g * M + int(h_colsel[t // V, g, pos[t, g, s]])
+                out[col] += hv[t, 2 * g + s] * dY[t]
+    return out
+
+
+# ---------------------------------------------------------------------------
 # sparse plus low-rank  [SLOPE abstract: low-rank adapters joined to the sparse
 # weight for the last iterations of pre-training, at little extra cost]
 # ---------------------------------------------------------------------------

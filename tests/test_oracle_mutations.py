@@ -142,6 +142,30 @@ def _general_slot_shift(values, meta, R, K, N, M, B_raw, dtype):
     return A.reshape(R, K) @ O.decode(B_raw, dtype)
 
 
+_orig_kept = O.venom_kept_columns
+
+
+def _kept_no_colsel(meta, colsel, T, F, V, M):
+    G = F // M
+    pos = O.unpack_positions(meta, T, G * 4, 2, 4)
+    return (np.arange(G)[None, :, None] * M + pos).reshape(T, G * 2)   # mistake: j_s used as the column
+
+
+def _kept_block_of_next_row(meta, colsel, T, F, V, M):
+    return _orig_kept(meta, np.roll(colsel, -1, axis=0), T, F, V, M)    # mistake: wrong V-block's choice
+
+
+def _sddmm_venom_gate_inverted(dY_raw, Wd_raw, h_values, h_meta, h_colsel, T, F, V, M, dtype, relu):
+    full = O.decode(dY_raw, dtype) @ O.decode(Wd_raw, dtype).T
+    out = np.take_along_axis(full, _orig_kept(h_meta, h_colsel, T, F, V, M), axis=1)
+    return np.where(O.decode(h_values, dtype) <= 0, out, 0.0) if relu else out   # mistake: gate inverted
+
+
+def _spmm_venom_tn_tokens_shifted(h_values, h_meta, h_colsel, T, F, V, M, dY_raw, dtype):
+    H = O.decode(O.decompress_venom(h_values, h_meta, h_colsel, T, F, V, M), dtype)
+    return H.T @ np.roll(O.decode(dY_raw, dtype), 1, axis=0)   # mistake: dY rows paired with the wrong tokens
+
+
 MUTATIONS = [
     ("nm_select", _select_tie_high, [lambda: P.test_nm_select_exhaustive_m4(2, "f32")]),
     ("nm_select", _select_no_ties, [lambda: P.test_prune_compress_invariants(2, 4, "bf16")]),
@@ -163,6 +187,14 @@ MUTATIONS = [
                                                  lambda: P.test_spmm_lowrank_special_cases()]),
     ("spmm_nm_lowrank", _lowrank_k_reversed, [lambda: P.test_spmm_lowrank_exact_integers()]),
     ("spmm_nm_general", _general_slot_shift, [lambda: P.test_spmm_general_gather_loop_and_exact_integers(2, 8)]),
+    ("venom_kept_columns", _kept_no_colsel, [lambda: P.test_sddmm_venom_loop_and_exact_integers(False),
+                                             lambda: P.test_venom_backward_adjoint_identities(4, 8)]),
+    ("venom_kept_columns", _kept_block_of_next_row, [lambda: P.test_sddmm_venom_loop_and_exact_integers(False),
+                                                     lambda: P.test_venom_backward_adjoint_identities(4, 8)]),
+    ("sddmm_venom", _sddmm_venom_gate_inverted, [lambda: P.test_sddmm_venom_loop_and_exact_integers(True),
+                                                 lambda: P.test_sddmm_venom_relu_gate()]),
+    ("spmm_venom_tn", _spmm_venom_tn_tokens_shifted, [lambda: P.test_spmm_venom_tn_loop_and_exact_integers(),
+                                                lambda: P.test_venom_backward_adjoint_identities(2, 4)]),
 ]
 
 

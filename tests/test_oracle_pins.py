@@ -332,6 +332,82 @@ def test_spmm_venom_gather_loop_equals_dgemm():
     assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
 
 
+# ---------------------------------------------------------------------------
+# backward of the V:N:M down-projection: loop forms, adjoint identities with the
+# forward SpMM, the M = 4 case, the ReLU gate
+# ---------------------------------------------------------------------------
+
+def _venom_bwd_case(T, F, Nc, V, M, seed, ints, relu=True):
+    gen = synth.small_ints if ints else synth.normal
+    z = gen((T, F), seed, dtype="bf16")
+    hv, hm, hc, _, _ = O.prune_venom(z, "bf16", V, M, apply_relu=relu)
+    dY = gen((T, Nc), seed + 1, dtype="bf16")
+    Wd = gen((F, Nc), seed + 2, dtype="bf16")
+    return hv, hm, hc, dY, Wd
+
+
+@pytest.mark.parametrize("relu", [False, True])
+def test_sddmm_venom_loop_and_exact_integers(relu):
+    T, F, Nc, V, M = 8, 32, 5, 4, 8
+    for ints in (False, True):
+        hv, hm, hc, dY, Wd = _venom_bwd_case(T, F, Nc, V, M, 80 + ints, ints, relu)
+        a = O.sddmm_venom(dY, Wd, hv, hm, hc, T, F, V, M, "bf16", relu)
+        b = O.sddmm_venom_loop(dY, Wd, hv, hm, hc, T, F, V, M, "bf16", relu)
+        assert np.array_equal(a, b) if ints else np.allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+def test_spmm_venom_tn_loop_and_exact_integers():
+    T, F, Nc, V, M = 8, 48, 6, 2, 16
+    for ints in (False, True):
+        hv, hm, hc, dY, _ = _venom_bwd_case(T, F, Nc, V, M, 84 + ints, ints)
+        a = O.spmm_venom_tn(hv, hm, hc, T, F, V, M, dY, "bf16")
+        b = O.spmm_venom_tn_loop(hv, hm, hc, T, F, V, M, dY, "bf16")
+        assert np.array_equal(a, b) if ints else np.allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("V,M", [(4, 8), (2, 4), (8, 16), (1, 8)])
+def test_venom_backward_adjoint_identities(V, M):
+    """<h_s W, dY> = <h_s^T dY, W> = sum over kept entries of h * (dY W^T): the two backward
+    products are the adjoints of the pinned forward product (exact on integers)."""
+    T, F, Nc = 16, 4 * M, 6
+    hv, hm, hc, dY, Wd = _venom_bwd_case(T, F, Nc, V, M, 90 + M, True, relu=False)
+    Y = O.spmm_venom(hv, hm, hc, T, F, V, M, Wd, "bf16")
+    dW = O.spmm_venom_tn(hv, hm, hc, T, F, V, M, dY, "bf16")
+    dz = O.sddmm_venom(dY, Wd, hv, hm, hc, T, F, V, M, "bf16", relu=False)
+    lhs = float(np.sum(Y * O.decode(dY, "bf16")))
+    assert lhs == float(np.sum(dW * O.decode(Wd, "bf16")))
+    assert lhs == float(np.sum(O.decode(hv, "bf16") * dz))
+
+
+def test_sddmm_venom_m4_is_sddmm_nm():
+    """M = 4 keeps every column (colsel = 0..3), so the V:N:M SDDMM is the 2:4 SDDMM with h_s's
+    nibbles."""
+    T, F, Nc, V = 8, 16, 7, 4
+    hv, hm, hc, dY, Wd = _venom_bwd_case(T, F, Nc, V, 4, 95, False, relu=False)
+    assert (hc == np.arange(4, dtype=np.uint8)).all()
+    assert np.array_equal(O.sddmm_venom(dY, Wd, hv, hm, hc, T, F, V, 4, "bf16", relu=False),
+                          O.sddmm_nm(dY, Wd, hm, T, F, "bf16"))
+
+
+def test_sddmm_venom_relu_gate():
+    T, F, Nc, V, M = 8, 32, 4, 4, 8
+    hv, hm, hc, dY, Wd = _venom_bwd_case(T, F, Nc, V, M, 97, False, relu=True)
+    gated = O.sddmm_venom(dY, Wd, hv, hm, hc, T, F, V, M, "bf16", relu=True)
+    plain = O.sddmm_venom(dY, Wd, hv, hm, hc, T, F, V, M, "bf16", relu=False)
+    pos = O.decode(hv, "bf16") > 0
+    assert 0 < pos.sum() < pos.size                     # both kinds of kept entries occur
+    assert np.array_equal(gated[pos], plain[pos]) and not gated[~pos].any()
+
+
+def test_abs_bound_hand_values():
+    # |A| |B| by hand: [[1*1 + 2*2, 1*4 + 2*5], [0*1 + 3*2, 0*4 + 3*5]]
+    A = np.array([[1.0, -2.0], [0.0, 3.0]])
+    B = np.array([[-1.0, 4.0], [2.0, -5.0]])
+    assert np.array_equal(O.abs_bound(A, B), np.array([[5.0, 14.0], [6.0, 15.0]]))
+    # a product that cancels to zero keeps its full bound
+    assert np.array_equal(O.abs_bound(np.array([[1.0, 1.0]]), np.array([[1.0], [-1.0]])), np.array([[2.0]]))
+
+
 def test_sddmm_exact_rational():
     R, Kc, T = 4, 8, 6
     D = synth.small_ints((R, T), 70, dtype="bf16")
