@@ -269,6 +269,55 @@ nm_status spmm_nm_general(nm_dtype dt, const void* values, const uint8_t* meta, 
                           nm_stream stream);
 
 /*
+ * sddmm_venom -- gradient reaching V:N:M activations through a down-projection
+ * ("To 2:4 Sparsity and Beyond", abstract: v:n:m activations in every FFN
+ * matmul).  For Y = h_s . W_down with h_s the V:N:M form (prune_act_venom,
+ * apply_relu) of h = ReLU(z) [T][F]:
+ *   dz[t][2g+s] = sum_c dY[t][c] * W_down[g*M + colsel[t/V][g][j_s]][c]
+ *                 (times [h_values[t][2g+s] > 0] when apply_relu)
+ * i.e. dY . W_down^T at the entries h_s keeps -- the only ones through which
+ * the gradient flows -- gated by ReLU's derivative.
+ *   dY       [T][lddy] dtype dt         W_down [F][ldw] dtype dt (Nc columns)
+ *   h_values [T][(F/M)*2], h_meta [T][ceil(F/M/2)], h_colsel [T/V][F/M][4]:
+ *            h_s as prune_act_venom writes it (N = 2, 4 kept columns per group)
+ *   dz       [T][(F/M)*2] fp32 output, aligned with h_values
+ *   dYt      optional (NULL allowed, bf16 only): dYt [Nc][lddyt] receives
+ *            dY^T, the operand spmm_venom_tn takes
+ * M in {4, 8, 16}, 1 <= V <= 256, F % M == 0, T % V == 0.  bf16 with
+ * V % 128 == 0, Nc % 64 == 0 and 16-byte aligned rows runs the pipelined
+ * matrix-core kernel (B rows gathered per V-block); other calls a SIMT kernel
+ * (then dYt by nm_transpose).  Errors as for sddmm_nm.
+ */
+nm_status sddmm_venom(nm_dtype dt, const void* dY, int64_t lddy, const void* W_down, int64_t ldw,
+                      int64_t T, int64_t F, int64_t Nc, int V, int M, const void* h_values,
+                      const uint8_t* h_meta, const uint8_t* h_colsel, int apply_relu, float* dz,
+                      void* dYt, int64_t lddyt, nm_stream stream);
+
+/*
+ * spmm_venom_tn -- weight gradient of the same down-projection:
+ *   dW[k][c] = sum_t h_s[t][k] * dY[t][c]      (h_s^T . dY)
+ *   h_values, h_meta, h_colsel: h_s [T][F] in V:N:M form (as for sddmm_venom)
+ *   dYt  [Nc][lddyt] dY^T, dtype dt (token index contiguous)
+ *   dW   [F][lddw] fp32 output
+ *   work optional device memory of work_bytes bytes, 16-byte aligned, not
+ *        overlapping any argument (NULL allowed)
+ * The reduction runs over tokens and every V-block of tokens keeps a different
+ * half of each group's rows, so the product has no empty blocks for the matrix
+ * instructions to skip.  bf16 with work of at least
+ * nm_venom_tn_work_bytes(dt, T, F) bytes, T % 64 == 0, lddyt % 8 == 0,
+ * lddw % 4 == 0 and 16-byte aligned operands writes h_s^T densely into work
+ * and runs a matrix-core NT GEMM; other calls a SIMT kernel on the compressed
+ * form.  Errors as for spmm_venom, plus NM_ERR_SHAPE for work_bytes < 0.
+ */
+nm_status spmm_venom_tn(nm_dtype dt, const void* h_values, const uint8_t* h_meta,
+                        const uint8_t* h_colsel, int64_t T, int64_t F, int V, int M,
+                        const void* dYt, int64_t lddyt, int64_t Nc, float* dW, int64_t lddw,
+                        void* work, int64_t work_bytes, nm_stream stream);
+
+/* Work bytes spmm_venom_tn uses for T tokens and F columns of h (host only; 0 = none). */
+int64_t nm_venom_tn_work_bytes(nm_dtype dt, int64_t T, int64_t F);
+
+/*
  * spmm_nm_general_noalloc -- spmm_nm_general for callers that cannot allocate
  * device memory (code under stream capture, tight serving loops, harnesses that
  * forbid allocation): the same product and kernels, with the 2:4 rewrite held

@@ -24,6 +24,9 @@ from .nmsparse import (  # noqa: F401
     general_work_bytes,
     general_scratch_bytes,
     spmm_nm_general_noalloc,
+    sddmm_venom,
+    spmm_venom_tn,
+    venom_tn_work_bytes,
     spmm_nm_t,
     spmm_nm_t_lowrank,
     spmm_nm_t_relu_venom,

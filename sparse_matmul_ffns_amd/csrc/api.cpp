@@ -148,6 +148,39 @@ nm_status spmm_nm_general_noalloc(nm_dtype dt, const void* values, const uint8_t
                                                         hs(stream)));
 }
 
+nm_status sddmm_venom(nm_dtype dt, const void* dY, int64_t lddy, const void* W_down, int64_t ldw, int64_t T,
+                      int64_t F, int64_t Nc, int V, int M, const void* h_values, const uint8_t* h_meta,
+                      const uint8_t* h_colsel, int apply_relu, float* dz, void* dYt, int64_t lddyt,
+                      nm_stream stream) {
+  if (!dY || !W_down || !h_values || !h_meta || !h_colsel || !dz) return NM_ERR_NULL;
+  if (!dtype_ok(dt) || !m_ok(M) || !v_ok(V) || (dYt && dt != NM_BF16)) return NM_ERR_UNSUPPORTED;
+  if (T <= 0 || F <= 0 || Nc <= 0 || F % M != 0 || T % V != 0 || lddy < Nc || ldw < Nc || (dYt && lddyt < T))
+    return NM_ERR_SHAPE;
+  if (!aligned(dY, esize(dt)) || !aligned(W_down, esize(dt)) || !aligned(h_values, 2 * esize(dt)) ||
+      !aligned(h_colsel, 4) || !aligned(dz, 8) || !aligned(dYt, esize(dt)))
+    return NM_ERR_ALIGN;
+  return hip_status(nms::launch_sddmm_venom(dt, dY, lddy, W_down, ldw, T, F, Nc, V, M, h_values, h_meta, h_colsel,
+                                            apply_relu ? 1 : 0, dz, dYt, lddyt, hs(stream)));
+}
+
+nm_status spmm_venom_tn(nm_dtype dt, const void* h_values, const uint8_t* h_meta, const uint8_t* h_colsel, int64_t T,
+                        int64_t F, int V, int M, const void* dYt, int64_t lddyt, int64_t Nc, float* dW, int64_t lddw,
+                        void* work, int64_t work_bytes, nm_stream stream) {
+  if (!h_values || !h_meta || !h_colsel || !dYt || !dW) return NM_ERR_NULL;
+  if (!dtype_ok(dt) || !m_ok(M) || !v_ok(V)) return NM_ERR_UNSUPPORTED;
+  if (T <= 0 || F <= 0 || Nc <= 0 || F % M != 0 || T % V != 0 || lddyt < T || lddw < Nc || work_bytes < 0)
+    return NM_ERR_SHAPE;
+  if (!aligned(h_values, 2 * esize(dt)) || !aligned(h_colsel, 4) || !aligned(dYt, esize(dt)) || !aligned(dW, 4))
+    return NM_ERR_ALIGN;
+  return hip_status(nms::launch_spmm_venom_tn(dt, h_values, h_meta, h_colsel, T, F, V, M, dYt, lddyt, Nc, dW, lddw,
+                                              work, work_bytes, hs(stream)));
+}
+
+int64_t nm_venom_tn_work_bytes(nm_dtype dt, int64_t T, int64_t F) {
+  if (!dtype_ok(dt) || T <= 0 || F <= 0) return 0;
+  return nms::venom_tn_work_bytes(esize(dt), T, F);
+}
+
 int64_t nm_general_scratch_bytes(void) { return nms::GENERAL_SCRATCH_BYTES; }
 
 int64_t nm_general_work_bytes(nm_dtype dt, int64_t R, int64_t K, int N, int M) {

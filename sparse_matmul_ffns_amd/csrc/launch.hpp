@@ -82,6 +82,22 @@ hipError_t launch_nm_transpose(int dt, const void* src, int64_t lds, int64_t R, 
                                hipStream_t s);
 hipError_t launch_sddmm_nm_dt(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
                               int64_t Tn, const uint8_t* meta, float* out, void* Dt, int64_t lddt, hipStream_t s);
+bool sddmm_venom_fast_ok(const void* dY, int64_t lddy, const void* Wd, int64_t ldw, int64_t Tn, int64_t F, int64_t Nc,
+                         int V, int M, const void* hv, const float* dz, const void* dYt, int64_t lddyt);
+hipError_t launch_sddmm_venom_dma(const void* dY, int64_t lddy, const void* Wd, int64_t ldw, int64_t Tn, int64_t F,
+                                  int64_t Nc, int V, int M, const void* hv, const uint8_t* hm, const uint8_t* hc,
+                                  int relu, float* dz, void* dYt, int64_t lddyt, hipStream_t s);
+bool dense_nt_fast_ok(const void* A, int64_t lda, const void* B, int64_t ldb, const float* out, int64_t ldo,
+                      int64_t Tn);
+hipError_t launch_dense_nt(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t R, int64_t Kc, int64_t Tn,
+                           float* out, int64_t ldo, hipStream_t s);
+int64_t venom_tn_work_bytes(int esz, int64_t Tn, int64_t F);
+hipError_t launch_sddmm_venom(int dt, const void* dY, int64_t lddy, const void* Wd, int64_t ldw, int64_t Tn,
+                              int64_t F, int64_t Nc, int V, int M, const void* hv, const uint8_t* hm,
+                              const uint8_t* hc, int relu, float* dz, void* dYt, int64_t lddyt, hipStream_t s);
+hipError_t launch_spmm_venom_tn(int dt, const void* hv, const uint8_t* hm, const uint8_t* hc, int64_t Tn, int64_t F,
+                                int V, int M, const void* dYt, int64_t lddyt, int64_t Nc, float* dW, int64_t lddw,
+                                void* work, int64_t work_bytes, hipStream_t s);
 hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R,
                            int64_t Kc, int64_t T, const uint8_t* meta, float* out, hipStream_t s);
 

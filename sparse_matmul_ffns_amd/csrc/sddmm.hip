@@ -247,16 +247,30 @@ struct SdCfg {
   static_assert(STAGES == 2 && STAGE * STAGES <= 160 * 1024, "two LDS buffers");
 };
 
-// WRITE_DT: the kernel also writes Dt[t][r] = D[r][t].  Every 64-t stage of a 256-row panel of D
+// WRITE_DT: the kernel also writes Dt[t][r] = D[r][t].  Every 64-t stage of a BM-row panel of D
 // passes through the LDS of all the panel's column tiles; the one with column tile
-// tn == kt % (number of column tiles) transposes stage kt from LDS -- waves 0-3, one 8 x 8 block
-// per lane (eight 16-byte LDS reads, v_perm, eight 16-byte stores; the 8 lanes of a t row write
-// 128 contiguous bytes) -- so each stage is written once and the work is spread evenly.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool WRITE_DT>
+// tn == kt % (number of column tiles) transposes stage kt from LDS -- waves 0 .. BM/64 - 1, one
+// 8 x 8 block per lane (eight 16-byte LDS reads, v_perm, eight 16-byte stores; the 8 lanes of a t
+// row write 128 contiguous bytes) -- so each stage is written once and the work is spread evenly.
+//
+// MODE: SD_NM -- out[r][2g+s] = (D X^T)[r][4g + p_s(r, g)], p_s from the 2:4 nibbles `meta` (the
+//   weight gradient of a 2:4 layer);
+// SD_VNM -- the columns of X are the rows gathered through a V:N:M column selection: gathered
+//   column 4g + j is row g*M + colsel[r/V][g][j] of X (the tile's BM rows lie in one V-block), and
+//   out[r][2g+s] = (D X_gathered^T)[r][4g + j_s(r, g)] with j_s from the V:N:M nibbles `meta`,
+//   set to 0 where hval[r][2g+s] (bf16) is not > 0 when relu (the gradient of ReLU'd V:N:M
+//   activations);
+// SD_DENSE -- out[r][c] = (D X^T)[r][c] for every column, row stride ldo (a plain NT GEMM).
+enum { SD_NM = 0, SD_VNM = 1, SD_DENSE = 2 };
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool WRITE_DT, int MODE = SD_NM>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
     const uint16_t* __restrict__ D, int64_t ldd, const uint16_t* __restrict__ X, int64_t ldx, int64_t R, int64_t Kc,
-    int64_t Tn, const uint8_t* __restrict__ meta, float* __restrict__ out, uint16_t* __restrict__ Dt, int64_t lddt) {
+    int64_t Tn, const uint8_t* __restrict__ meta, float* __restrict__ out, uint16_t* __restrict__ Dt, int64_t lddt,
+    const uint8_t* __restrict__ colsel, int V, int M, const uint16_t* __restrict__ hval, int relu, int64_t ldo) {
   using Cfg = SdCfg<BM, BN, WAVES_M, WAVES_N, STAGES>;
+  static_assert(!WRITE_DT || BM % 64 == 0, "transposing waves cover 64 rows each");
+  static_assert(!WRITE_DT || BM / 64 <= WAVES_M * WAVES_N, "enough waves to transpose a stage");
   constexpr int FM = Cfg::FM;
   extern __shared__ __align__(1024) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -295,6 +309,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
     const int n = (r & ~127) | ((r & 31) << 2) | ((r & 127) >> 5);   // inverse of sd_xrow
     int64_t col = n0 + n;
     col = col < Kc ? col : Kc - 1;
+    if constexpr (MODE == SD_VNM) {
+      // gathered column -> row of X through the tile's V-block's column selection
+      const int64_t g = col >> 2, G = Kc >> 2;
+      col = g * M + (colsel[((m0 / V) * G + g) * 4 + (col & 3)] & (M - 1));
+    }
     b_src[t] = X + col * ldx + 8 * c;
   }
   auto issue = [&](int kt) {
@@ -365,8 +384,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   // Dt: stage kt of this row panel is written by the workgroup whose column tile is kt % ntn
   constexpr int kDtStores = 8;   // 16-byte stores per lane of a transposing wave and stage
   auto transpose_stage = [&](int kt) {
-    // waves 0-3: 32 row blocks x 8 t blocks of 8 x 8; the 8 lanes of a row block read the 8
-    // chunks of each of its rows (the whole 128-byte LDS row: no bank conflicts among them)
+    // waves 0 .. BM/64 - 1: BM/8 row blocks x 8 t blocks of 8 x 8; the 8 lanes of a row block
+    // read the 8 chunks of each of its rows (the whole 128-byte LDS row: no bank conflicts)
     const int tb = lane & 7, rb = 8 * wave + (lane >> 3);
     const unsigned char* st = smem + (kt % STAGES) * Cfg::STAGE;
     u32x4 v[8];
@@ -412,7 +431,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
     if (kt + 1 < KT) issue(kt + 1);
     compute(kt);
     wrote = false;
-    if (WRITE_DT && kt % ntn == tn && wave < 4) {
+    if (WRITE_DT && kt % ntn == tn && wave < BM / 64) {
       transpose_stage(kt);
       wrote = whole_panel;
     }
@@ -422,6 +441,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   // epilogue: lane l32 holds columns 4*l32 .. +3 of the wave's 128 = 2:4 group gq
   const int64_t G = Kc / 4, mrow = (Kc + 7) / 8;
   const int64_t gq = (n0 + wn * 128) / 4 + l32;
+  if constexpr (MODE == SD_DENSE) {
+    // every column: 16 contiguous bytes per lane and row (the 32 lanes of a row write 512 bytes)
+    const int64_t c0 = 4 * gq;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * Cfg::WM + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
+        if (row < R && c0 < Kc) {
+          float* dst = out + row * ldo + c0;
+          if (c0 + 4 <= Kc) {
+            __builtin_nontemporal_store(f32x4{acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]},
+                                        reinterpret_cast<f32x4*>(dst));
+          } else {
+            const float v[4] = {acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]};
+            for (int q = 0; q < 4 && c0 + q < Kc; ++q) dst[q] = v[q];
+          }
+        }
+      }
+    return;
+  }
+  const int64_t mrow_v = MODE == SD_VNM ? (G + 1) / 2 : mrow;   // V:N:M nibbles: one per gathered group
   if (gq < G) {
     uint32_t mb[FM][16];   // the metadata byte of every output row of the lane, loaded up front
 #pragma unroll
@@ -430,7 +471,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
       for (int e = 0; e < 16; ++e) {
         int64_t row = m0 + wm * Cfg::WM + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
         row = row < R ? row : R - 1;
-        mb[i][e] = meta[row * mrow + gq / 2];
+        mb[i][e] = meta[row * mrow_v + gq / 2];
       }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -445,6 +486,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
           f32x2 o;
           o[0] = p0 == 0 ? v0 : p0 == 1 ? v1 : p0 == 2 ? v2 : v3;
           o[1] = p1 == 0 ? v0 : p1 == 1 ? v1 : p1 == 2 ? v2 : v3;
+          if constexpr (MODE == SD_VNM) {
+            if (relu) {
+              // ReLU's derivative at the kept activations: 1 where the bf16 value is > 0
+              const uint32_t hp = *reinterpret_cast<const uint32_t*>(hval + row * (2 * G) + 2 * gq);
+              o[0] = Elem<uint16_t>::positive((uint16_t)(hp & 0xFFFF)) ? o[0] : 0.f;
+              o[1] = Elem<uint16_t>::positive((uint16_t)(hp >> 16)) ? o[1] : 0.f;
+            }
+          }
           __builtin_nontemporal_store(o, reinterpret_cast<f32x2*>(out + row * (Kc / 2) + 2 * gq));
         }
       }
@@ -452,16 +501,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool WRITE_DT>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool WRITE_DT, int MODE = SD_NM>
 static hipError_t run_sddmm_dma(const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
-                                int64_t Tn, const uint8_t* meta, float* out, void* Dt, int64_t lddt, hipStream_t s) {
+                                int64_t Tn, const uint8_t* meta, float* out, void* Dt, int64_t lddt, hipStream_t s,
+                                const uint8_t* colsel = nullptr, int V = 1, int M = 4, const void* hval = nullptr,
+                                int relu = 0, int64_t ldo = 0) {
   using Cfg = SdCfg<BM, BN, WAVES_M, WAVES_N, STAGES>;
   const size_t lds = (size_t)Cfg::STAGE * STAGES;
-  auto kern = sddmm_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, WRITE_DT>;
+  auto kern = sddmm_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, WRITE_DT, MODE>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int64_t ntiles = ((R + BM - 1) / BM) * ((Kc + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg::NT), lds, s, (const uint16_t*)D, ldd, (const uint16_t*)X,
-                     ldx, R, Kc, Tn, meta, out, (uint16_t*)Dt, lddt);
+                     ldx, R, Kc, Tn, meta, out, (uint16_t*)Dt, lddt, colsel, V, M, (const uint16_t*)hval, relu, ldo);
   return hipGetLastError();
 }
 
@@ -511,6 +562,40 @@ hipError_t launch_sddmm_nm_dt(int dt, const void* D, int64_t ldd, const void* X,
   const hipError_t e = launch_sddmm_nm(dt, D, ldd, X, ldx, R, Kc, Tn, meta, out, s);
   if (e != hipSuccess) return e;
   return launch_nm_transpose(dt, D, ldd, R, Tn, Dt, lddt, s);
+}
+
+// V:N:M SDDMM (gradient of V:N:M activations): 128 x 512 tiles (128 tokens inside one V-block,
+// 512 gathered columns), eight waves of 64 x 128, two stages of 80 KB.
+bool sddmm_venom_fast_ok(const void* dY, int64_t lddy, const void* Wd, int64_t ldw, int64_t Tn, int64_t F, int64_t Nc,
+                         int V, int M, const void* hv, const float* dz, const void* dYt, int64_t lddyt) {
+  (void)Tn, (void)F, (void)M;
+  return Nc % TK == 0 && V % 128 == 0 && lddy % 8 == 0 && ldw % 8 == 0 && (uintptr_t)dY % 16 == 0 &&
+         (uintptr_t)Wd % 16 == 0 && (uintptr_t)dz % 8 == 0 && (uintptr_t)hv % 4 == 0 &&
+         (!dYt || ((uintptr_t)dYt % 16 == 0 && lddyt % 8 == 0));
+}
+
+hipError_t launch_sddmm_venom_dma(const void* dY, int64_t lddy, const void* Wd, int64_t ldw, int64_t Tn, int64_t F,
+                                  int64_t Nc, int V, int M, const void* hv, const uint8_t* hm, const uint8_t* hc,
+                                  int relu, float* dz, void* dYt, int64_t lddyt, hipStream_t s) {
+  const int64_t Kg = F / M * 4;   // gathered columns
+  if (dYt)
+    return run_sddmm_dma<128, 512, 2, 4, 2, true, SD_VNM>(dY, lddy, Wd, ldw, Tn, Kg, Nc, hm, dz, dYt, lddyt, s, hc, V,
+                                                           M, hv, relu, 0);
+  return run_sddmm_dma<128, 512, 2, 4, 2, false, SD_VNM>(dY, lddy, Wd, ldw, Tn, Kg, Nc, hm, dz, nullptr, 0, s, hc, V,
+                                                          M, hv, relu, 0);
+}
+
+// Dense NT GEMM out[r][c] = sum_t A[r][t] B[c][t] (fp32 out, row stride ldo), bf16 operands.
+bool dense_nt_fast_ok(const void* A, int64_t lda, const void* B, int64_t ldb, const float* out, int64_t ldo,
+                      int64_t Tn) {
+  return Tn % TK == 0 && lda % 8 == 0 && ldb % 8 == 0 && ldo % 4 == 0 && (uintptr_t)A % 16 == 0 &&
+         (uintptr_t)B % 16 == 0 && (uintptr_t)out % 16 == 0;
+}
+
+hipError_t launch_dense_nt(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t R, int64_t Kc, int64_t Tn,
+                           float* out, int64_t ldo, hipStream_t s) {
+  return run_sddmm_dma<256, 256, 4, 2, 2, false, SD_DENSE>(A, lda, B, ldb, R, Kc, Tn, nullptr, out, nullptr, 0, s,
+                                                           nullptr, 1, 4, nullptr, 0, ldo);
 }
 
 }  // namespace nms

@@ -42,6 +42,9 @@ _SIGNATURES = {
     "spmm_nm_t_relu_venom": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp],
     "spmm_nm_general": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp],
     "spmm_nm_general_noalloc": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
+    "sddmm_venom": [_int, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _vp, _vp, _i64,
+                    _vp],
+    "spmm_venom_tn": [_int, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp],
     "nm_transpose": [_int, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "prune_act_venom": [_int, _vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _i64, _vp],
     "spmm_venom": [_int, _vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp],
@@ -80,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.nm_sizes.restype = None
         L.nm_general_work_bytes.argtypes = [_int, _i64, _i64, _int, _int]
         L.nm_general_work_bytes.restype = _i64
+        L.nm_venom_tn_work_bytes.argtypes = [_int, _i64, _i64]
+        L.nm_venom_tn_work_bytes.restype = _i64
         L.nm_general_scratch_bytes.argtypes = []
         L.nm_general_scratch_bytes.restype = _i64
         L.nm_status_str.argtypes = [_int]
@@ -373,6 +378,65 @@ def spmm_nm_general_noalloc(values: torch.Tensor, meta: torch.Tensor, K: int, N:
         raise ValueError("Bt must have K columns and out must be an fp32 [R, Nc] tensor")
     _check(lib().spmm_nm_general_noalloc(_dt(Bt), _p(values), _p(meta), R, K, N, M, _p(Bt), _rows(Bt, "Bt"), Nc,
                                          _p(out), _rows(out, "out"), _stream()), "spmm_nm_general_noalloc")
+    return out
+
+
+def sddmm_venom(dY: torch.Tensor, W_down: torch.Tensor, h_values: torch.Tensor, h_meta: torch.Tensor,
+                h_colsel: torch.Tensor, V: int, M: int = 8, apply_relu: bool = True, out=None, dYt=None):
+    """dZ [T, (F/M)*2] fp32: dY @ W_down^T at the entries the V:N:M activations h_s keep (times
+    ReLU's derivative when apply_relu).  With `dYt` (a [Nc, T] bf16 tensor) the call also writes
+    dY^T there and returns (out, dYt)."""
+    _dev(dY, W_down, h_values, h_meta, h_colsel, out, dYt)
+    _flat(h_values, "h_values"), _flat(h_meta, "h_meta"), _flat(h_colsel, "h_colsel")
+    if dY.dtype != W_down.dtype or h_values.dtype != dY.dtype:
+        raise TypeError("dY, W_down and h_values must share a dtype")
+    T, Nc = dY.shape
+    F = W_down.shape[0]
+    if W_down.shape[1] != Nc:
+        raise ValueError("W_down must have dY's number of columns")
+    if out is None:
+        out = torch.empty((T, F // M * 2), dtype=torch.float32, device=dY.device)
+    _flat(out, "out")
+    if dYt is not None and (tuple(dYt.shape) != (Nc, T) or dYt.dtype != dY.dtype):
+        raise ValueError("dYt must be [Nc, T] with dY's dtype")
+    _check(lib().sddmm_venom(_dt(dY), _p(dY), _rows(dY, "dY"), _p(W_down), _rows(W_down, "W_down"), T, F, Nc, V, M,
+                             _p(h_values), _p(h_meta), _p(h_colsel), int(bool(apply_relu)), _p(out), _p(dYt),
+                             _rows(dYt, "dYt") if dYt is not None else 0, _stream()), "sddmm_venom")
+    return (out, dYt) if dYt is not None else out
+
+
+def venom_tn_work_bytes(dtype: torch.dtype, T: int, F: int) -> int:
+    """Bytes of work memory spmm_venom_tn uses (0: none)."""
+    return int(lib().nm_venom_tn_work_bytes(NM_BF16 if dtype == torch.bfloat16 else NM_F32, T, F))
+
+
+def spmm_venom_tn(h_values: torch.Tensor, h_meta: torch.Tensor, h_colsel: torch.Tensor, F: int, V: int, M: int,
+                  dYt: torch.Tensor, out=None, work="auto") -> torch.Tensor:
+    """dW [F, Nc] fp32 = h_s^T @ dY for V:N:M activations h_s [T, F], given dYt = dY^T [Nc, T].
+    `work`: a uint8 device tensor, None, or "auto" (allocated with torch when the call uses it)."""
+    _dev(h_values, h_meta, h_colsel, dYt, out)
+    _flat(h_values, "h_values"), _flat(h_meta, "h_meta"), _flat(h_colsel, "h_colsel")
+    if h_values.dtype != dYt.dtype:
+        raise TypeError("h_values and dYt must share a dtype")
+    T = h_values.shape[0]
+    Nc = dYt.shape[0]
+    if dYt.shape[1] != T:
+        raise ValueError("dYt must be [Nc, T]")
+    if out is None:
+        out = torch.empty((F, Nc), dtype=torch.float32, device=dYt.device)
+    if isinstance(work, str):
+        if work != "auto":
+            raise ValueError("work must be a tensor, None or 'auto'")
+        nbytes = venom_tn_work_bytes(h_values.dtype, T, F)
+        work = torch.empty(nbytes, dtype=torch.uint8, device=dYt.device) if nbytes else None
+    if work is not None:
+        _dev(work)
+        _flat(work, "work")
+    _check(lib().spmm_venom_tn(_dt(dYt), _p(h_values), _p(h_meta), _p(h_colsel), T, F, V, M, _p(dYt),
+                               _rows(dYt, "dYt"), Nc, _p(out), _rows(out, "out"),
+                               _p(work) if work is not None else None,
+                               work.numel() * work.element_size() if work is not None else 0, _stream()),
+           "spmm_venom_tn")
     return out
 
 

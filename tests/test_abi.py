@@ -25,7 +25,8 @@ def test_exports_every_header_function(L):
 
 def test_binding_covers_header():
     assert set(nm._SIGNATURES) | {"nm_sizes", "nm_status_str", "nm_last_hip_error", "nm_version",
-                                  "nm_general_work_bytes", "nm_general_scratch_bytes"} == set(nm.header_functions())
+                                  "nm_general_work_bytes", "nm_general_scratch_bytes",
+                                  "nm_venom_tn_work_bytes"} == set(nm.header_functions())
 
 
 def test_status_strings(L):
@@ -120,6 +121,28 @@ def test_lowrank_general_fused_errors(L):
     assert L.nm_general_work_bytes(1, 8, 64, 2, 8) == 8 * 32 * 2 + 8 * 8
     assert L.nm_general_work_bytes(0, 8, 64, 1, 4) == 8 * 32 * 4 + 8 * 8
     assert L.nm_general_work_bytes(1, 8, 64, 3, 8) == 0
+    # sddmm_venom(dt, dY, lddy, Wd, ldw, T, F, Nc, V, M, hv, hm, hc, relu, dz, dYt, lddyt, stream)
+    assert L.sddmm_venom(1, None, 8, FAKE, 8, 128, 64, 8, 128, 8, FAKE, FAKE, FAKE, 1, FAKE, None, 0, s) == \
+        nm.NM_ERR_NULL
+    assert L.sddmm_venom(1, FAKE, 8, FAKE, 8, 128, 64, 8, 128, 6, FAKE, FAKE, FAKE, 1, FAKE, None, 0, s) == \
+        nm.NM_ERR_UNSUPPORTED
+    assert L.sddmm_venom(0, FAKE, 8, FAKE, 8, 128, 64, 8, 128, 8, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 128, s) == \
+        nm.NM_ERR_UNSUPPORTED                                  # dY^T only in bf16
+    assert L.sddmm_venom(1, FAKE, 8, FAKE, 8, 100, 64, 8, 128, 8, FAKE, FAKE, FAKE, 1, FAKE, None, 0, s) == \
+        nm.NM_ERR_SHAPE                                        # T % V
+    assert L.sddmm_venom(1, FAKE, 8, FAKE, 8, 128, 64, 8, 128, 8, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 64, s) == \
+        nm.NM_ERR_SHAPE                                        # lddyt < T
+    assert L.sddmm_venom(1, FAKE + 2, 8, FAKE, 8, 128, 64, 8, 128, 8, FAKE, FAKE, FAKE, 1, FAKE + 4, None, 0, s) == \
+        nm.NM_ERR_ALIGN                                        # dz not 8-byte aligned
+    # spmm_venom_tn(dt, hv, hm, hc, T, F, V, M, dYt, lddyt, Nc, dW, lddw, work, work_bytes, stream)
+    assert L.spmm_venom_tn(1, FAKE, FAKE, None, 128, 64, 128, 8, FAKE, 128, 8, FAKE, 8, None, 0, s) == \
+        nm.NM_ERR_NULL
+    assert L.spmm_venom_tn(1, FAKE, FAKE, FAKE, 128, 60, 128, 8, FAKE, 128, 8, FAKE, 8, None, 0, s) == \
+        nm.NM_ERR_SHAPE                                        # F % M
+    assert L.spmm_venom_tn(1, FAKE, FAKE, FAKE, 128, 64, 128, 8, FAKE, 128, 8, FAKE, 8, None, -1, s) == \
+        nm.NM_ERR_SHAPE
+    assert L.nm_venom_tn_work_bytes(1, 8192, 16384) == 8192 * 16384 * 2
+    assert L.nm_venom_tn_work_bytes(0, 64, 64) == 0
     # spmm_nm_general_noalloc(dt, values, meta, R, K, N, M, Bt, ldbt, Nc, C, ldc, stream)
     assert L.nm_general_scratch_bytes() == 64 << 20
     assert L.spmm_nm_general_noalloc(1, None, FAKE, 8, 16, 2, 8, FAKE, 16, 8, FAKE, 8, s) == nm.NM_ERR_NULL
