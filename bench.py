@@ -25,8 +25,9 @@ and the fp64 CPU oracle timed on the host (rank 0, N = 1 only).
 Without --workload the headline is the 2:4 up-projection, and `configs` adds
 the same measurement (step time, dense-equivalent TFLOP/s, share of the bf16
 peak, per-kernel times, roofline of the dominant kernel, oracle sample) for the
-small fp32 case, the V:N:M down-projection, the double-pruned training step and
-the ReLU V:N:M step.
+small fp32 case, the V:N:M down-projection, the double-pruned training step,
+the ReLU V:N:M step and that step's backward (dZ at the kept activations and
+dW_down).
 
 Warm-up: the W untimed steps are repeated until at least one second of them
 has run, so that the timed steps see settled GPU clocks.  `cold` reports, beside
@@ -56,7 +57,8 @@ METRIC = "dense-equivalent TFLOP/s of 2:4 & V:N:M SpMM at FFN shapes; % of bf16 
 HEADLINE = "ffn_up_nm24_8192x2048x4096"
 # the other workloads of the metric, measured beside the headline in a default run
 CONFIGS = ["nm24_fp32_256x512x128", "ffn_down_vnm64_2_8_2048x8192x4096",
-           "train_step_nm24_dmodel4096_dff16384_tok8192", "relu_act_vnm128_2_8_8192x16384x4096"]
+           "train_step_nm24_dmodel4096_dff16384_tok8192", "relu_act_vnm128_2_8_8192x16384x4096",
+           "relu_act_vnm128_bwd_8192x16384x4096"]
 
 
 def _parse():
@@ -256,6 +258,32 @@ def _w_venom(w, relu):
     return steps, flops, algo, "spmm_venom"
 
 
+def _w_venom_bwd(w):
+    """Backward of the ReLU V:N:M down-projection: dZ at the kept activations (and dY^T), then
+    dW_down = h_s^T dY.  h_s comes from the forward's prune (not timed)."""
+    import torch
+    import sparse_matmul_ffns_amd as nm
+    from sparse_matmul_ffns_amd import synth
+    T, F, Nc, V, M = w["R"], w["K"], w["Nc"], w["V"], w["M"]
+    Z = _dev(synth.normal((T, F), w["Z"]["seed"], w["Z"]["mean"], w["Z"]["std"]))
+    Wd = _dev(synth.normal((F, Nc), w["W"]["seed"], w["W"]["mean"], w["W"]["std"]))
+    dY = _dev(synth.normal((T, Nc), w["dY"]["seed"], w["dY"]["mean"], w["dY"]["std"]))
+    hv, hm, hc = nm.prune_act_venom(Z, V, M, apply_relu=True)
+    del Z
+    dz = torch.empty((T, F // M * 2), dtype=torch.float32, device="cuda")
+    dYt = torch.empty((Nc, T), dtype=dY.dtype, device="cuda")
+    dW = torch.empty((F, Nc), dtype=torch.float32, device="cuda")
+    work = torch.empty(nm.venom_tn_work_bytes(dY.dtype, T, F), dtype=torch.uint8, device="cuda")
+    steps = [
+        ("sddmm_venom", lambda: nm.sddmm_venom(dY, Wd, hv, hm, hc, V, M, apply_relu=True, out=dz, dYt=dYt)),
+        ("spmm_venom_tn", lambda: nm.spmm_venom_tn(hv, hm, hc, F, V, M, dYt, out=dW, work=work)),
+    ]
+    g = 2.0 * T * F * Nc
+    flops = {"sddmm_venom": g, "spmm_venom_tn": g}
+    algo = {"sddmm_venom": ("mfma", g / M * 4), "spmm_venom_tn": ("mfma", g)}
+    return steps, flops, algo, "spmm_venom_tn"
+
+
 def _w_train(w):
     import torch
     import sparse_matmul_ffns_amd as nm
@@ -305,6 +333,8 @@ def build_workload(name):
         return _w_venom(w, relu=False)
     if w["kind"] == "act_venom":
         return _w_venom(w, relu=True)
+    if w["kind"] == "act_venom_bwd":
+        return _w_venom_bwd(w)
     return _w_train(w)
 
 
@@ -371,6 +401,21 @@ def cpu_baseline(name):
         fl = 2.0 * R * K * Nc
         sample = (f"whole workload, one step: prune + compress of the [{R}x{K}] weight, fp64 decompress-and-dgemm "
                   f"with the [{K}x{Nc}] operand plus the rank-{r} adapter")
+    elif w["kind"] == "act_venom_bwd":
+        # one V-block of tokens through both backward products (the oracle's own V:N:M prune of
+        # that block of activations first)
+        T, F, Nc, V, M = w["R"], w["K"], w["Nc"], w["V"], w["M"]
+        Z = synth.normal((V, F), w["Z"]["seed"], w["Z"]["mean"], w["Z"]["std"])
+        Wd = synth.normal((F, Nc), w["W"]["seed"], w["W"]["mean"], w["W"]["std"])
+        dY = synth.normal((V, Nc), w["dY"]["seed"], w["dY"]["mean"], w["dY"]["std"])
+        hv, hm, hc, _, _ = O.prune_venom(Z, "bf16", V, M, True)
+        t0 = time.perf_counter()
+        O.sddmm_venom(dY, Wd, hv, hm, hc, V, F, V, M, "bf16", True)
+        O.spmm_venom_tn(hv, hm, hc, V, F, V, M, dY, "bf16")
+        dt = time.perf_counter() - t0
+        fl = 2 * 2.0 * V * F * Nc
+        sample = (f"{V} of {T} tokens (one V-block, pruned by the oracle first, not timed): dZ at the kept "
+                  f"activations and dW_down's share of that block, fp64")
     elif w["kind"] == "train_step":
         # a slice of the d_ff rows of the layer (whole 2:4 groups of W_s^T): W's prune + compress,
         # Y for those rows, the re-pruned transpose of the slice and its share of dX, dW at the

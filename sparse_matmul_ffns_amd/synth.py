@@ -108,4 +108,9 @@ WORKLOADS = {
     "relu_act_vnm128_2_8_8192x16384x4096": dict(
         kind="act_venom", dtype="bf16", R=8192, K=16384, Nc=4096, V=128, M=8,
         Z=dict(seed=5000, mean=-0.5, std=1.0), W=dict(seed=5001, mean=0.0, std=0.02)),
+    # the backward of the down-projection above: the same activations and weight, and dY [T x Nc]
+    "relu_act_vnm128_bwd_8192x16384x4096": dict(
+        kind="act_venom_bwd", dtype="bf16", R=8192, K=16384, Nc=4096, V=128, M=8,
+        Z=dict(seed=5000, mean=-0.5, std=1.0), W=dict(seed=5001, mean=0.0, std=0.02),
+        dY=dict(seed=5002, mean=0.0, std=1.0)),
 }

@@ -22,7 +22,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_configs_cover_the_metric_workloads():
     names = [bench.HEADLINE] + bench.CONFIGS
-    assert len(set(names)) == 5
+    assert len(set(names)) == 6
     assert all(n in synth.WORKLOADS for n in names)
     kinds = {synth.WORKLOADS[n]["kind"] for n in names}
     assert {"spmm_nm", "spmm_venom", "train_step", "act_venom"} <= kinds

@@ -4,9 +4,8 @@ instantiations and launch grids run).
 
 Selection results (masks, compressed values, metadata, column selections,
 re-pruned transposes) are compared bit for bit with the fp64 oracle over the
-whole matrix, except for the activation prune of the [8192 x 16384] ReLU
-workload, where the oracle prunes a handful of 128-row blocks (blocks are
-independent, so each checked block is exact).  Matmul outputs are checked on
+whole matrix (the [8192 x 16384] activation prune included: the oracle prunes
+it once and the forward and backward tests share the result).  Matmul outputs are checked on
 sampled rows (and, where the oracle's dense operand fits, sampled columns):
 the oracle computes those outputs one by one in fp64 from its own compressed
 operands and the seeded inputs, and the acceptance test is the usual one
@@ -193,31 +192,81 @@ def test_ffn_down_vnm64_full():
 # Z [8192 x 16384], W_down [16384 x 4096]
 # ---------------------------------------------------------------------------
 
+_ORACLE_CACHE = {}
+
+
+def _oracle_relu_prune(w):
+    """The oracle's ReLU + V:N:M prune of the workload's whole activation matrix (computed once)."""
+    key = (w["Z"]["seed"], w["R"], w["K"], w["V"], w["M"])
+    if key not in _ORACLE_CACHE:
+        Z = _gen(w["Z"], (w["R"], w["K"]))
+        wv, wm, wc, _, _ = O.prune_venom(Z, "bf16", w["V"], w["M"], True)
+        _ORACLE_CACHE[key] = (Z, wv, wm, wc)
+    return _ORACLE_CACHE[key]
+
+
 def test_relu_act_vnm128_full():
+    """The activation prune over the whole [8192 x 16384] matrix, bit for bit (all 64 V-blocks);
+    the down-projection on sampled rows of sampled blocks."""
     w = synth.WORKLOADS["relu_act_vnm128_2_8_8192x16384x4096"]
     R, K, Nc, V, M = w["R"], w["K"], w["Nc"], w["V"], w["M"]
-    Z, Wdn = _gen(w["Z"], (R, K)), _gen(w["W"], (K, Nc))
+    Z, wv, wm, wc = _oracle_relu_prune(w)
+    Wdn = _gen(w["W"], (K, Nc))
     Zd, Wdd = dev(Z, "bf16"), dev(Wdn, "bf16")
 
     vals, meta, colsel = nm.prune_act_venom(Zd, V, M, apply_relu=True)
     C = nm.spmm_venom(vals, meta, colsel, K, V, M, Wdd)
     _finite(C, "spmm_venom")
-    gv, gm, gc = host(vals), host(meta), host(colsel)
+    assert np.array_equal(host(colsel), wc), "colsel"
+    assert host(vals).tobytes() == wv.tobytes(), "values"
+    assert np.array_equal(host(meta), wm), "metadata"
     del vals, meta, colsel, Zd
 
-    # the oracle prunes whole V-row blocks: first, last and four more
     rng = np.random.default_rng(31)
-    blocks = sorted({0, R // V - 1} | set(rng.choice(R // V, 4, replace=False).tolist()))
     W64 = O.decode(Wdn, "bf16")
-    for b in blocks:
+    for b in sorted({0, R // V - 1} | set(rng.choice(R // V, 4, replace=False).tolist())):
         rs = slice(b * V, (b + 1) * V)
-        wv, wm, wc, _, _ = O.prune_venom(Z[rs], "bf16", V, M, True)
-        assert np.array_equal(gc[b:b + 1], wc), f"colsel of block {b}"
-        assert gv[rs].tobytes() == wv.tobytes(), f"values of block {b}"
-        assert np.array_equal(gm[rs], wm), f"metadata of block {b}"
-        A64 = O.decode(O.decompress_venom(wv, wm, wc, V, K, V, M), "bf16")
+        A64 = O.decode(O.decompress_venom(wv[rs], wm[rs], wc[b:b + 1], V, K, V, M), "bf16")
         rows = np.array(sorted({0, V - 1} | set(rng.choice(V, 6, replace=False).tolist())))
         _check_rows(C, A64[rows], W64, b * V + rows, f"relu_act block {b} spmm_venom")
+
+
+def test_relu_act_vnm128_bwd_full():
+    """The backward of the same down-projection at full size, from the oracle's own activations
+    (bit-identical to the GPU's, above): dZ on sampled tokens, dY^T over the whole matrix, dW_down
+    on sampled rows (every column)."""
+    w = synth.WORKLOADS["relu_act_vnm128_bwd_8192x16384x4096"]
+    T, F, Nc, V, M = w["R"], w["K"], w["Nc"], w["V"], w["M"]
+    Z, wv, wm, wc = _oracle_relu_prune(w)
+    Wd = _gen(w["W"], (F, Nc))
+    dY = _gen(w["dY"], (T, Nc))
+    hv, hm, hc = nm.prune_act_venom(dev(Z, "bf16"), V, M, apply_relu=True)
+    assert host(hv).tobytes() == wv.tobytes() and np.array_equal(host(hm), wm) and np.array_equal(host(hc), wc)
+    dYd = dev(dY, "bf16")
+    dz, dYt = nm.sddmm_venom(dYd, dev(Wd, "bf16"), hv, hm, hc, V, M, apply_relu=True,
+                             dYt=torch.empty((Nc, T), dtype=torch.bfloat16, device="cuda"))
+    dW = nm.spmm_venom_tn(hv, hm, hc, F, V, M, dYt)
+    _finite(dz, "sddmm_venom")
+    _finite(dW, "spmm_venom_tn")
+    assert np.array_equal(host(dYt), np.ascontiguousarray(dY.T)), "dY^T"
+    del hv, hm, hc, dYd
+
+    # dZ on sampled tokens: the oracle's SDDMM restricted to those rows (rows are independent)
+    toks = _sample(T, 24, 41, tile=128)
+    got = host(dz[torch.as_tensor(toks, device="cuda")])
+    ref = O.sddmm_venom(dY[toks], Wd, wv[toks], wm[toks], wc[toks // V], len(toks), F, 1, M, "bf16", True)
+    full = np.abs(O.decode(dY[toks], "bf16")) @ np.abs(O.decode(Wd, "bf16")).T
+    bound = np.take_along_axis(full, O.venom_kept_columns(wm[toks], wc[toks // V], len(toks), F, 1, M), axis=1)
+    check_close(got, ref, bound, "sddmm_venom sampled tokens")
+
+    # dW_down on sampled rows k: sum over every token of h_s[t][k] dY[t]
+    ks = _sample(F, 24, 42)
+    Hraw = O.decompress_venom(wv, wm, wc, T, F, V, M)
+    Hk = O.decode(np.ascontiguousarray(Hraw[:, ks]), "bf16")            # [T, len(ks)]
+    del Hraw
+    dY64 = O.decode(dY, "bf16")
+    got = host(dW[torch.as_tensor(ks, device="cuda")])
+    check_close(got, Hk.T @ dY64, O.abs_bound(np.abs(Hk.T), dY64), "spmm_venom_tn sampled rows")
 
 
 # ---------------------------------------------------------------------------
