@@ -336,6 +336,27 @@ nm_status spmm_nm_general_noalloc(nm_dtype dt, const void* values, const uint8_t
                                   int64_t K, int N, int M, const void* Bt, int64_t ldbt, int64_t Nc,
                                   float* C, int64_t ldc, nm_stream stream);
 
+/*
+ * nm_gmp_n_at -- host only: the N:M pattern a gradual magnitude pruning
+ * schedule has in effect at a training step ("Success story: ESPLAG",
+ * Highlights and Research Topic: semi-structured gradual magnitude pruning;
+ * "To 2:4 Sparsity and Beyond", abstract: sparse steps, then regular dense
+ * steps towards the end).  The pages give no schedule; the one implemented:
+ *   - dense (returns M) before t_begin and, when t_dense >= 0, from t_dense on;
+ *   - pruning events at t_begin + e*interval for e = 0 .. E-1,
+ *     E = (t_end - t_begin) / interval + 1;
+ *   - after event e the pattern is N_e : M with
+ *     N_e = M - ceil((M - n_final) * (e + 1) / E), falling linearly to n_final
+ *     at the last event and held until the dense switch.
+ * *prune_now (nullable) is set to 1 when `step` is a pruning event: the caller
+ * then magnitude-prunes its current weight to N_e:M (nm_prune_compress) and
+ * keeps the pruned entries at zero.  Returns -1 for invalid parameters
+ * (M not in {4, 8, 16}, n_final outside 1 .. M-1, t_begin < 0,
+ * t_end < t_begin, interval < 1).
+ */
+int nm_gmp_n_at(int M, int n_final, int64_t t_begin, int64_t t_end, int64_t interval,
+                int64_t t_dense, int64_t step, int* prune_now);
+
 /* Bytes of the fixed scratch buffer of spmm_nm_general_noalloc (host only). */
 int64_t nm_general_scratch_bytes(void);
 

@@ -470,6 +470,30 @@ def spmm_venom_tn_loop(h_values, h_meta, h_colsel, T, F, V, M, dY_raw, dtype):
 
 
 # ---------------------------------------------------------------------------
+# gradual magnitude pruning schedule  [ESPLAG Highlights, Research Topic
+# (semi-structured gradual magnitude pruning); 2:4+ abstract (sparse steps,
+# then regular dense steps towards the end)]
+#
+# Reading (the pages give no schedule): dense before the ramp; pruning events
+# every `interval` steps from t_begin through t_end; the kept count per group
+# falls linearly (the removed count rounded up) from M
+# to n_final over the events; the last pattern holds until the dense switch at
+# t_dense (none when t_dense < 0).
+# ---------------------------------------------------------------------------
+
+def gmp_n_at(M, n_final, t_begin, t_end, interval, t_dense, step):
+    """(N in effect at `step` -- M when dense --, whether `step` is a pruning event)."""
+    if step < t_begin or (t_dense >= 0 and step >= t_dense):
+        return M, False
+    event_steps = list(range(t_begin, t_end + 1, interval))
+    E = len(event_steps)
+    done = [s for s in event_steps if s <= step]                  # events so far, this one included
+    e = len(done) - 1
+    removed = -((-(M - n_final) * (e + 1)) // E)                  # ceil((M - n_final)(e + 1) / E)
+    return M - removed, step in event_steps
+
+
+# ---------------------------------------------------------------------------
 # sparse plus low-rank  [SLOPE abstract: low-rank adapters joined to the sparse
 # weight for the last iterations of pre-training, at little extra cost]
 # ---------------------------------------------------------------------------

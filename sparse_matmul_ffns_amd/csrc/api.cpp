@@ -181,6 +181,19 @@ int64_t nm_venom_tn_work_bytes(nm_dtype dt, int64_t T, int64_t F) {
   return nms::venom_tn_work_bytes(esize(dt), T, F);
 }
 
+int nm_gmp_n_at(int M, int n_final, int64_t t_begin, int64_t t_end, int64_t interval, int64_t t_dense, int64_t step,
+                int* prune_now) {
+  if (prune_now) *prune_now = 0;
+  if (!m_ok(M) || n_final < 1 || n_final >= M || t_begin < 0 || t_end < t_begin || interval < 1) return -1;
+  if (step < t_begin || (t_dense >= 0 && step >= t_dense)) return M;   // dense before the ramp and after the switch
+  const int64_t events = (t_end - t_begin) / interval + 1;           // at t_begin + e * interval
+  int64_t e = (step - t_begin) / interval;                             // the last event at or before step
+  if (e > events - 1) e = events - 1;
+  if (prune_now && (step - t_begin) % interval == 0 && (step - t_begin) / interval < events) *prune_now = 1;
+  const int64_t removed = ((int64_t)(M - n_final) * (e + 1) + events - 1) / events;   // ceil
+  return M - (int)removed;
+}
+
 int64_t nm_general_scratch_bytes(void) { return nms::GENERAL_SCRATCH_BYTES; }
 
 int64_t nm_general_work_bytes(nm_dtype dt, int64_t R, int64_t K, int N, int M) {

@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.nm_general_work_bytes.restype = _i64
         L.nm_venom_tn_work_bytes.argtypes = [_int, _i64, _i64]
         L.nm_venom_tn_work_bytes.restype = _i64
+        L.nm_gmp_n_at.argtypes = [_int, _int, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_int)]
+        L.nm_gmp_n_at.restype = _int
         L.nm_general_scratch_bytes.argtypes = []
         L.nm_general_scratch_bytes.restype = _i64
         L.nm_status_str.argtypes = [_int]

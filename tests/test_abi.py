@@ -26,7 +26,7 @@ def test_exports_every_header_function(L):
 def test_binding_covers_header():
     assert set(nm._SIGNATURES) | {"nm_sizes", "nm_status_str", "nm_last_hip_error", "nm_version",
                                   "nm_general_work_bytes", "nm_general_scratch_bytes",
-                                  "nm_venom_tn_work_bytes"} == set(nm.header_functions())
+                                  "nm_venom_tn_work_bytes", "nm_gmp_n_at"} == set(nm.header_functions())
 
 
 def test_status_strings(L):
@@ -173,3 +173,27 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         nm.spmm_nm(torch.zeros(4, 4, dtype=torch.bfloat16), torch.zeros(4, 1, dtype=torch.uint8), 8,
                    torch.zeros(8, 8, dtype=torch.bfloat16))
+
+
+# gradual pruning schedules worked by hand from the stated rule (events at t_begin + e*interval,
+# N_e = M - ceil((M - n_final)(e + 1)/E), dense before t_begin and from t_dense on)
+GMP_HAND = [
+    # (M, n_final, t_begin, t_end, interval, t_dense): [(step, N, pruning event)]
+    ((8, 2, 2, 8, 3, 12), [(0, 8, 0), (1, 8, 0), (2, 6, 1), (3, 6, 0), (4, 6, 0), (5, 4, 1), (6, 4, 0), (7, 4, 0),
+                           (8, 2, 1), (9, 2, 0), (11, 2, 0), (12, 8, 0), (40, 8, 0)]),
+    ((4, 2, 0, 0, 1, -1), [(0, 2, 1), (1, 2, 0), (1000, 2, 0)]),
+    ((16, 1, 10, 40, 10, 50), [(9, 16, 0), (10, 12, 1), (19, 12, 0), (20, 8, 1), (30, 4, 1), (39, 4, 0), (40, 1, 1),
+                               (45, 1, 0), (50, 16, 0)]),
+    ((8, 4, 0, 7, 4, -1), [(0, 6, 1), (3, 6, 0), (4, 4, 1), (7, 4, 0), (8, 4, 0)]),   # t_end between events
+]
+
+
+@pytest.mark.parametrize("params,table", GMP_HAND)
+def test_gmp_schedule_hand_worked(L, params, table):
+    for step, n, ev in table:
+        flag = ctypes.c_int(7)
+        assert L.nm_gmp_n_at(*params, step, ctypes.byref(flag)) == n, (params, step)
+        assert flag.value == ev, (params, step)
+    assert L.nm_gmp_n_at(8, 8, 0, 4, 1, -1, 0, None) == -1          # n_final must be < M
+    assert L.nm_gmp_n_at(8, 2, 5, 4, 1, -1, 0, None) == -1          # t_end < t_begin
+    assert L.nm_gmp_n_at(6, 2, 0, 4, 1, -1, 0, None) == -1          # M

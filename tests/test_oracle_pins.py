@@ -399,6 +399,24 @@ def test_sddmm_venom_relu_gate():
     assert np.array_equal(gated[pos], plain[pos]) and not gated[~pos].any()
 
 
+def test_gmp_schedule_hand_worked():
+    """The oracle's schedule against the hand-worked tables (the rule stated in its comment)."""
+    from tests.test_abi import GMP_HAND
+    for params, table in GMP_HAND:
+        for step, n, ev in table:
+            assert O.gmp_n_at(*params, step) == (n, bool(ev)), (params, step)
+
+
+def test_gmp_schedule_properties():
+    for M, nf in [(4, 2), (4, 1), (8, 2), (8, 6), (16, 1)]:
+        for begin, end, interval in [(0, 0, 1), (3, 20, 4), (5, 50, 7)]:
+            ns = [O.gmp_n_at(M, nf, begin, end, interval, end + 10, t)[0] for t in range(end + 12)]
+            sparse = ns[begin:end + 10]
+            assert all(a >= b for a, b in zip(sparse, sparse[1:]))          # monotone ramp
+            assert sparse[-1] == nf and max(sparse) < M                     # reaches the target; every event prunes
+            assert ns[:begin] == [M] * begin and ns[end + 10:] == [M] * 2   # dense before and after
+
+
 def test_abs_bound_hand_values():
     # |A| |B| by hand: [[1*1 + 2*2, 1*4 + 2*5], [0*1 + 3*2, 0*4 + 3*5]]
     A = np.array([[1.0, -2.0], [0.0, 3.0]])
