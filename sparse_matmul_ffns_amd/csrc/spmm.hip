@@ -103,6 +103,84 @@ __global__ __launch_bounds__(256) void spmm_generic_kernel(const T* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// fp32 path: v_mfma_f32_16x16x4f32 on the decompressed operand.  There is no
+// structured-sparse fp32 matrix instruction, so the 2:4 rows are expanded (two
+// kept values and two +0.0 per group) into LDS.  A workgroup owns a 16 x 16
+// tile of C and stages up to 256 k of A (16 rows) and B (16 columns) at once;
+// its four waves take interleaved 4-k steps (wave w: steps w, w+4, ...) with
+// one matrix instruction each, and wave 0 adds the four partial tiles in wave
+// order (a fixed summation order: the result does not depend on timing).
+// v_mfma_f32_16x16x4f32: lane l holds A[row l%16][k l/16] and B[k l/16][col
+// l%16]; the result holds column l%16, rows 4*(l/16) .. +3.
+// ---------------------------------------------------------------------------
+constexpr int F32_KC = 256;   // k staged per chunk (38 KB of LDS)
+
+__global__ __launch_bounds__(256) void spmm_f32_mfma_kernel(const float* __restrict__ values,
+                                                            const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+                                                            const float* __restrict__ B, int64_t sbk, int64_t sbn,
+                                                            int64_t Nc, float* __restrict__ C, int64_t ldc) {
+  __shared__ float As[16][F32_KC + 4];
+  __shared__ float Bs[F32_KC][16 + 1];
+  __shared__ f32x4 part[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = (int64_t)blockIdx.y * 16, n0 = (int64_t)blockIdx.x * 16;
+  const int64_t G = K / 4, vrow = K / 2, mrow = (G + 1) / 2;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t k0 = 0; k0 < K; k0 += F32_KC) {
+    const int kc = (int)((K - k0) < F32_KC ? (K - k0) : F32_KC);   // a multiple of 4
+    // A: one (row, group) unit per thread and pass: both kept values and the two zeros
+    for (int u = tid; u < 16 * (kc / 4); u += 256) {
+      const int r = u / (kc / 4), gi = u % (kc / 4);
+      const int64_t row = m0 + r, g = k0 / 4 + gi;
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+      if (row < R) {
+        const uint32_t nib = (meta[row * mrow + g / 2] >> (4 * (g & 1))) & 0xF;
+        a4[nib & 3] = values[row * vrow + 2 * g];
+        a4[(nib >> 2) & 3] = values[row * vrow + 2 * g + 1];
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) As[r][4 * gi + p] = a4[p];
+    }
+    for (int i = tid; i < 16 * kc; i += 256) {
+      const int kk = i / 16, nn = i % 16;
+      const int64_t n = n0 + nn;
+      Bs[kk][nn] = n < Nc ? B[(k0 + kk) * sbk + n * sbn] : 0.f;
+    }
+    __syncthreads();
+    for (int st = wave; st < kc / 4; st += 4) {
+      const int k = 4 * st + (lane >> 4);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(As[lane & 15][k], Bs[k][lane & 15], acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 sum = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const f32x4 o = part[w][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[e] += o[e];
+    }
+    const int64_t col = n0 + (lane & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t row = m0 + 4 * (lane >> 4) + e;
+      if (row < R && col < Nc) C[row * ldc + col] = sum[e];
+    }
+  }
+}
+
+static hipError_t run_f32_mfma(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* B,
+                               int64_t sbk, int64_t sbn, int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
+  const dim3 grid((unsigned)((Nc + 15) / 16), (unsigned)((R + 15) / 16));
+  hipLaunchKernelGGL(spmm_f32_mfma_kernel, grid, dim3(256), 0, s, (const float*)values, meta, R, K, (const float*)B,
+                     sbk, sbn, Nc, C, ldc);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // fast path: bf16, v_smfmac_f32_16x16x64_bf16
 // ---------------------------------------------------------------------------
 constexpr int SK = 64;          // dense k (2:4 domain) per k-step
@@ -363,6 +441,7 @@ hipError_t launch_spmm_nm(int dt, const void* values, const uint8_t* meta, int64
     return launch_spmm_nm_dma(values, meta, R, K, B, ldb, Nc, C, ldc, s);
   if (dt == DT_BF16 && !force_generic() && fast_ok(values, meta, B, ldb, Nc, C, ldc, K))
     return run_smfmac<256, 128, 128, 64, false>(values, meta, nullptr, R, K, 4, 4, K / 4, B, ldb, Nc, C, ldc, s);
+  if (dt == DT_F32 && !force_generic()) return run_f32_mfma(values, meta, R, K, B, ldb, 1, Nc, C, ldc, s);
   return dt == DT_BF16 ? run_generic<uint16_t, false>(values, meta, nullptr, R, K, 4, 4, B, ldb, 1, Nc, C, ldc, s)
                        : run_generic<uint32_t, false>(values, meta, nullptr, R, K, 4, 4, B, ldb, 1, Nc, C, ldc, s);
 }
@@ -371,6 +450,7 @@ hipError_t launch_spmm_nm_t(int dt, const void* values, const uint8_t* meta, int
                             int64_t ldbt, int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
   if (dt == DT_BF16 && !force_generic() && spmm_nt_ok(values, meta, Bt, ldbt, R, Nc, K))
     return launch_spmm_nm_nt_dma(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
+  if (dt == DT_F32 && !force_generic()) return run_f32_mfma(values, meta, R, K, Bt, 1, ldbt, Nc, C, ldc, s);
   return dt == DT_BF16 ? run_generic<uint16_t, false>(values, meta, nullptr, R, K, 4, 4, Bt, 1, ldbt, Nc, C, ldc, s)
                        : run_generic<uint32_t, false>(values, meta, nullptr, R, K, 4, 4, Bt, 1, ldbt, Nc, C, ldc, s);
 }
