@@ -457,13 +457,39 @@ def cpu_baseline(name):
 # counters recorded with rocprofv3 (profiles/), valid while the kernel source is unchanged
 # ---------------------------------------------------------------------------
 
+# the kernel sources behind each step name whose counters are recorded: the file of the kernel and
+# of the launch routine that picks it (besides the files every kernel shares)
+KERNEL_SOURCES = {
+    "spmm_nm_t": ["spmm_nt.hip", "spmm.hip"],
+    "spmm_nm_t_fwd": ["spmm_nt.hip", "spmm.hip"],
+    "spmm_nm_t_dx": ["spmm_nt.hip", "spmm.hip"],
+    "spmm_nm_t_up": ["spmm_nt.hip", "spmm.hip"],
+    "spmm_nm_t_lowrank": ["spmm_nt.hip", "lowrank.hip"],
+    "spmm_nm_t_relu_venom": ["spmm_nt.hip"],
+    "spmm_nm_general": ["general.hip", "spmm_nt.hip", "spmm.hip"],
+    "spmm_nm": ["spmm.hip", "spmm_dma.hip"],
+    "spmm_venom": ["spmm.hip", "spmm_vnm.hip", "spmm_dma.hip"],
+    "spmm_venom_down": ["spmm.hip", "spmm_vnm.hip", "spmm_dma.hip"],
+    "sddmm_nm_dt": ["sddmm.hip"],
+    "sddmm_venom": ["sddmm.hip", "venom_bwd.hip"],
+    "spmm_venom_tn": ["sddmm.hip", "venom_bwd.hip"],
+    "prune_act_venom": ["venom.hip"],
+    "nm_reprune_t": ["reprune.hip"],
+}
+SHARED_SOURCES = ["api.cpp", "common.hpp", "dma.hpp", "launch.hpp", "prep_bodies.hpp"]
+
+
 def _src_hash(kernel=None):
-    """Hash of every source file of the library (kernels, headers, C ABI) and of the build flags:
-    recorded counters describe the code built from exactly these."""
+    """Hash of the sources a kernel is built from (its own file and its launch routine, the shared
+    headers, the C ABI, the public header) and of the build flags: recorded counters describe the
+    code built from exactly these.  Without a kernel (or for one not listed), every source file."""
     from sparse_matmul_ffns_amd import build
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_matmul_ffns_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    names = sorted(os.listdir(csrc))
+    if kernel in KERNEL_SOURCES:
+        names = sorted(set(KERNEL_SOURCES[kernel]) | set(SHARED_SOURCES))
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     with open(os.path.join(ROOT, "include", "nmsparse.h"), "rb") as f:

@@ -35,6 +35,20 @@ def test_source_hash_is_stable_and_path_free():
     assert build.ROOT not in " ".join(build.FLAGS).replace(build.ROOT, "<repo>")
 
 
+def test_kernel_source_sets():
+    """Every file named for a kernel's counters exists, every quoted include of those files is in
+    the set, and the per-kernel hashes differ from the whole-tree hash."""
+    import re
+    csrc = os.path.join(ROOT, "sparse_matmul_ffns_amd", "csrc")
+    for kernel, files in bench.KERNEL_SOURCES.items():
+        names = set(files) | set(bench.SHARED_SOURCES)
+        for name in names:
+            assert os.path.exists(os.path.join(csrc, name)), (kernel, name)
+            for inc in re.findall(r'#include "([^"]+)"', open(os.path.join(csrc, name)).read()):
+                assert inc in names or inc.endswith("include/nmsparse.h"), (kernel, name, inc)
+        assert bench._src_hash(kernel) != bench._src_hash()
+
+
 def test_cpu_baseline_small_case():
     r = bench.cpu_baseline("nm24_fp32_256x512x128")
     assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
