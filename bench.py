@@ -466,7 +466,7 @@ KERNEL_SOURCES = {
     "spmm_nm_t_up": ["spmm_nt.hip", "spmm.hip"],
     "spmm_nm_t_lowrank": ["spmm_nt.hip", "lowrank.hip"],
     "spmm_nm_t_relu_venom": ["spmm_nt.hip"],
-    "spmm_nm_general": ["general.hip", "spmm_nt.hip", "spmm.hip"],
+    "spmm_nm_general": ["general.hip", "spmm_nt.hip", "spmm.hip", "sddmm.hip"],
     "spmm_nm": ["spmm.hip", "spmm_dma.hip"],
     "spmm_venom": ["spmm.hip", "spmm_vnm.hip", "spmm_dma.hip"],
     "spmm_venom_down": ["spmm.hip", "spmm_vnm.hip", "spmm_dma.hip"],

@@ -258,8 +258,11 @@ nm_status spmm_nm_t_relu_venom(nm_dtype dt, const void* values, const uint8_t* m
  * 4 columns holds at most two survivors: with work of at least
  * nm_general_work_bytes(dt, R, K, N, M) bytes the matrix is rewritten there
  * in 2:4 form (runs padded with +0.0) and spmm_nm_t computes the product; 2:4
- * itself goes to spmm_nm_t directly.  Other patterns, and N <= 2 without
- * enough work memory, take a plain SIMT kernel.  Errors as for spmm_nm_t, plus
+ * itself goes to spmm_nm_t directly.  With N > 2 (bf16, K % 64 == 0, ldbt % 8
+ * == 0, ldc % 4 == 0, 16-byte aligned Bt and C) the work memory receives the
+ * matrix as dense bf16 rows [R][K] and a dense matrix-core GEMM computes the
+ * product.  Other calls, and any without enough work memory, take a plain SIMT
+ * kernel.  Errors as for spmm_nm_t, plus
  * NM_ERR_UNSUPPORTED for an N:M outside the set above and NM_ERR_SHAPE for
  * K % M != 0 or work_bytes < 0.
  */
@@ -320,8 +323,8 @@ int64_t nm_venom_tn_work_bytes(nm_dtype dt, int64_t T, int64_t F);
 /*
  * spmm_nm_general_noalloc -- spmm_nm_general for callers that cannot allocate
  * device memory (code under stream capture, tight serving loops, harnesses that
- * forbid allocation): the same product and kernels, with the 2:4 rewrite held
- * in a fixed 64 MiB scratch buffer that the library keeps in each GPU's memory
+ * forbid allocation): the same product and kernels, with the work memory (the
+ * 2:4 rewrite or the dense rows) held in a fixed 64 MiB scratch buffer that the library keeps in each GPU's memory
  * for the life of the process (nm_general_scratch_bytes() gives the size).
  * The call allocates nothing and takes no work argument; the caller still
  * passes inputs and outputs as for spmm_nm_general.  Every call on one GPU

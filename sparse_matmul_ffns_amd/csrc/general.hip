@@ -5,8 +5,11 @@
 // When N <= 2 every aligned run of 4 columns holds at most two survivors, so the matrix is also a
 // 2:4 matrix once each run is padded to two slots with +0.0: nm_to24_kernel rewrites the compressed
 // form that way (into caller memory) and the 2:4 SMFMAC SpMM does the product at the 2:4 rate.
-// Other patterns (and calls without that memory) take a plain SIMT kernel that decodes the
-// position stream directly.
+// With N > 2 a run can hold three or four survivors, which no structured-sparse matrix instruction
+// takes; at those densities (3:4, 4:8, 6:8, ...) the matrix is expanded to dense bf16 rows in
+// caller memory (nm_expand_kernel) and multiplied by the dense NT GEMM of the SDDMM
+// (v_mfma_f32_32x32x16_bf16).  Other calls (fp32, or no work memory) take a plain SIMT kernel
+// that decodes the position stream directly.
 #include <mutex>
 
 #include "common.hpp"
@@ -80,6 +83,51 @@ __global__ __launch_bounds__(256) void nm_to24_kernel(const T* __restrict__ valu
   m24[(int64_t)row * tpr + t] = (uint8_t)byte;
 }
 
+// Dense bf16 rows of an N:M compressed matrix (the SpMM's own copy, row stride K): one thread per
+// (row, group) reads the group's N values and N * log2(M) metadata bits, places each value at its
+// position (a later survivor overwrites an earlier one at the same position, as nm_decompress
+// does) and writes the group's M elements with one 8-, 16- or 32-byte store, so a wave's stores
+// cover whole lines.  The group is held as M/4 64-bit words indexed by constant expressions.
+template <int M>
+__global__ __launch_bounds__(256) void nm_expand_kernel(const uint16_t* __restrict__ values,
+                                                        const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+                                                        int N, uint16_t* __restrict__ out) {
+  constexpr int b = M == 4 ? 2 : M == 8 ? 3 : 4;
+  constexpr int W = M / 4;   // 64-bit words of a group
+  const int64_t G = K / M;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= R * G) return;
+  const int64_t r = u / G, g = u - r * G;
+  const uint8_t* mr = meta + r * ((G * N * b + 7) / 8);
+  const int64_t bit0 = g * N * b;
+  const int sh = (int)(bit0 & 7);
+  const int nb = (sh + N * b + 7) >> 3;   // at most 8 (N * b <= 60 and sh + N * b <= 64)
+  uint64_t bits = 0;
+  for (int i = 0; i < nb; ++i) bits |= (uint64_t)mr[(bit0 >> 3) + i] << (8 * i);
+  bits >>= sh;
+  const uint16_t* v = values + r * G * N + g * N;
+  uint64_t w[W];
+#pragma unroll
+  for (int q = 0; q < W; ++q) w[q] = 0;
+  for (int s = 0; s < N; ++s) {
+    const uint32_t p = (uint32_t)(bits >> (s * b)) & (uint32_t)(M - 1);
+    const uint32_t sft = 16 * (p & 3);
+    const uint64_t put = (uint64_t)v[s] << sft, clr = ~((uint64_t)0xFFFF << sft);
+#pragma unroll
+    for (int q = 0; q < W; ++q)
+      if ((p >> 2) == (uint32_t)q) w[q] = (w[q] & clr) | put;
+  }
+  uint16_t* o = out + r * K + g * M;
+  if constexpr (W == 1) {
+    *reinterpret_cast<uint64_t*>(o) = w[0];
+  } else {
+#pragma unroll
+    for (int q = 0; q < W; q += 2)
+      reinterpret_cast<u32x4*>(o)[q / 2] =
+          u32x4{(uint32_t)w[q], (uint32_t)(w[q] >> 32), (uint32_t)w[q + 1], (uint32_t)(w[q + 1] >> 32)};
+  }
+}
+
 // Plain SIMT product for any N:M (64 x 64 tiles, 32-k chunks staged densely in LDS): the kept
 // values of each (row, group) are scattered to their dense columns by the decoded positions.
 template <typename T>
@@ -141,10 +189,12 @@ __global__ __launch_bounds__(256) void spmm_general_generic_kernel(const T* __re
   }
 }
 
-// Bytes of caller memory the 2:4 route needs (values [R][K/2], then metadata [R][ceil(K/8)] at the
-// next 16-byte boundary); 0 when the pattern does not take that route.
+// Bytes of caller memory a route needs: the 2:4 rewrite (N <= 2: values [R][K/2], then metadata
+// [R][ceil(K/8)] at the next 16-byte boundary) or the dense bf16 rows (N > 2, bf16, K % 64 == 0:
+// [R][K]); 0 when the pattern takes neither.
 int64_t general_work_bytes(int esz, int64_t R, int64_t K, int N, int M) {
-  if (N > 2 || (N == 2 && M == 4)) return 0;
+  if (N == 2 && M == 4) return 0;
+  if (N > 2) return esz == 2 && K % 64 == 0 ? R * K * 2 : 0;
   const int64_t vbytes = (R * (K / 2) * esz + 15) / 16 * 16;
   return vbytes + R * ((K + 7) / 8);
 }
@@ -155,8 +205,23 @@ hipError_t launch_spmm_nm_general(int dt, const void* values, const uint8_t* met
   if (N == 2 && M == 4) return launch_spmm_nm_t(dt, values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
   const int esz = dt == DT_BF16 ? 2 : 4;
   const int64_t need = general_work_bytes(esz, R, K, N, M);
-  if (need > 0 && work && work_bytes >= need && (uintptr_t)work % 16 == 0 && R * ((K + 7) / 8) < (int64_t(1) << 32) &&
-      !force_generic()) {
+  if (N > 2 && need > 0 && work && work_bytes >= need && (uintptr_t)work % 16 == 0 && !force_generic() &&
+      (R * (K / M) + 255) / 256 <= (int64_t)INT32_MAX &&
+      dense_nt_fast_ok(work, K, Bt, ldbt, C, ldc, K)) {
+    const int64_t groups = R * (K / M);
+    const unsigned blocks = (unsigned)((groups + 255) / 256);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, s, (const uint16_t*)values, meta, R, K, N, (uint16_t*)work);
+    };
+    if (M == 4) go(nm_expand_kernel<4>);
+    else if (M == 8) go(nm_expand_kernel<8>);
+    else go(nm_expand_kernel<16>);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_dense_nt(work, K, Bt, ldbt, R, Nc, K, C, ldc, s);
+  }
+  if (N <= 2 && need > 0 && work && work_bytes >= need && (uintptr_t)work % 16 == 0 &&
+      R * ((K + 7) / 8) < (int64_t(1) << 32) && !force_generic()) {
     unsigned char* w = (unsigned char*)work;
     uint8_t* m24 = w + (R * (K / 2) * esz + 15) / 16 * 16;
     const unsigned blocks = (unsigned)((R * ((K + 7) / 8) + 255) / 256);

@@ -86,6 +86,9 @@ WORKLOADS = {
     "ffn_up_nm28_8192x2048x4096": dict(
         kind="spmm_nm_general", dtype="bf16", R=8192, K=2048, Nc=4096, N=2, M=8,
         A=dict(seed=2000, mean=0.0, std=0.02), B=dict(seed=2001, mean=0.0, std=1.0)),
+    "ffn_up_nm48_8192x2048x4096": dict(
+        kind="spmm_nm_general", dtype="bf16", R=8192, K=2048, Nc=4096, N=4, M=8,
+        A=dict(seed=2000, mean=0.0, std=0.02), B=dict(seed=2001, mean=0.0, std=1.0)),
     "ffn_down_vnm64_2_8_2048x8192x4096": dict(
         kind="spmm_venom", dtype="bf16", R=2048, K=8192, Nc=4096, V=64, M=8,
         A=dict(seed=3000, mean=0.0, std=0.02), B=dict(seed=3001, mean=0.0, std=1.0)),

@@ -120,7 +120,9 @@ def test_lowrank_general_fused_errors(L):
     assert L.spmm_nm_general(1, None, FAKE, 8, 16, 2, 8, FAKE, 16, 8, FAKE, 8, None, 0, s) == nm.NM_ERR_NULL
     assert L.nm_general_work_bytes(1, 8, 64, 2, 8) == 8 * 32 * 2 + 8 * 8
     assert L.nm_general_work_bytes(0, 8, 64, 1, 4) == 8 * 32 * 4 + 8 * 8
-    assert L.nm_general_work_bytes(1, 8, 64, 3, 8) == 0
+    assert L.nm_general_work_bytes(1, 8, 64, 3, 8) == 8 * 64 * 2
+    assert L.nm_general_work_bytes(0, 8, 64, 3, 8) == 0
+    assert L.nm_general_work_bytes(1, 8, 72, 3, 8) == 0
     # sddmm_venom(dt, dY, lddy, Wd, ldw, T, F, Nc, V, M, hv, hm, hc, relu, dz, dYt, lddyt, stream)
     assert L.sddmm_venom(1, None, 8, FAKE, 8, 128, 64, 8, 128, 8, FAKE, FAKE, FAKE, 1, FAKE, None, 0, s) == \
         nm.NM_ERR_NULL

@@ -136,12 +136,14 @@ def test_ffn_up_nm24_lowrank64_full():
 
 
 # ---------------------------------------------------------------------------
-# 2:8 up-projection: nm_prune_compress_transpose (N:M) -> spmm_nm_general (2:4 form in work memory),
+# 2:8 and 4:8 up-projections: nm_prune_compress_transpose (N:M) -> spmm_nm_general (2:8: the 2:4
+# form in work memory; 4:8: dense bf16 rows in work memory and the dense GEMM),
 # W [8192 x 2048], X [2048 x 4096]
 # ---------------------------------------------------------------------------
 
-def test_ffn_up_nm28_full():
-    w = synth.WORKLOADS["ffn_up_nm28_8192x2048x4096"]
+@pytest.mark.parametrize("name", ["ffn_up_nm28_8192x2048x4096", "ffn_up_nm48_8192x2048x4096"])
+def test_ffn_up_general_full(name):
+    w = synth.WORKLOADS[name]
     R, K, Nc, N, M = w["R"], w["K"], w["Nc"], w["N"], w["M"]
     W, X = _gen(w["A"], (R, K)), _gen(w["B"], (K, Nc))
     fmask, fvals, fmeta, fXt = nm.nm_prune_compress_transpose(dev(W, "bf16"), dev(X, "bf16"), N, M)
@@ -155,9 +157,9 @@ def test_ffn_up_nm28_full():
     A64 = O.decode(O.decompress_nm(wv, wm, R, K, N, M), "bf16")
     X64 = O.decode(X, "bf16")
     rows = _sample(R, 48, 17)
-    _check_rows(C, A64[rows], X64, rows, "ffn_up 2:8 spmm_nm_general")
+    _check_rows(C, A64[rows], X64, rows, f"ffn_up {N}:{M} spmm_nm_general")
     cols = _sample(Nc, 24, 18)
-    _check_cols(C, A64, X64[:, cols], cols, "ffn_up 2:8 spmm_nm_general")
+    _check_cols(C, A64, X64[:, cols], cols, f"ffn_up {N}:{M} spmm_nm_general")
 
 
 # ---------------------------------------------------------------------------

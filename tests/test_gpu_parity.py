@@ -403,9 +403,13 @@ GENERAL_CASES = [
     (1, 16, 64, 256, 40),
     (1, 4, 40, 36, 13),        # K % 8 == 4: a half-filled last metadata byte in 2:4 form
     (2, 4, 256, 512, 256),     # 2:4 itself: spmm_nm_t
-    (4, 8, 200, 256, 72),      # N > 2: the SIMT kernel
+    (4, 8, 200, 256, 72),      # N > 2, bf16 with work memory: dense rows + the dense NT GEMM
     (3, 8, 64, 128, 40),
-    (8, 16, 130, 512, 33),
+    (3, 4, 300, 320, 264),     # 3:4: five 64-k stages, ragged row and column tiles
+    (6, 8, 520, 1024, 136),
+    (12, 16, 72, 512, 96),
+    (8, 16, 130, 512, 33),     # ldc % 4 != 0: the SIMT kernel
+    (3, 4, 64, 96, 40),        # K % 64 != 0: the SIMT kernel
 ]
 
 
@@ -414,8 +418,9 @@ GENERAL_CASES = [
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("work", ["auto", None])
 def test_spmm_nm_general(N, M, R, K, Nc, kind, dtype, work, tier_t):
-    """Any N:M against the oracle; N <= 2 with work memory goes through the 2:4 form (runs padded
-    with +0.0), without it through the SIMT kernel."""
+    """Any N:M against the oracle.  With work memory N <= 2 goes through the 2:4 form (runs padded
+    with +0.0) and N > 2 in bf16 (K % 64 == 0, ldc % 4 == 0) through dense rows and the dense NT
+    GEMM; everything else through the SIMT kernel."""
     raw = _inputs(kind, (R, K), seed=R + K + N + M, dtype=dtype)
     vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, dtype, N, M), N, M)
     Btraw = _inputs(kind, (Nc, K), seed=Nc + N, dtype=dtype)
@@ -430,7 +435,9 @@ def test_spmm_nm_general(N, M, R, K, Nc, kind, dtype, work, tier_t):
 
 def test_spmm_nm_general_work_bytes_and_errors():
     assert nm.general_work_bytes(torch.bfloat16, 8, 64, 2, 8) == 8 * 32 * 2 + 8 * 8
-    assert nm.general_work_bytes(torch.bfloat16, 8, 64, 4, 8) == 0      # N > 2: no 2:4 form
+    assert nm.general_work_bytes(torch.bfloat16, 8, 64, 4, 8) == 8 * 64 * 2   # N > 2: dense bf16 rows
+    assert nm.general_work_bytes(torch.float32, 8, 64, 4, 8) == 0       # N > 2 in fp32: SIMT only
+    assert nm.general_work_bytes(torch.bfloat16, 8, 72, 3, 8) == 0      # K % 64 != 0: SIMT only
     assert nm.general_work_bytes(torch.bfloat16, 8, 64, 2, 4) == 0      # 2:4 itself
     assert nm.general_work_bytes(torch.bfloat16, 8, 60, 2, 8) == 0      # K % M != 0
     z = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt, device="cuda")   # noqa: E731

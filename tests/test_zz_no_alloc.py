@@ -2,7 +2,7 @@
 of caller work memory) against spmm_nm_general with work memory: the same kernels, so the same
 bits, and both within the fp64 oracle's tolerance.  Two calls in a row on one GPU, the second
 with a smaller input (the buffer keeps the first call's bytes beyond the second's rewrite), then
-a pattern that needs no scratch at all, and an fp32 call.
+a pattern with dense rows in the buffer, one that needs no scratch at all, and an fp32 call.
 """
 
 import numpy as np
@@ -48,7 +48,8 @@ def test_noalloc_two_calls_second_smaller():
     _run(2048, 4096, 2, 8, 520, 31)               # 2:8: rewritten into the scratch buffer (18.9 MB)
     _run(256, 512, 1, 4, 264, 32)                 # smaller, 1:4: the start of the buffer again
     _run(512, 1024, 2, 16, 136, 33, kind="ints")  # bit-exact integers
-    _run(256, 512, 4, 8, 72, 34)                  # 4:8: no scratch (SIMT kernel)
+    _run(256, 512, 4, 8, 72, 34)                  # 4:8: dense bf16 rows in the scratch buffer
+    _run(64, 96, 3, 4, 40, 36)                    # 3:4 with K % 64 != 0: no scratch (SIMT kernel)
     _run(128, 256, 2, 8, 64, 35, dtype="f32")     # fp32 2:8 through the scratch buffer
 
 
