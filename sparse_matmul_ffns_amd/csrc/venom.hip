@@ -100,44 +100,79 @@ __global__ __launch_bounds__(256) void venom_prune_kernel(const T* __restrict__ 
   }
   __syncthreads();
 
-  // 2. block column L1 norms, fp64, rows in ascending order: LDS values fetched 8 rows at a
-  //    time, added one by one
-  for (int c = tid; c < cols; c += 256) {
-    double acc = 0.0;
-    int r = 0;
-    for (; r + 8 <= V; r += 8) {
-      float x[8];
+  // 2. block column L1 norms, fp64, rows in ascending order.  bf16 tiles of 512 columns: a lane
+  //    owns two adjacent columns and reads both with one 4-byte LDS load per row (8 rows at a
+  //    time), the two sums being independent chains; otherwise one column per lane
+  if (sizeof(T) == 2 && cols == 512) {
+    for (int c = 2 * tid; c < cols; c += 512) {   // cols is a multiple of M, hence even
+      double a0 = 0.0, a1 = 0.0;
+      const unsigned char* col = reinterpret_cast<const unsigned char*>(tile) + 2 * c;
+      int r = 0;
+      for (; r + 8 <= V; r += 8) {
+        uint32_t w[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) x[k] = fabsf(Elem<T>::to_f32(tile[(r + k) * pitch + c]));
+        for (int k = 0; k < 8; ++k) w[k] = *reinterpret_cast<const uint32_t*>(col + (size_t)(r + k) * pitch * 2);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc += (double)x[k];
+        for (int k = 0; k < 8; ++k) {
+          a0 += (double)__uint_as_float((w[k] & 0x7FFFu) << 16);
+          a1 += (double)__uint_as_float(w[k] & 0x7FFF0000u);
+        }
+      }
+      for (; r < V; ++r) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(col + (size_t)r * pitch * 2);
+        a0 += (double)__uint_as_float((w & 0x7FFFu) << 16);
+        a1 += (double)__uint_as_float(w & 0x7FFF0000u);
+      }
+      l1[c] = a0;
+      l1[c + 1] = a1;
     }
-    for (; r < V; ++r) acc += (double)fabsf(Elem<T>::to_f32(tile[r * pitch + c]));
-    l1[c] = acc;
+  } else {
+    for (int c = tid; c < cols; c += 256) {
+      double acc = 0.0;
+      int r = 0;
+      for (; r + 8 <= V; r += 8) {
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = fabsf(Elem<T>::to_f32(tile[(r + k) * pitch + c]));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += (double)x[k];
+      }
+      for (; r < V; ++r) acc += (double)fabsf(Elem<T>::to_f32(tile[r * pitch + c]));
+      l1[c] = acc;
+    }
   }
   __syncthreads();
 
-  // 3. keep the 4 columns of each group with the largest L1 (lower column on ties)
-  for (int g = tid; g < ngr; g += 256) {
-    double k[M];
+  // 3. keep the 4 columns of each group with the largest L1 (lower column on ties): one lane per
+  //    (group, column) ranks its column among the group's M (M consecutive lanes of a wave hold a
+  //    group); the group's first lane packs the kept columns, in ascending order, from the wave's
+  //    ballot
+  for (int u = tid; u < ngr * M; u += 256) {   // ngr * M == cols; 256 is a multiple of M
+    const int g = u / M, p = u % M;
+    const double kp = l1[u];
+    int rk = 0;
 #pragma unroll
-    for (int p = 0; p < M; ++p) k[p] = l1[g * M + p];
-    uint32_t packed = 0;
-    int j = 0;
-#pragma unroll
-    for (int p = 0; p < M; ++p) {
-      if (rank_f64<M>(k, p) < 4) {
-        packed |= (uint32_t)p << (8 * j);
-        ++j;
-      }
+    for (int q = 0; q < M; ++q) {
+      const double kq = l1[g * M + q];
+      rk += (kq > kp || (q < p && kq == kp)) ? 1 : 0;
     }
-    *reinterpret_cast<uint32_t*>(csel + 4 * g) = packed;
-    const int64_t gg = c0 / M + g;
-    uint8_t* dst = colsel + (blk * G + gg) * 4;
-    if (((uintptr_t)dst & 3) == 0) {
-      *reinterpret_cast<uint32_t*>(dst) = packed;
-    } else {
-      for (int e = 0; e < 4; ++e) dst[e] = (uint8_t)(packed >> (8 * e));
+    const uint64_t kept = __ballot(rk < 4);
+    if (p == 0) {
+      const uint32_t bits = (uint32_t)(kept >> ((threadIdx.x & 63) & ~(M - 1))) & ((1u << M) - 1u);
+      uint32_t packed = 0, rest = bits;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        packed |= (uint32_t)__builtin_ctz(rest) << (8 * j);
+        rest &= rest - 1u;
+      }
+      *reinterpret_cast<uint32_t*>(csel + 4 * g) = packed;
+      const int64_t gg = c0 / M + g;
+      uint8_t* dst = colsel + (blk * G + gg) * 4;
+      if (((uintptr_t)dst & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = packed;
+      } else {
+        for (int e = 0; e < 4; ++e) dst[e] = (uint8_t)(packed >> (8 * e));
+      }
     }
   }
   __syncthreads();

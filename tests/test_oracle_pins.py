@@ -229,6 +229,25 @@ def test_venom_l1_is_sequential_fp64():
     assert O.venom_column_l1(x, 4, 8)[0, 0] == 2.0 ** 53 + 2
 
 
+@pytest.mark.parametrize("V,t", [(64, 2.0 ** -58), (128, 2.0 ** -59)])
+def test_venom_sequential_sum_decides_a_tie(V, t):
+    """The premise of the GPU test of the order-dependent tile: column 1 = (1, t, t, ...) sums to
+    exactly 1.0 in row order (each t is below half an ulp of 1.0), ties column 0 = (1, 0, ...) and
+    loses it; its exact sum (what any other order of exact-sum arithmetic would give) exceeds 1.0
+    and would win."""
+    x = np.zeros((V, 8), np.float32)
+    x[0, 0] = x[0, 1] = 1.0
+    x[1:, 1] = t
+    x[0, 2:5] = 5.0
+    raw = synth.f32_to_bf16_bits(x)
+    assert np.array_equal(synth.bf16_bits_to_f32(raw), x)           # every value exact in bf16
+    l1 = O.venom_column_l1(O.decode(raw, "bf16"), V, 8)
+    assert l1[0, 0] == l1[0, 1] == 1.0
+    assert 1.0 + (V - 1) * t > 1.0 + 2.0 ** -53                       # the exact sum rounds up
+    _, _, colsel, _, _ = O.prune_venom(raw, "bf16", V, 8, False)
+    assert list(colsel[0, 0]) == [0, 2, 3, 4]
+
+
 # ---------------------------------------------------------------------------
 # double pruning
 # ---------------------------------------------------------------------------
