@@ -83,6 +83,81 @@ __global__ __launch_bounds__(256) void nm_to24_kernel(const T* __restrict__ valu
   m24[(int64_t)row * tpr + t] = (uint8_t)byte;
 }
 
+// The same rewrite for bf16 2:8 and 1:8 with 16-byte rows (K % 64 == 0): one thread per 24 bits of
+// positions (4 groups of 2:8, 8 of 1:8), i.e. 8 kept values -- one 16-byte load of values, three
+// byte loads of positions -- and 32 or 64 bytes of 2:4 values plus 4 or 8 bytes of nibbles out
+// with 16-, 4- and 8-byte stores; consecutive threads cover consecutive bytes of every stream.  A
+// group of 8 columns is the two runs 2g, 2g+1 of the 2:4 form, so its output nibble byte is g.
+template <int N>
+__global__ __launch_bounds__(256) void nm_to24_m8_kernel(const uint16_t* __restrict__ values,
+                                                         const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+                                                         uint16_t* __restrict__ v24, uint8_t* __restrict__ m24) {
+  constexpr int GPT = N == 2 ? 4 : 8;   // groups per thread
+  const uint32_t G = (uint32_t)(K / 8), per_row = G / GPT;
+  const uint32_t u = blockIdx.x * 256u + threadIdx.x;
+  if (u >= (uint32_t)R * per_row) return;
+  const uint32_t r = u / per_row, q = u - r * per_row;
+  const uint8_t* mp = meta + (int64_t)r * (3 * per_row) + 3 * q;
+  const uint32_t bits = (uint32_t)mp[0] | ((uint32_t)mp[1] << 8) | ((uint32_t)mp[2] << 16);
+  const u32x4 vin = *reinterpret_cast<const u32x4*>(values + (int64_t)r * G * N + (int64_t)q * GPT * N);
+  uint32_t ov[2 * GPT];
+  uint32_t ob[GPT];
+#pragma unroll
+  for (int g = 0; g < GPT; ++g) {
+    uint32_t p[N], v[N];
+#pragma unroll
+    for (int s = 0; s < N; ++s) {
+      const int i = g * N + s;   // survivor index within the thread's 8
+      p[s] = (bits >> (3 * i)) & 7u;
+      v[s] = (vin[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    }
+    uint32_t nib[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // survivors inside run h (positions 4h .. 4h+3), in ascending position; free slots get +0.0
+      // at the lowest free positions
+      uint32_t cnt = 0, pa = 0, pb = 1, va = 0, vb = 0;
+#pragma unroll
+      for (int s = 0; s < N; ++s) {
+        if ((p[s] >> 2) == (uint32_t)h) {
+          if (cnt == 0) {
+            pa = p[s] & 3u;
+            va = v[s];
+          } else {
+            pb = p[s] & 3u;
+            vb = v[s];
+          }
+          ++cnt;
+        }
+      }
+      if (cnt == 1) {
+        if (pa == 0) {
+          pb = 1;
+          vb = 0;
+        } else {
+          pb = pa;
+          vb = va;
+          pa = 0;
+          va = 0;
+        }
+      }
+      ov[2 * g + h] = va | (vb << 16);
+      nib[h] = pa | (pb << 2);
+    }
+    ob[g] = nib[0] | (nib[1] << 4);
+  }
+  u32x4* vd = reinterpret_cast<u32x4*>(v24 + (int64_t)r * (K / 2) + (int64_t)q * GPT * 4);
+#pragma unroll
+  for (int k = 0; k < GPT / 2; ++k) vd[k] = u32x4{ov[4 * k], ov[4 * k + 1], ov[4 * k + 2], ov[4 * k + 3]};
+  uint8_t* md = m24 + (int64_t)r * (K / 8) + (int64_t)q * GPT;
+  if constexpr (GPT == 4) {
+    *reinterpret_cast<uint32_t*>(md) = ob[0] | (ob[1] << 8) | (ob[2] << 16) | (ob[3] << 24);
+  } else {
+    *reinterpret_cast<u32x2*>(md) = u32x2{ob[0] | (ob[1] << 8) | (ob[2] << 16) | (ob[3] << 24),
+                                          ob[4] | (ob[5] << 8) | (ob[6] << 16) | (ob[7] << 24)};
+  }
+}
+
 // Dense bf16 rows of an N:M compressed matrix (the SpMM's own copy, row stride K): one thread per
 // (row, group) reads the group's N values and N * log2(M) metadata bits, places each value at its
 // position (a later survivor overwrites an earlier one at the same position, as nm_decompress
@@ -225,7 +300,17 @@ hipError_t launch_spmm_nm_general(int dt, const void* values, const uint8_t* met
     unsigned char* w = (unsigned char*)work;
     uint8_t* m24 = w + (R * (K / 2) * esz + 15) / 16 * 16;
     const unsigned blocks = (unsigned)((R * ((K + 7) / 8) + 255) / 256);
-    if (dt == DT_BF16)
+    if (dt == DT_BF16 && M == 8 && K % 64 == 0 && (uintptr_t)values % 16 == 0) {
+      // 2:8 and 1:8: one thread per 8 kept values (4 groups of 2:8, 8 of 1:8)
+      const int64_t threads = R * (K / (N == 2 ? 32 : 64));
+      const unsigned b2 = (unsigned)((threads + 255) / 256);
+      if (N == 2)
+        hipLaunchKernelGGL(nm_to24_m8_kernel<2>, dim3(b2), dim3(256), 0, s, (const uint16_t*)values, meta, R, K,
+                           (uint16_t*)w, m24);
+      else
+        hipLaunchKernelGGL(nm_to24_m8_kernel<1>, dim3(b2), dim3(256), 0, s, (const uint16_t*)values, meta, R, K,
+                           (uint16_t*)w, m24);
+    } else if (dt == DT_BF16)
       hipLaunchKernelGGL(nm_to24_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, (const uint16_t*)values, meta, R, K,
                          N, M, (uint16_t*)w, m24);
     else

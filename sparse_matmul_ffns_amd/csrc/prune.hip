@@ -473,6 +473,97 @@ hipError_t launch_nm_compress(int dt, const void* A, int64_t lda, const uint8_t*
                        : compress_dispatch<uint32_t>(A, lda, mask, ldmask, R, K, N, M, values, meta, bad, s);
 }
 
+// ---------------------------------------------------------------------------
+// nm_prune_compress for bf16 N:8 (1 <= N <= 7) with 16-byte aligned rows and K % 64 == 0, one pass:
+// one thread per chunk of CG groups whose positions fill whole bytes (CG = 4 for even N, 8 for
+// odd).  The 64 lanes of a wave load the pieces of the wave's 64 chunks in address order (whole
+// lines per instruction) into LDS, each thread's region padded by 16 bytes so that the lanes'
+// reads of their own chunks fall on distinct banks.  Per group the positions are ranked on keys
+// extended by position ((|x| << 3) | (7 - p): distinct, larger key first, lower position on ties,
+// the order of rank_of), the kept ones taken in ascending order from the kept bits; the chunk
+// leaves as 16-byte stores of mask bytes and values and byte stores of its positions.
+// ---------------------------------------------------------------------------
+template <int N>
+__global__ __launch_bounds__(256) void nm_prune_compress_m8_kernel(const uint16_t* __restrict__ A, int64_t lda,
+                                                                   int64_t R, int64_t K, uint8_t* __restrict__ mask,
+                                                                   int64_t ldmask, uint16_t* __restrict__ values,
+                                                                   uint8_t* __restrict__ meta) {
+  constexpr int M = 8, CG = (N % 2 == 0) ? 4 : 8, E = CG * M, PA = E * 2 / 16, PS = PA + 1;
+  constexpr int MB = CG * N * 3 / 8;           // metadata bytes per chunk
+  constexpr int NW32 = (CG * N * 3 + 31) / 32; // 32-bit words of positions
+  __shared__ u32x4 stage[256 * PS];
+  const int64_t G = K / M, per_row = G / CG, total = R * per_row;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int q = lane; q < 64 * PA; q += 64) {
+    const int tl = q / PA, j = q % PA;
+    const int64_t c = (int64_t)blockIdx.x * 256 + 64 * wave + tl;
+    if (c < total) {
+      const int64_t rr = c / per_row, gg = (c - rr * per_row) * CG;
+      stage[(64 * wave + tl) * PS + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(A + rr * lda + gg * M + 8 * j));
+    }
+  }
+  __syncthreads();
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= total) return;
+  const int64_t rr = c / per_row, gg = (c - rr * per_row) * CG;
+  uint32_t x[E / 2];
+#pragma unroll
+  for (int j = 0; j < PA; ++j) {
+    const u32x4 v = stage[threadIdx.x * PS + j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * j + e] = v[e];
+  }
+  uint32_t mk[E / 4];          // mask bytes, 4 per word
+  uint32_t vo[CG * N / 2];     // kept values, 2 per word
+  uint32_t w[NW32];            // positions, LSB first
+#pragma unroll
+  for (int k = 0; k < NW32; ++k) w[k] = 0;
+#pragma unroll
+  for (int g = 0; g < CG; ++g) {
+    uint32_t ext[M];
+#pragma unroll
+    for (int p = 0; p < M; ++p) {
+      const uint32_t b = (x[(g * M + p) >> 1] >> (16 * (p & 1))) & 0x7FFFu;
+      ext[p] = (b << 3) | (uint32_t)(7 - p);
+    }
+    uint32_t kept = 0;
+#pragma unroll
+    for (int p = 0; p < M; ++p) {
+      int rk = 0;
+#pragma unroll
+      for (int q = 0; q < M; ++q) rk += ext[q] > ext[p] ? 1 : 0;
+      kept |= (rk < N ? 1u : 0u) << p;
+    }
+    // mask bytes of the group: byte p = bit p of kept
+    mk[2 * g] = ((kept & 1u) | ((kept & 2u) << 7) | ((kept & 4u) << 14) | ((kept & 8u) << 21));
+    mk[2 * g + 1] = (((kept >> 4) & 1u) | (((kept >> 4) & 2u) << 7) | (((kept >> 4) & 4u) << 14) |
+                     (((kept >> 4) & 8u) << 21));
+    uint32_t rest = kept;
+#pragma unroll
+    for (int s2 = 0; s2 < N; ++s2) {
+      const uint32_t p = (uint32_t)__builtin_ctz(rest);
+      rest &= rest - 1u;
+      const uint32_t d = (p >> 1) == 0 ? x[4 * g] : (p >> 1) == 1 ? x[4 * g + 1] : (p >> 1) == 2 ? x[4 * g + 2] : x[4 * g + 3];
+      const uint32_t v = (d >> (16 * (p & 1))) & 0xFFFFu;
+      const int i = g * N + s2;   // kept value index within the chunk
+      if (i & 1) vo[i >> 1] |= v << 16;
+      else vo[i >> 1] = v;
+      const int off = 3 * i;
+      w[off >> 5] |= p << (off & 31);
+      if ((off & 31) > 29) w[(off >> 5) + 1] |= p >> (32 - (off & 31));
+    }
+  }
+  u32x4* md = reinterpret_cast<u32x4*>(mask + rr * ldmask + gg * M);
+#pragma unroll
+  for (int k = 0; k < E / 16; ++k) md[k] = u32x4{mk[4 * k], mk[4 * k + 1], mk[4 * k + 2], mk[4 * k + 3]};
+  u32x4* vd = reinterpret_cast<u32x4*>(values + rr * (G * N) + gg * N);
+#pragma unroll
+  for (int k = 0; k < CG * N / 8; ++k) vd[k] = u32x4{vo[4 * k], vo[4 * k + 1], vo[4 * k + 2], vo[4 * k + 3]};
+  uint8_t* mt = meta + rr * (G * N * 3 / 8) + (gg / CG) * MB;
+#pragma unroll
+  for (int k = 0; k < MB; ++k) mt[k] = (uint8_t)(w[k >> 2] >> (8 * (k & 3)));
+}
+
 template <typename T>
 static hipError_t prune_compress_dispatch(const void* A, int64_t lda, int64_t R, int64_t K, int N, int M,
                                           uint8_t* mask, int64_t ldmask, void* values, uint8_t* meta, hipStream_t s) {
@@ -487,6 +578,25 @@ static hipError_t prune_compress_dispatch(const void* A, int64_t lda, int64_t R,
       hipLaunchKernelGGL((nm_prune_compress24_vec_kernel<T, int64_t>), dim3(nblocks(n, 256 * kFusedU)), dim3(256), 0,
                          s, (const T*)A, lda, R, K, mask, ldmask, (T*)values, meta);
     return hipGetLastError();
+  }
+  if (esz == 2 && M == 8 && K % 64 == 0 && (uintptr_t)A % 16 == 0 && (lda * esz) % 16 == 0 &&
+      (uintptr_t)mask % 16 == 0 && ldmask % 16 == 0 && (uintptr_t)values % 16 == 0 && !force_generic()) {
+    const int64_t chunks = R * ((K / 8) / (N % 2 == 0 ? 4 : 8));
+    const unsigned grid = (unsigned)((chunks + 255) / 256);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, (const uint16_t*)A, lda, R, K, mask, ldmask,
+                         (uint16_t*)values, meta);
+      return hipGetLastError();
+    };
+    switch (N) {
+      case 1: return go(nm_prune_compress_m8_kernel<1>);
+      case 2: return go(nm_prune_compress_m8_kernel<2>);
+      case 3: return go(nm_prune_compress_m8_kernel<3>);
+      case 4: return go(nm_prune_compress_m8_kernel<4>);
+      case 5: return go(nm_prune_compress_m8_kernel<5>);
+      case 6: return go(nm_prune_compress_m8_kernel<6>);
+      default: return go(nm_prune_compress_m8_kernel<7>);
+    }
   }
   // other patterns and layouts: the two passes, mask in between
   const hipError_t e = prune_dispatch<T>(A, lda, R, K, N, M, mask, ldmask, s);

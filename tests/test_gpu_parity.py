@@ -64,7 +64,11 @@ def test_prune_compress_decompress(N, M, R, K, dtype, kind, pad):
 
 
 FUSED_CASES = [(2, 4, 37, 48), (2, 4, 300, 1024), (2, 4, 513, 2064), (2, 4, 8, 16), (2, 4, 5, 44), (2, 8, 33, 88),
-               (4, 16, 17, 96)]
+               (4, 16, 17, 96),
+               # bf16 N:8 with K % 64 == 0: the one-pass N:8 kernel, every N (chunks of 4 groups for even N,
+               # 8 for odd), several workgroups, rows that end inside a workgroup
+               (1, 8, 40, 128), (2, 8, 65, 192), (3, 8, 24, 64), (4, 8, 130, 256), (5, 8, 16, 320),
+               (6, 8, 33, 64), (7, 8, 20, 128), (2, 8, 300, 2048)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -73,7 +77,7 @@ FUSED_CASES = [(2, 4, 37, 48), (2, 4, 300, 1024), (2, 4, 513, 2064), (2, 4, 8, 1
 @pytest.mark.parametrize("pad", [0, 16])
 def test_prune_compress_fused(N, M, R, K, dtype, kind, pad):
     """nm_prune_compress: mask, values and metadata byte-identical to the oracle (2:4 with K % 16 == 0
-    runs the one-pass kernel, the rest the two passes)."""
+    and bf16 N:8 with K % 64 == 0 run one-pass kernels, the rest the two passes)."""
     raw = _inputs(kind, (R, K), seed=R * 5 + K + N, dtype=dtype)
     A = dev(raw, dtype, pad=pad)
     mask_t = torch.full((R, K + pad), 7, dtype=torch.uint8, device="cuda")[:, :K]
@@ -98,6 +102,7 @@ PREP_CASES = [
     (2, 4, 64, 256, 128, 64, 8),    # mask rows of 264 bytes (not a multiple of 16): two kernels
     (2, 4, 5, 44, 40, 24, 0),       # K % 16 != 0: two kernels
     (2, 8, 33, 88, 96, 17, 0),      # 2:8: two kernels
+    (2, 8, 64, 256, 128, 64, 0),    # 2:8 with K % 64 == 0: the one-pass N:8 kernel, then the transpose
 ]
 
 
@@ -399,6 +404,7 @@ GENERAL_CASES = [
     (1, 4, 300, 1024, 264),
     (2, 8, 520, 2048, 136),
     (1, 8, 256, 512, 96),
+    (2, 8, 72, 96, 40),        # K % 64 != 0: the 2:4 rewrite's general kernel
     (2, 16, 384, 1024, 520),
     (1, 16, 64, 256, 40),
     (1, 4, 40, 36, 13),        # K % 8 == 4: a half-filled last metadata byte in 2:4 form
