@@ -480,7 +480,8 @@ hipError_t launch_nm_compress(int dt, const void* A, int64_t lda, const uint8_t*
 // lines per instruction) into LDS, each thread's region padded by 16 bytes so that the lanes'
 // reads of their own chunks fall on distinct banks.  Per group the positions are ranked on keys
 // extended by position ((|x| << 3) | (7 - p): distinct, larger key first, lower position on ties,
-// the order of rank_of), the kept ones taken in ascending order from the kept bits; the chunk
+// the order of rank_of) -- the N largest are those at least the N-th of the keys sorted by a
+// 19-comparator network -- and the kept ones taken in ascending order from the kept bits; the chunk
 // leaves as 16-byte stores of mask bytes and values and byte stores of its positions.
 // ---------------------------------------------------------------------------
 template <int N>
@@ -526,14 +527,27 @@ __global__ __launch_bounds__(256) void nm_prune_compress_m8_kernel(const uint16_
       const uint32_t b = (x[(g * M + p) >> 1] >> (16 * (p & 1))) & 0x7FFFu;
       ext[p] = (b << 3) | (uint32_t)(7 - p);
     }
+    // the N-th largest extended key (a sorting network over a copy, descending), then position p
+    // is kept iff its key is at least that one (the keys are distinct)
+    uint32_t srt[M];
+#pragma unroll
+    for (int p = 0; p < M; ++p) srt[p] = ext[p];
+    auto cx = [&](int i, int j) {
+      const uint32_t hi = srt[i] > srt[j] ? srt[i] : srt[j], lo = srt[i] > srt[j] ? srt[j] : srt[i];
+      srt[i] = hi;
+      srt[j] = lo;
+    };
+    // 8-input sorting network of 19 comparators
+    cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
+    cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
+    cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
+    cx(2, 4); cx(3, 5);
+    cx(1, 4); cx(3, 6);
+    cx(1, 2); cx(3, 4); cx(5, 6);
+    const uint32_t thr = srt[N - 1];
     uint32_t kept = 0;
 #pragma unroll
-    for (int p = 0; p < M; ++p) {
-      int rk = 0;
-#pragma unroll
-      for (int q = 0; q < M; ++q) rk += ext[q] > ext[p] ? 1 : 0;
-      kept |= (rk < N ? 1u : 0u) << p;
-    }
+    for (int p = 0; p < M; ++p) kept |= (ext[p] >= thr ? 1u : 0u) << p;
     // mask bytes of the group: byte p = bit p of kept
     mk[2 * g] = ((kept & 1u) | ((kept & 2u) << 7) | ((kept & 4u) << 14) | ((kept & 8u) << 21));
     mk[2 * g + 1] = (((kept >> 4) & 1u) | (((kept >> 4) & 2u) << 7) | (((kept >> 4) & 4u) << 14) |
