@@ -84,7 +84,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
   const int ntm = (int)((R + BM - 1) / BM), ntn = (int)((Nc + BN - 1) / BN);
   const int nwg = ntm * ntn;
   const int wg = xcd_remap(blockIdx.x, nwg);
-  constexpr int GM = 4;
+  // row tiles per group of the tile order: with long rows (K >= 4096: 64 or more steps per tile,
+  // the training step's products) eight row tiles share each column panel while they run, at
+  // K = 2048 four (measured: 591 -> 575 us at 4096 x 16384 x 8192, 586 -> 583 at 16384 x 4096 x
+  // 8192; 86 -> 97 us at 8192 x 2048 x 4096 with eight)
+  const int GM = Kd >= 4096 ? 8 : 4;
   const int grp = wg / (GM * ntn);
   const int first_m = grp * GM;
   const int gsz = (ntm - first_m) < GM ? (ntm - first_m) : GM;
