@@ -39,6 +39,9 @@
 namespace nms {
 
 __device__ __forceinline__ int nt_apos(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// largest C (bytes) written with ordinary stores
+constexpr int64_t kCachedCBytes = int64_t(160) << 20;
 __device__ __forceinline__ int nt_bpos(int n, int c) { return c ^ ((n >> 1) & 7); }
 __device__ __forceinline__ int nt_mpos(int r, int p) { return p ^ ((r >> 3) & 1); }
 
@@ -67,7 +70,7 @@ struct NtCfg {
 // tokens) to V:N:M with V = vnm_v tokens (64, 128 or 256) and M rows of C (4, 8 or 16), writing
 // h's values, nibbles and column choices (hv, hm, hc in the layout of prune_act_venom; R and Nc
 // multiples of 256).
-template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT, bool LR, int VNM = 0>
+template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT, bool LR, int VNM = 0, bool CACHED = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
     const uint16_t* __restrict__ values, const uint8_t* __restrict__ meta, int64_t R, int64_t Kd,
     const uint16_t* __restrict__ Bt, int64_t ldbt, int64_t Nc, OutT* __restrict__ C, int64_t ldc,
@@ -409,6 +412,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
     return;
   }
 
+  // CACHED: C leaves with ordinary stores (chosen while C fits the last-level cache comfortably:
+  // each round's burst of tiles is then absorbed there); otherwise with non-temporal ones, which
+  // keep C from evicting the operands the later tiles still read
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -418,23 +424,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void spmm_nt_kernel(
       for (int e = 0; e < 16; ++e) {
         const int64_t row = m0 + wm * Cfg::WM + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
         if (row < R && col < Nc) {
-          if constexpr (sizeof(OutT) == 4)
-            __builtin_nontemporal_store(acc[i][j][e], C + row * ldc + col);
-          else
-            __builtin_nontemporal_store(f32_to_bf16_rne(acc[i][j][e]), C + row * ldc + col);
+          OutT v;
+          if constexpr (sizeof(OutT) == 4) v = acc[i][j][e];
+          else v = f32_to_bf16_rne(acc[i][j][e]);
+          if constexpr (CACHED) C[row * ldc + col] = v;
+          else __builtin_nontemporal_store(v, C + row * ldc + col);
         }
       }
     }
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT, bool LR = false, int VNM = 0>
+template <int BM, int BN, int WAVES_M, int WAVES_N, typename OutT, bool LR = false, int VNM = 0, bool CACHED = false>
 static hipError_t run_nt(const void* values, const uint8_t* meta, int64_t R, int64_t Kd, const void* Bt, int64_t ldbt,
                          int64_t Nc, OutT* C, int64_t ldc, hipStream_t s, const void* U = nullptr, int64_t ldu = 0,
                          const float* Tt = nullptr, int rank = 0, uint16_t* hv = nullptr, uint8_t* hm = nullptr,
                          uint8_t* hc = nullptr, int vnm_v = 0) {
   using Cfg = NtCfg<BM, BN, WAVES_M, WAVES_N>;
-  auto kern = spmm_nt_kernel<BM, BN, WAVES_M, WAVES_N, OutT, LR, VNM>;
+  auto kern = spmm_nt_kernel<BM, BN, WAVES_M, WAVES_N, OutT, LR, VNM, CACHED>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   const int64_t ntiles = ((R + BM - 1) / BM) * ((Nc + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg::NT), (size_t)Cfg::LDS, s, (const uint16_t*)values, meta,
@@ -452,6 +459,8 @@ bool spmm_nt_ok(const void* values, const uint8_t* meta, const void* Bt, int64_t
 
 hipError_t launch_spmm_nm_nt_dma(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
                                  int64_t ldbt, int64_t Nc, float* C, int64_t ldc, hipStream_t s) {
+  if (R * Nc * 4 <= kCachedCBytes)
+    return run_nt<256, 256, 2, 4, float, false, 0, true>(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
   return run_nt<256, 256, 2, 4>(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s);
 }
 
@@ -482,6 +491,9 @@ hipError_t launch_spmm_nm_t_relu_venom(const void* values, const uint8_t* meta, 
 hipError_t launch_spmm_nm_nt_dma_lowrank(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
                                          int64_t ldbt, int64_t Nc, const void* U, int64_t ldu, const float* Tt,
                                          int rank, float* C, int64_t ldc, hipStream_t s) {
+  if (R * Nc * 4 <= kCachedCBytes)
+    return run_nt<256, 256, 2, 4, float, true, 0, true>(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s, U, ldu, Tt,
+                                                        rank);
   return run_nt<256, 256, 2, 4, float, true>(values, meta, R, K, Bt, ldbt, Nc, C, ldc, s, U, ldu, Tt, rank);
 }
 
