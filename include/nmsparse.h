@@ -418,6 +418,24 @@ nm_status nm_reprune_t(nm_dtype dt, const void* values, const uint8_t* meta, int
                        void* values_t, uint8_t* meta_t, nm_stream stream);
 
 /*
+ * nm_reprune_t_transpose -- nm_reprune_t of W_s and nm_transpose of X in one
+ * launch: the two passes of a double-pruned training step (NSF PAR award
+ * 2340011, SLOPE abstract: the transposed weight re-pruned for the backward
+ * pass; the layer input then feeds spmm_nm_t K-contiguous) that touch
+ * disjoint data.
+ *   values, meta, R, K, values_t, meta_t as for nm_reprune_t;
+ *   X [RX][ldx] dense input, Xt [CX][ldxt] output (ldxt >= RX): Xt[c][r] = X[r][c].
+ * Outputs are byte-identical to nm_reprune_t followed by nm_transpose.  bf16
+ * only (NM_ERR_UNSUPPORTED otherwise).  With R and K multiples of 128 and the
+ * re-prune's aligned layout the two run as one kernel; otherwise as the two
+ * kernels.  No output may overlap an input.  Errors as for the two calls.
+ */
+nm_status nm_reprune_t_transpose(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R,
+                                 int64_t K, void* values_t, uint8_t* meta_t, const void* X,
+                                 int64_t ldx, int64_t RX, int64_t CX, void* Xt, int64_t ldxt,
+                                 nm_stream stream);
+
+/*
  * sddmm_nm -- the weight gradient of a 2:4 layer, sampled at the weight's
  * survivors ("Success story: ESPLAG", Research Topic: kernels for the full
  * sparse training step):

@@ -15,6 +15,7 @@ from .nmsparse import (  # noqa: F401
     nm_prune,
     nm_prune_compress,
     nm_prune_compress_transpose,
+    nm_reprune_t_transpose,
     nm_reprune_t,
     prune_act_venom,
     sddmm_nm,

@@ -254,6 +254,19 @@ nm_status nm_reprune_t(nm_dtype dt, const void* values, const uint8_t* meta, int
   return hip_status(nms::launch_nm_reprune_t(dt, values, meta, R, K, values_t, meta_t, hs(stream)));
 }
 
+nm_status nm_reprune_t_transpose(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                                 void* values_t, uint8_t* meta_t, const void* X, int64_t ldx, int64_t RX, int64_t CX,
+                                 void* Xt, int64_t ldxt, nm_stream stream) {
+  if (!values || !meta || !values_t || !meta_t || !X || !Xt) return NM_ERR_NULL;
+  if (dt != NM_BF16) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || R % 4 != 0 || K % 4 != 0) return NM_ERR_SHAPE;
+  if (RX <= 0 || CX <= 0 || ldx < CX || ldxt < RX) return NM_ERR_SHAPE;
+  if (!aligned(values, esize(dt)) || !aligned(values_t, esize(dt)) || !aligned(X, esize(dt)) || !aligned(Xt, esize(dt)))
+    return NM_ERR_ALIGN;
+  return hip_status(nms::launch_nm_reprune_t_transpose(dt, values, meta, R, K, values_t, meta_t, X, ldx, RX, CX, Xt,
+                                                       ldxt, hs(stream)));
+}
+
 nm_status sddmm_nm(nm_dtype dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
                    int64_t T, const uint8_t* meta, float* values_out, nm_stream stream) {
   if (!D || !X || !meta || !values_out) return NM_ERR_NULL;

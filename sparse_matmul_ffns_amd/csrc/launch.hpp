@@ -33,6 +33,9 @@ hipError_t launch_prune_act_venom(int dt, const void* Z, int64_t ldz, int64_t R,
                                   int64_t ldmask, hipStream_t s);
 hipError_t launch_nm_reprune_t(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
                                void* values_t, uint8_t* meta_t, hipStream_t s);
+hipError_t launch_nm_reprune_t_transpose(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                                         void* values_t, uint8_t* meta_t, const void* X, int64_t ldx, int64_t RX,
+                                         int64_t CX, void* Xt, int64_t ldxt, hipStream_t s);
 hipError_t launch_spmm_nm(int dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* B,
                           int64_t ldb, int64_t Nc, float* C, int64_t ldc, hipStream_t s);
 hipError_t launch_spmm_venom(int dt, const void* values, const uint8_t* meta, const uint8_t* colsel, int64_t R,

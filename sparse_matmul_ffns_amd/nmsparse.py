@@ -31,6 +31,7 @@ _SIGNATURES = {
     "nm_prune": [_int, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp],
     "nm_compress": [_int, _vp, _i64, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp],
     "nm_prune_compress": [_int, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _vp, _vp],
+    "nm_reprune_t_transpose": [_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "nm_prune_compress_transpose": [_int, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _vp, _vp, _i64, _i64,
                                     _i64, _vp, _i64, _vp],
     "nm_decompress": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _vp],
@@ -507,6 +508,27 @@ def nm_reprune_t(values: torch.Tensor, meta: torch.Tensor, R: int, K: int, value
     _check(lib().nm_reprune_t(_dt(values), _p(values), _p(meta), R, K, _p(values_t), _p(meta_t), _stream()),
            "nm_reprune_t")
     return values_t, meta_t
+
+
+def nm_reprune_t_transpose(values: torch.Tensor, meta: torch.Tensor, R: int, K: int, X: torch.Tensor,
+                           values_t=None, meta_t=None, Xt=None):
+    """nm_reprune_t of (values, meta) and transpose of X (bf16) in one launch; returns
+    (values_t, meta_t, Xt)."""
+    _dev(values, meta, values_t, meta_t, X, Xt)
+    _flat(values, "values"), _flat(meta, "meta")
+    if values_t is None:
+        values_t = torch.empty((K, R // 2), dtype=values.dtype, device=values.device)
+    if meta_t is None:
+        meta_t = torch.empty((K, (R + 7) // 8), dtype=torch.uint8, device=values.device)
+    RX, CX = X.shape
+    if Xt is None:
+        Xt = torch.empty((CX, RX), dtype=X.dtype, device=X.device)
+    if Xt.shape != (CX, RX) or Xt.dtype != X.dtype:
+        raise ValueError("Xt must be [CX, RX] with X's dtype")
+    _check(lib().nm_reprune_t_transpose(_dt(values), _p(values), _p(meta), R, K, _p(values_t), _p(meta_t), _p(X),
+                                        _rows(X, "X"), RX, CX, _p(Xt), _rows(Xt, "Xt"), _stream()),
+           "nm_reprune_t_transpose")
+    return values_t, meta_t, Xt
 
 
 def sddmm_nm(D: torch.Tensor, X: torch.Tensor, meta: torch.Tensor, out=None, Dt=None):

@@ -62,6 +62,9 @@ int main() {
   EXPECT(spmm_venom(B, P, U8, U8, 128, 256, 0, 8, P, 64, 64, F, 64, 0), NM_ERR_UNSUPPORTED);
   EXPECT(nm_reprune_t(B, P, U8, 128, 128, P, U8, 0), H);
   EXPECT(nm_reprune_t(B, P, U8, 126, 128, P, U8, 0), NM_ERR_SHAPE);
+  EXPECT(nm_reprune_t_transpose(B, P, U8, 128, 128, P, U8, P, 64, 64, 64, P, 64, 0), H);
+  EXPECT(nm_reprune_t_transpose(B, P, U8, 128, 128, P, U8, P, 32, 64, 64, P, 64, 0), NM_ERR_SHAPE);
+  EXPECT(nm_reprune_t_transpose(S, P, U8, 128, 128, P, U8, P, 64, 64, 64, P, 64, 0), NM_ERR_UNSUPPORTED);
   EXPECT(sddmm_nm(B, P, 64, P, 64, 64, 64, 64, U8, F, 0), H);
   EXPECT(sddmm_nm_dt(B, P, 64, P, 64, 64, 64, 64, U8, F, P, 64, 0), H);
   EXPECT(sddmm_venom(B, P, 64, P, 64, 128, 256, 64, 128, 8, P, U8, U8, 1, F, P, 128, 0), H);

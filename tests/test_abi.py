@@ -96,6 +96,15 @@ def test_venom_reprune_sddmm_errors(L):
     assert L.nm_reprune_t(1, FAKE, FAKE, 6, 8, FAKE, FAKE, s) == nm.NM_ERR_SHAPE
     assert L.nm_reprune_t(1, FAKE, FAKE, 8, 8, FAKE, None, s) == nm.NM_ERR_NULL
     assert L.nm_reprune_t(1, FAKE, FAKE, 8, 8, FAKE + 1, FAKE, s) == nm.NM_ERR_ALIGN
+    # nm_reprune_t_transpose(dt, values, meta, R, K, values_t, meta_t, X, ldx, RX, CX, Xt, ldxt, stream)
+    assert L.nm_reprune_t_transpose(1, FAKE, FAKE, 8, 8, FAKE, FAKE, None, 8, 8, 8, FAKE, 8, s) == nm.NM_ERR_NULL
+    assert L.nm_reprune_t_transpose(0, FAKE, FAKE, 8, 8, FAKE, FAKE, FAKE, 8, 8, 8, FAKE, 8, s) == \
+        nm.NM_ERR_UNSUPPORTED
+    assert L.nm_reprune_t_transpose(1, FAKE, FAKE, 6, 8, FAKE, FAKE, FAKE, 8, 8, 8, FAKE, 8, s) == nm.NM_ERR_SHAPE
+    assert L.nm_reprune_t_transpose(1, FAKE, FAKE, 8, 8, FAKE, FAKE, FAKE, 4, 8, 8, FAKE, 8, s) == nm.NM_ERR_SHAPE
+    assert L.nm_reprune_t_transpose(1, FAKE, FAKE, 8, 8, FAKE, FAKE, FAKE, 8, 8, 8, FAKE, 4, s) == nm.NM_ERR_SHAPE
+    assert L.nm_reprune_t_transpose(1, FAKE, FAKE, 8, 8, FAKE, FAKE, FAKE + 1, 8, 8, 8, FAKE, 8, s) == \
+        nm.NM_ERR_ALIGN
     assert L.sddmm_nm(1, FAKE, 8, FAKE, 8, 4, 6, 8, FAKE, FAKE, s) == nm.NM_ERR_SHAPE
     assert L.sddmm_nm(1, FAKE, 4, FAKE, 8, 4, 8, 8, FAKE, FAKE, s) == nm.NM_ERR_SHAPE
     assert L.sddmm_nm(1, FAKE, 8, FAKE, 8, 4, 8, 8, None, FAKE, s) == nm.NM_ERR_NULL

@@ -337,10 +337,15 @@ def test_train_step_nm24_full():
     assert host(vals).tobytes() == wv.tobytes() and np.array_equal(host(meta), wm)
     del mask, want_mask, Wd
 
-    vt, mt = nm.nm_reprune_t(vals, meta, dff, dm)
+    # the step's first launch: W_ds^T and X^T together; then the re-prune alone, which must agree
+    vt, mt, Xt = nm.nm_reprune_t_transpose(vals, meta, dff, dm, Xd)
     wvt, wmt = O.reprune_t(wv, wm, dff, dm, "bf16")
     assert host(vt).tobytes() == wvt.tobytes()
     assert np.array_equal(host(mt), wmt)
+    assert np.array_equal(host(Xt), np.ascontiguousarray(X.T))
+    vt2, mt2 = nm.nm_reprune_t(vals, meta, dff, dm)
+    assert torch.equal(vt2.view(torch.int16), vt.view(torch.int16)) and torch.equal(mt2, mt)
+    del vt2, mt2
 
     X64 = O.decode(X, "bf16")
     # forward: Y = W_s X
@@ -350,7 +355,8 @@ def test_train_step_nm24_full():
     Ws_rows = O.decode(O.decompress_nm(wv[rows], wm[rows], len(rows), dm, 2, 4), "bf16")
     _check_rows(Y, Ws_rows, X64, rows, "train Y")
     del Y
-    Y = nm.spmm_nm_t(vals, meta, dm, nm.transpose(Xd))
+    Y = nm.spmm_nm_t(vals, meta, dm, Xt)
+    del Xt
     _finite(Y, "Y (spmm_nm_t)")
     _check_rows(Y, Ws_rows, X64, rows, "train Y (spmm_nm_t)")
     del Y

@@ -608,6 +608,36 @@ def test_spmm_venom(R, K, Nc, V, M, kind, venom_tier):
 # nm_reprune_t / sddmm_nm
 # ---------------------------------------------------------------------------
 
+REPRUNE_T_TRANSPOSE_CASES = [
+    # (R, K, RX, CX, pad): R and K multiples of 128 run the one-launch kernel (whole and ragged 64 x 64
+    # transpose tiles); the others the two kernels
+    (256, 512, 520, 136, 0),
+    (1024, 128, 64, 4096, 8),
+    (384, 640, 1000, 72, 16),
+    (132, 68, 96, 48, 0),       # R, K not multiples of 128: two kernels
+]
+
+
+@pytest.mark.parametrize("R,K,RX,CX,pad", REPRUNE_T_TRANSPOSE_CASES,
+                         ids=[f"{c[0]}x{c[1]}_X{c[2]}x{c[3]}" for c in REPRUNE_T_TRANSPOSE_CASES])
+def test_reprune_t_transpose(R, K, RX, CX, pad):
+    """nm_reprune_t_transpose: the re-pruned transpose byte-identical to the oracle's and to nm_reprune_t,
+    Xt the exact transpose of X, padding columns untouched."""
+    raw = synth.normal((R, K), R + 3 * K, dtype="bf16")
+    vals, meta, _ = O.compress_nm(raw, O.prune_nm(raw, "bf16", 2, 4), 2, 4)
+    xraw = synth.normal((RX, CX), RX + CX, dtype="bf16")
+    v, m, X = dev(vals, "bf16"), dev(meta, "u8"), dev(xraw, "bf16", pad=pad)
+    xt_buf = torch.full((CX, RX + pad), 3, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vt, mt, Xt = nm.nm_reprune_t_transpose(v, m, R, K, X, Xt=xt_buf[:, :RX])
+    wv, wm = O.reprune_t(vals, meta, R, K, "bf16")
+    assert host(vt).tobytes() == wv.tobytes() and np.array_equal(host(mt), wm)
+    v2, m2 = nm.nm_reprune_t(v, m, R, K)
+    assert torch.equal(vt.view(torch.int16), v2.view(torch.int16)) and torch.equal(mt, m2)
+    assert np.array_equal(host(Xt), np.ascontiguousarray(xraw.T))
+    if pad:
+        assert bool((xt_buf.view(torch.int16)[:, RX:] == 3).all())
+
+
 REPRUNE_CASES = [(132, 68), (256, 512), (16, 16), (300, 200), (4, 4), (1024, 128), (384, 640)]
 
 
