@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace nms {
 
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
@@ -44,6 +46,32 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Loads into registers from inline assembly: the compiler does not count them, so a kernel waits
+// with wait_vmcnt_regs, whose in/out register operands keep every reader of the destination
+// after the wait.  (tests/test_codegen.py checks the compiled kernels: nothing touches a
+// destination register before a wait has retired its load.)
+__device__ __forceinline__ u32x4 load16_async(const void* g) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(g));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_regs(u32x4 (&rb)[8]) {
+  asm volatile("s_waitcnt vmcnt(%8)"
+               : "+v"(rb[0]), "+v"(rb[1]), "+v"(rb[2]), "+v"(rb[3]), "+v"(rb[4]), "+v"(rb[5]), "+v"(rb[6]),
+                 "+v"(rb[7])
+               : "n"(N)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_regs(u32x4 (&r0)[8], u32x4 (&r1)[8]) {
+  asm volatile("s_waitcnt vmcnt(%16)"
+               : "+v"(r0[0]), "+v"(r0[1]), "+v"(r0[2]), "+v"(r0[3]), "+v"(r0[4]), "+v"(r0[5]), "+v"(r0[6]),
+                 "+v"(r0[7]), "+v"(r1[0]), "+v"(r1[1]), "+v"(r1[2]), "+v"(r1[3]), "+v"(r1[4]), "+v"(r1[5]),
+                 "+v"(r1[6]), "+v"(r1[7])
+               : "n"(N)
+               : "memory");
 }
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 // Barrier that first waits for this wave's LDS reads and writes (and scalar loads): after it,

@@ -16,6 +16,8 @@
 // group of the weight: the selection is lane-local (two of the lane's four
 // accumulators, chosen by the group's nibble), and the 16 lanes of a row write
 // 16 consecutive float2 pairs -- 128 contiguous bytes.
+#include <type_traits>
+
 #include "common.hpp"
 #include "dma.hpp"
 #include "launch.hpp"
@@ -263,6 +265,77 @@ struct SdCfg {
 // SD_DENSE -- out[r][c] = (D X^T)[r][c] for every column, row stride ldo (a plain NT GEMM).
 enum { SD_NM = 0, SD_VNM = 1, SD_DENSE = 2 };
 
+// Epilogue of the pipelined SDDMM kernels: a wave's FM x 4 accumulator fragments cover rows
+// r0w .. r0w + 32 FM - 1 and output columns c0w .. c0w + 127 (fragment j, lane c: column
+// c0w + 4c + j), so lane l32 holds every column of 2:4 group c0w/4 + l32.  SD_DENSE stores all
+// four (16 bytes per row), the other modes the two the nibble keeps (8 bytes per row).
+template <int FM, int MODE>
+__device__ __forceinline__ void sd_epilogue(const f32x16 (&acc)[FM][4], int64_t r0w, int64_t c0w, int l32, int aa,
+                                            int64_t R, int64_t Kc, const uint8_t* __restrict__ meta,
+                                            float* __restrict__ out, const uint16_t* __restrict__ hval, int relu,
+                                            int64_t ldo) {
+  const int64_t G = Kc / 4, mrow = (Kc + 7) / 8;
+  const int64_t gq = c0w / 4 + l32;
+  if constexpr (MODE == SD_DENSE) {
+    // every column: 16 contiguous bytes per lane and row (the 32 lanes of a row write 512 bytes)
+    const int64_t c0 = 4 * gq;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = r0w + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
+        if (row < R && c0 < Kc) {
+          float* dst = out + row * ldo + c0;
+          if (c0 + 4 <= Kc) {
+            __builtin_nontemporal_store(f32x4{acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]},
+                                        reinterpret_cast<f32x4*>(dst));
+          } else {
+            const float v[4] = {acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]};
+            for (int q = 0; q < 4 && c0 + q < Kc; ++q) dst[q] = v[q];
+          }
+        }
+      }
+    return;
+  }
+  const int64_t mrow_v = MODE == SD_VNM ? (G + 1) / 2 : mrow;   // V:N:M nibbles: one per gathered group
+  if (gq < G) {
+    uint32_t mb[FM][16];   // the metadata byte of every output row of the lane, loaded up front
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        int64_t row = r0w + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
+        row = row < R ? row : R - 1;
+        mb[i][e] = meta[row * mrow_v + gq / 2];
+      }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = r0w + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
+        if (row < R) {
+          const uint32_t nib = (mb[i][e] >> (4 * (gq & 1))) & 0xF;
+          const float v0 = acc[i][0][e], v1 = acc[i][1][e], v2 = acc[i][2][e], v3 = acc[i][3][e];
+          const uint32_t p0 = nib & 3, p1 = (nib >> 2) & 3;
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          f32x2 o;
+          o[0] = p0 == 0 ? v0 : p0 == 1 ? v1 : p0 == 2 ? v2 : v3;
+          o[1] = p1 == 0 ? v0 : p1 == 1 ? v1 : p1 == 2 ? v2 : v3;
+          if constexpr (MODE == SD_VNM) {
+            if (relu) {
+              // ReLU's derivative at the kept activations: 1 where the bf16 value is > 0
+              const uint32_t hp = *reinterpret_cast<const uint32_t*>(hval + row * (2 * G) + 2 * gq);
+              o[0] = Elem<uint16_t>::positive((uint16_t)(hp & 0xFFFF)) ? o[0] : 0.f;
+              o[1] = Elem<uint16_t>::positive((uint16_t)(hp >> 16)) ? o[1] : 0.f;
+            }
+          }
+          __builtin_nontemporal_store(o, reinterpret_cast<f32x2*>(out + row * (Kc / 2) + 2 * gq));
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool WRITE_DT, int MODE = SD_NM>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
     const uint16_t* __restrict__ D, int64_t ldd, const uint16_t* __restrict__ X, int64_t ldx, int64_t R, int64_t Kc,
@@ -438,67 +511,208 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   }
   if (WRITE_DT) wait_vmcnt<0>();
 
-  // epilogue: lane l32 holds columns 4*l32 .. +3 of the wave's 128 = 2:4 group gq
-  const int64_t G = Kc / 4, mrow = (Kc + 7) / 8;
-  const int64_t gq = (n0 + wn * 128) / 4 + l32;
-  if constexpr (MODE == SD_DENSE) {
-    // every column: 16 contiguous bytes per lane and row (the 32 lanes of a row write 512 bytes)
-    const int64_t c0 = 4 * gq;
+  sd_epilogue<FM, MODE>(acc, m0 + wm * Cfg::WM, n0 + wn * 128, l32, aa, R, Kc, meta, out, hval, relu, ldo);
+}
+
+// ---------------------------------------------------------------------------
+// Four-wave path: 128 x 128 per wave on a 256 x 256 tile, the memory instructions issued between
+// the matrix instructions.
+//
+// Two LDS buffers of one 64-t stage (2 x 64 KB), filled by direct-to-LDS loads of whole 128-byte
+// rows (the swizzle and column placement of the kernel above: sd_swz, sd_xrow).  A stage is four
+// 16-t sub-steps of 16 v_mfma_f32_32x32x16_bf16 per wave; after every other matrix instruction
+// the wave reads one operand of the next sub-step from LDS, so no sub-step waits for its operands.
+// The barrier sits before the last sub-step: by then every wave has read all of the stage (the
+// last sub-step's operands are read during the one before), so the last sub-step reads the next
+// stage's first operands, and the buffer just left takes the loads of the stage after next: half
+// of them during that last sub-step, the other half during the next stage's first sub-step, one
+// after every other matrix instruction (issued faster, they queue in the vector-memory address
+// unit and hold the wave at the issue of the next).  One wave per SIMD: a wave's 256 fp32
+// accumulators sit in the accumulation registers.
+// ---------------------------------------------------------------------------
+constexpr int SR_A = 256 * TK * 2, SR_STAGE = 2 * SR_A;   // D and X parts of a stage: 32 KB each
+
+template <bool WRITE_DT, int MODE>
+__global__ __launch_bounds__(256) void sddmm_reg_kernel(const uint16_t* __restrict__ D, int64_t ldd,
+                                                        const uint16_t* __restrict__ X, int64_t ldx, int64_t R,
+                                                        int64_t Kc, int64_t Tn, const uint8_t* __restrict__ meta,
+                                                        float* __restrict__ out, uint16_t* __restrict__ Dt,
+                                                        int64_t lddt, int64_t ldo) {
+  static_assert(MODE == SD_NM || MODE == SD_DENSE, "the gathered mode keeps the direct-to-LDS kernel");
+  constexpr int FM = 4;
+  extern __shared__ __align__(1024) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int ntm = (int)((R + 255) / 256), ntn = (int)((Kc + 255) / 256);
+  const int nwg = ntm * ntn;
+  const int wg = xcd_remap(blockIdx.x, nwg);
+  constexpr int GM = 4;
+  const int grp = wg / (GM * ntn);
+  const int first_m = grp * GM;
+  const int gsz = (ntm - first_m) < GM ? (ntm - first_m) : GM;
+  const int within = wg - grp * GM * ntn;
+  const int tm = first_m + within % gsz, tn = within / gsz;
+  const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
+  const int KT = (int)(Tn / TK);
+
+  // load t of a wave: LDS rows 8 (8 wave + t) .. +7 of the D part (t < 8) or of the X part;
+  // lane -> row 8 (8 wave + t) + lane / 8, LDS chunk lane % 8 holding source chunk (lane % 8) ^ swz.
+  // Sources are 32-bit byte offsets from the stage's wave-uniform base (the dispatch checks that
+  // both operands are smaller than 4 GiB).
+  uint32_t off[16];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * Cfg::WM + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
-        if (row < R && c0 < Kc) {
-          float* dst = out + row * ldo + c0;
-          if (c0 + 4 <= Kc) {
-            __builtin_nontemporal_store(f32x4{acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]},
-                                        reinterpret_cast<f32x4*>(dst));
-          } else {
-            const float v[4] = {acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]};
-            for (int q = 0; q < 4 && c0 + q < Kc; ++q) dst[q] = v[q];
-          }
-        }
-      }
-    return;
+  for (int t = 0; t < 8; ++t) {
+    const int r = 8 * (8 * wave + t) + (lane >> 3);
+    const int c = (lane & 7) ^ sd_swz(r);
+    int64_t row = m0 + r;
+    row = row < R ? row : R - 1;
+    off[t] = (uint32_t)(2 * (row * ldd + 8 * c));
+    const int n = (r & ~127) | ((r & 31) << 2) | ((r & 127) >> 5);   // inverse of sd_xrow
+    int64_t col = n0 + n;
+    col = col < Kc ? col : Kc - 1;
+    off[8 + t] = (uint32_t)(2 * (col * ldx + 8 * c));
   }
-  const int64_t mrow_v = MODE == SD_VNM ? (G + 1) / 2 : mrow;   // V:N:M nibbles: one per gathered group
-  if (gq < G) {
-    uint32_t mb[FM][16];   // the metadata byte of every output row of the lane, loaded up front
+  const uint32_t lds_wave = lds_addr(smem) + (8 * wave) * 1024;
+  // load t (< 16) of stage kl into LDS buffer buf
+  auto dma = [&](int t, int kl, int buf) {
+    const uint16_t* base = (t < 8 ? D : X) + (int64_t)kl * TK;
+    dma16s(off[t], base, uniform(lds_wave + buf * SR_STAGE + (t < 8 ? 0 : SR_A) + (t & 7) * 1024));
+  };
+
+  f32x16 acc[FM][4];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        int64_t row = m0 + wm * Cfg::WM + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
-        row = row < R ? row : R - 1;
-        mb[i][e] = meta[row * mrow_v + gq / 2];
-      }
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int l32 = lane & 31, aa = lane >> 5;
+  // Fragment i's rows start at a multiple of 32, so every fragment's row l32 has the swizzle
+  // sd_swz(l32): one per-lane base per operand, fragments and buffers as constant offsets.
+  const int a_base = (wm * 128 + l32) * (TK * 2), b_base = SR_A + (wn * 128 + l32) * (TK * 2);
+  const int swz = sd_swz(l32);
+  // operand q of sub-step kk (q < 4: A fragment q, else B fragment q - 4)
+  auto read_op = [&](int buf, int kk, int q, bf16x8 (&a)[FM], bf16x8 (&b)[4]) {
+    const int co = buf * SR_STAGE + (((2 * kk + aa) ^ swz) << 4);
+    if (q < 4)
+      a[q] = *reinterpret_cast<const bf16x8*>(smem + a_base + co + q * 32 * (TK * 2));
+    else
+      b[q - 4] = *reinterpret_cast<const bf16x8*>(smem + b_base + co + (q - 4) * 32 * (TK * 2));
+  };
+  // One 16-t sub-step: 16 matrix instructions on (a, b); after the m-th, one LDS read of the next
+  // operands (m even: operand m/2 of sub-step kk_next of buffer rbuf, into an / bn; none when
+  // kk_next < 0) and other(m) (every m when EVERY == 1, odd m only when EVERY == 2): global loads
+  // or LDS writes of the stages in flight.  Scheduling barriers keep this order, so that each
+  // memory instruction issues while a matrix instruction runs.
+  auto substep = [&](auto every, const bf16x8 (&a)[FM], const bf16x8 (&b)[4], int rbuf, int kk_next,
+                     bf16x8 (&an)[FM], bf16x8 (&bn)[4], auto other) {
+    constexpr int EVERY = decltype(every)::value;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * Cfg::WM + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
-        if (row < R) {
-          const uint32_t nib = (mb[i][e] >> (4 * (gq & 1))) & 0xF;
-          const float v0 = acc[i][0][e], v1 = acc[i][1][e], v2 = acc[i][2][e], v3 = acc[i][3][e];
-          const uint32_t p0 = nib & 3, p1 = (nib >> 2) & 3;
-          typedef float f32x2 __attribute__((ext_vector_type(2)));
-          f32x2 o;
-          o[0] = p0 == 0 ? v0 : p0 == 1 ? v1 : p0 == 2 ? v2 : v3;
-          o[1] = p1 == 0 ? v0 : p1 == 1 ? v1 : p1 == 2 ? v2 : v3;
-          if constexpr (MODE == SD_VNM) {
-            if (relu) {
-              // ReLU's derivative at the kept activations: 1 where the bf16 value is > 0
-              const uint32_t hp = *reinterpret_cast<const uint32_t*>(hval + row * (2 * G) + 2 * gq);
-              o[0] = Elem<uint16_t>::positive((uint16_t)(hp & 0xFFFF)) ? o[0] : 0.f;
-              o[1] = Elem<uint16_t>::positive((uint16_t)(hp >> 16)) ? o[1] : 0.f;
-            }
-          }
-          __builtin_nontemporal_store(o, reinterpret_cast<f32x2*>(out + row * (Kc / 2) + 2 * gq));
-        }
+    for (int m = 0; m < 16; ++m) {
+      const int j = m >> 2, i = m & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if ((m & 1) == 0 && kk_next >= 0) read_op(rbuf, kk_next, m >> 1, an, bn);
+      if (EVERY == 1) other(m);
+      else if (m & 1) other(m >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Dt: stage kt of this row panel is written by the workgroup whose column tile is kt % ntn; all
+  // four waves, one 8 x 8 block per lane (as in the direct-to-LDS kernel)
+  auto transpose_stage = [&](int kt) {
+    const int tb = lane & 7, rb = 8 * wave + (lane >> 3);
+    const unsigned char* st = smem + (kt & 1) * SR_STAGE;
+    u32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * rb + i;
+      v[i] = *reinterpret_cast<const u32x4*>(st + r * (TK * 2) + ((tb ^ sd_swz(r)) << 4));
+    }
+    const int64_t col = m0 + 8 * rb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 d;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[j] = __builtin_amdgcn_perm(v[2 * j + 1][e >> 1], v[2 * j][e >> 1], sel);
+      uint16_t* dst = Dt + ((int64_t)kt * TK + 8 * tb + e) * lddt + col;
+      if (col + 8 <= R) {
+        __builtin_nontemporal_store(d, reinterpret_cast<u32x4*>(dst));
+      } else {
+        for (int q = 0; q < 8; ++q)
+          if (col + q < R) dst[q] = (uint16_t)(d[q >> 1] >> (16 * (q & 1)));
       }
     }
+  };
+
+  // Stage kt (a0 / b0: its sub-step-0 operands, read during the previous stage).  The wait before
+  // the barrier is for stage kt+1's loads (issued during the previous stage's last sub-step);
+  // a transposing wave's Dt stores of this stage are younger than them and may stay in flight
+  // (a whole panel's wave issues exactly kDtStores; in a partial last panel every wait is for all).
+  constexpr int kDtStores = 8;
+  const bool whole_panel = m0 + 256 <= R;
+  auto stage = [&](int kt, bf16x8 (&a0)[FM], bf16x8 (&b0)[4]) {
+    const int buf = kt & 1;
+    bf16x8 a1[FM], b1[4];
+    auto none = [&](int) {};
+    const int kn = kt + 1 < KT ? kt + 1 : KT - 1;   // past the end: a repeat that is never read
+    substep(std::integral_constant<int, 2>(), a0, b0, buf, 1, a1, b1, [&](int t) { dma(8 + t, kn, buf ^ 1); });
+    substep(std::integral_constant<int, 2>(), a1, b1, buf, 2, a0, b0, none);
+    substep(std::integral_constant<int, 2>(), a0, b0, buf, 3, a1, b1, none);
+    bool wrote = false;
+    if constexpr (WRITE_DT) {
+      if (kt % ntn == tn) {
+        transpose_stage(kt);
+        wrote = whole_panel;
+      }
+    }
+    if (wrote) wait_vmcnt<kDtStores>(); else wait_vmcnt<0>();
+    lds_barrier();   // stage kt+1 is in LDS for every wave; every wave has read all it needs of stage kt
+    const int kl = kt + 2 < KT ? kt + 2 : KT - 1;   // past the end: a repeat that is never read
+    substep(std::integral_constant<int, 2>(), a1, b1, buf ^ 1, 0, a0, b0, [&](int t) { dma(t, kl, buf); });
+  };
+
+  // KT is even and at least 2 (the dispatch checks Tn % 128 == 0)
+#pragma unroll
+  for (int t = 0; t < 16; ++t) dma(t, 0, 0);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) dma(t, 1, 1);
+  wait_vmcnt<8>();   // stage 0
+  lds_barrier();
+  bf16x8 a0[FM], b0[4];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) read_op(0, 0, q, a0, b0);
+  for (int kt = 0; kt < KT; kt += 2) {
+    stage(kt, a0, b0);
+    stage(kt + 1, a0, b0);
   }
+  wait_vmcnt<0>();   // drain: no load may land in LDS after the workgroup ends
+
+  sd_epilogue<FM, MODE>(acc, m0 + wm * 128, n0 + wn * 128, l32, aa, R, Kc, meta, out, nullptr, 0, ldo);
+}
+
+template <bool WRITE_DT, int MODE>
+static hipError_t run_sddmm_reg(const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
+                                int64_t Tn, const uint8_t* meta, float* out, void* Dt, int64_t lddt, int64_t ldo,
+                                hipStream_t s) {
+  const size_t lds = 2 * (size_t)SR_STAGE;
+  auto kern = sddmm_reg_kernel<WRITE_DT, MODE>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const int64_t ntiles = ((R + 255) / 256) * ((Kc + 255) / 256);
+  hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(256), lds, s, (const uint16_t*)D, ldd, (const uint16_t*)X,
+                     ldx, R, Kc, Tn, meta, out, (uint16_t*)Dt, lddt, ldo);
+  return hipGetLastError();
+}
+
+// The register-staged kernel takes pairs of 64-t stages and addresses each operand with 32-bit
+// byte offsets from its base.
+static bool sd_reg_ok(int64_t R, int64_t ldd, int64_t Kc, int64_t ldx, int64_t Tn) {
+  if (env_is_one("NMSPARSE_SDDMM_DMA")) return false;
+  return Tn % (2 * TK) == 0 && R * ldd * 2 < (int64_t(1) << 32) && Kc * ldx * 2 < (int64_t(1) << 32);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool WRITE_DT, int MODE = SD_NM>
@@ -537,7 +751,9 @@ hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, in
   const bool staged = tier && tier[0] == '1';
   if (dt == DT_BF16 && !force && !staged && Tn % TK == 0 && ldd % 8 == 0 && ldx % 8 == 0 && (uintptr_t)D % 16 == 0 &&
       (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0)
-    return run_sddmm_dma<256, 256, 4, 2, 2, false>(D, ldd, X, ldx, R, Kc, Tn, meta, out, nullptr, 0, s);
+    return sd_reg_ok(R, ldd, Kc, ldx, Tn)
+               ? run_sddmm_reg<false, SD_NM>(D, ldd, X, ldx, R, Kc, Tn, meta, out, nullptr, 0, 0, s)
+               : run_sddmm_dma<256, 256, 4, 2, 2, false>(D, ldd, X, ldx, R, Kc, Tn, meta, out, nullptr, 0, s);
   if (dt == DT_BF16 && !force && Tn % 8 == 0 && ldd % 8 == 0 && ldx % 8 == 0 && (uintptr_t)D % 16 == 0 &&
       (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0)
     return run_sddmm_mfma<256, 128, 128, 64>(D, ldd, X, ldx, R, Kc, Tn, meta, out, s);
@@ -558,7 +774,9 @@ hipError_t launch_sddmm_nm_dt(int dt, const void* D, int64_t ldd, const void* X,
   if (dt == DT_BF16 && !force_generic() && !env_is_one("NMSPARSE_SPMM_TIER") && Tn % TK == 0 && ldd % 8 == 0 &&
       ldx % 8 == 0 && (uintptr_t)D % 16 == 0 && (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0 &&
       (uintptr_t)Dt % 16 == 0 && lddt % 8 == 0)
-    return run_sddmm_dma<256, 256, 4, 2, 2, true>(D, ldd, X, ldx, R, Kc, Tn, meta, out, Dt, lddt, s);
+    return sd_reg_ok(R, ldd, Kc, ldx, Tn)
+               ? run_sddmm_reg<true, SD_NM>(D, ldd, X, ldx, R, Kc, Tn, meta, out, Dt, lddt, 0, s)
+               : run_sddmm_dma<256, 256, 4, 2, 2, true>(D, ldd, X, ldx, R, Kc, Tn, meta, out, Dt, lddt, s);
   const hipError_t e = launch_sddmm_nm(dt, D, ldd, X, ldx, R, Kc, Tn, meta, out, s);
   if (e != hipSuccess) return e;
   return launch_nm_transpose(dt, D, ldd, R, Tn, Dt, lddt, s);
@@ -594,6 +812,8 @@ bool dense_nt_fast_ok(const void* A, int64_t lda, const void* B, int64_t ldb, co
 
 hipError_t launch_dense_nt(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t R, int64_t Kc, int64_t Tn,
                            float* out, int64_t ldo, hipStream_t s) {
+  if (sd_reg_ok(R, lda, Kc, ldb, Tn))
+    return run_sddmm_reg<false, SD_DENSE>(A, lda, B, ldb, R, Kc, Tn, nullptr, out, nullptr, 0, ldo, s);
   return run_sddmm_dma<256, 256, 4, 2, 2, false, SD_DENSE>(A, lda, B, ldb, R, Kc, Tn, nullptr, out, nullptr, 0, s,
                                                            nullptr, 1, 4, nullptr, 0, ldo);
 }

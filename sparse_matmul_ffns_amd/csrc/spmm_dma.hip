@@ -53,32 +53,9 @@
 
 namespace nms {
 
-// B rows are loaded with inline-assembly loads as well: their completion is
-// counted by the same explicit vmcnt waits as the direct loads, and the wait
-// takes the destination registers as in/out operands, so nothing reads them
-// before the data has arrived.
-__device__ __forceinline__ u32x4 load16_async(const void* g) {
-  u32x4 r;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(g));
-  return r;
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_regs(u32x4 (&rb)[8]) {
-  asm volatile("s_waitcnt vmcnt(%8)"
-               : "+v"(rb[0]), "+v"(rb[1]), "+v"(rb[2]), "+v"(rb[3]), "+v"(rb[4]), "+v"(rb[5]), "+v"(rb[6]),
-                 "+v"(rb[7])
-               : "n"(N)
-               : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_regs(u32x4 (&r0)[8], u32x4 (&r1)[8]) {
-  asm volatile("s_waitcnt vmcnt(%16)"
-               : "+v"(r0[0]), "+v"(r0[1]), "+v"(r0[2]), "+v"(r0[3]), "+v"(r0[4]), "+v"(r0[5]), "+v"(r0[6]),
-                 "+v"(r0[7]), "+v"(r1[0]), "+v"(r1[1]), "+v"(r1[2]), "+v"(r1[3]), "+v"(r1[4]), "+v"(r1[5]),
-                 "+v"(r1[6]), "+v"(r1[7])
-               : "n"(N)
-               : "memory");
-}
+// B rows are loaded with inline-assembly loads as well (load16_async, dma.hpp): their completion
+// is counted by the same explicit vmcnt waits as the direct loads, and the wait takes the
+// destination registers as in/out operands, so nothing reads them before the data has arrived.
 
 // Swizzled 16-byte chunk position of chunk c in B row n (the LDS row of tile column n).  Chosen
 // by measurement on gfx950: with it, 16 consecutive rows read at one chunk index, and the
