@@ -530,15 +530,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
 // unit and hold the wave at the issue of the next).  One wave per SIMD: a wave's 256 fp32
 // accumulators sit in the accumulation registers.
 // ---------------------------------------------------------------------------
-constexpr int SR_A = 256 * TK * 2, SR_STAGE = 2 * SR_A;   // D and X parts of a stage: 32 KB each
+constexpr int W4_A = 256 * TK * 2, W4_STAGE = 2 * W4_A;   // D and X parts of a stage: 32 KB each
 
 template <bool WRITE_DT, int MODE>
-__global__ __launch_bounds__(256) void sddmm_reg_kernel(const uint16_t* __restrict__ D, int64_t ldd,
+__global__ __launch_bounds__(256) void sddmm_w4_kernel(const uint16_t* __restrict__ D, int64_t ldd,
                                                         const uint16_t* __restrict__ X, int64_t ldx, int64_t R,
                                                         int64_t Kc, int64_t Tn, const uint8_t* __restrict__ meta,
                                                         float* __restrict__ out, uint16_t* __restrict__ Dt,
                                                         int64_t lddt, int64_t ldo) {
-  static_assert(MODE == SD_NM || MODE == SD_DENSE, "the gathered mode keeps the direct-to-LDS kernel");
+  static_assert(MODE == SD_NM || MODE == SD_DENSE, "the gathered (V:N:M) mode keeps the eight-wave kernel");
   constexpr int FM = 4;
   extern __shared__ __align__(1024) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(256) void sddmm_reg_kernel(const uint16_t* __restri
   // load t (< 16) of stage kl into LDS buffer buf
   auto dma = [&](int t, int kl, int buf) {
     const uint16_t* base = (t < 8 ? D : X) + (int64_t)kl * TK;
-    dma16s(off[t], base, uniform(lds_wave + buf * SR_STAGE + (t < 8 ? 0 : SR_A) + (t & 7) * 1024));
+    dma16s(off[t], base, uniform(lds_wave + buf * W4_STAGE + (t < 8 ? 0 : W4_A) + (t & 7) * 1024));
   };
 
   f32x16 acc[FM][4];
@@ -592,11 +592,11 @@ __global__ __launch_bounds__(256) void sddmm_reg_kernel(const uint16_t* __restri
   const int l32 = lane & 31, aa = lane >> 5;
   // Fragment i's rows start at a multiple of 32, so every fragment's row l32 has the swizzle
   // sd_swz(l32): one per-lane base per operand, fragments and buffers as constant offsets.
-  const int a_base = (wm * 128 + l32) * (TK * 2), b_base = SR_A + (wn * 128 + l32) * (TK * 2);
+  const int a_base = (wm * 128 + l32) * (TK * 2), b_base = W4_A + (wn * 128 + l32) * (TK * 2);
   const int swz = sd_swz(l32);
   // operand q of sub-step kk (q < 4: A fragment q, else B fragment q - 4)
   auto read_op = [&](int buf, int kk, int q, bf16x8 (&a)[FM], bf16x8 (&b)[4]) {
-    const int co = buf * SR_STAGE + (((2 * kk + aa) ^ swz) << 4);
+    const int co = buf * W4_STAGE + (((2 * kk + aa) ^ swz) << 4);
     if (q < 4)
       a[q] = *reinterpret_cast<const bf16x8*>(smem + a_base + co + q * 32 * (TK * 2));
     else
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(256) void sddmm_reg_kernel(const uint16_t* __restri
   // four waves, one 8 x 8 block per lane (as in the direct-to-LDS kernel)
   auto transpose_stage = [&](int kt) {
     const int tb = lane & 7, rb = 8 * wave + (lane >> 3);
-    const unsigned char* st = smem + (kt & 1) * SR_STAGE;
+    const unsigned char* st = smem + (kt & 1) * W4_STAGE;
     u32x4 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -696,11 +696,11 @@ __global__ __launch_bounds__(256) void sddmm_reg_kernel(const uint16_t* __restri
 }
 
 template <bool WRITE_DT, int MODE>
-static hipError_t run_sddmm_reg(const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
+static hipError_t run_sddmm_w4(const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
                                 int64_t Tn, const uint8_t* meta, float* out, void* Dt, int64_t lddt, int64_t ldo,
                                 hipStream_t s) {
-  const size_t lds = 2 * (size_t)SR_STAGE;
-  auto kern = sddmm_reg_kernel<WRITE_DT, MODE>;
+  const size_t lds = 2 * (size_t)W4_STAGE;
+  auto kern = sddmm_w4_kernel<WRITE_DT, MODE>;
   (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int64_t ntiles = ((R + 255) / 256) * ((Kc + 255) / 256);
   hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(256), lds, s, (const uint16_t*)D, ldd, (const uint16_t*)X,
@@ -708,9 +708,9 @@ static hipError_t run_sddmm_reg(const void* D, int64_t ldd, const void* X, int64
   return hipGetLastError();
 }
 
-// The register-staged kernel takes pairs of 64-t stages and addresses each operand with 32-bit
+// The four-wave kernel takes pairs of 64-t stages and addresses each operand with 32-bit
 // byte offsets from its base.
-static bool sd_reg_ok(int64_t R, int64_t ldd, int64_t Kc, int64_t ldx, int64_t Tn) {
+static bool sd_w4_ok(int64_t R, int64_t ldd, int64_t Kc, int64_t ldx, int64_t Tn) {
   if (env_is_one("NMSPARSE_SDDMM_DMA")) return false;
   return Tn % (2 * TK) == 0 && R * ldd * 2 < (int64_t(1) << 32) && Kc * ldx * 2 < (int64_t(1) << 32);
 }
@@ -751,8 +751,8 @@ hipError_t launch_sddmm_nm(int dt, const void* D, int64_t ldd, const void* X, in
   const bool staged = tier && tier[0] == '1';
   if (dt == DT_BF16 && !force && !staged && Tn % TK == 0 && ldd % 8 == 0 && ldx % 8 == 0 && (uintptr_t)D % 16 == 0 &&
       (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0)
-    return sd_reg_ok(R, ldd, Kc, ldx, Tn)
-               ? run_sddmm_reg<false, SD_NM>(D, ldd, X, ldx, R, Kc, Tn, meta, out, nullptr, 0, 0, s)
+    return sd_w4_ok(R, ldd, Kc, ldx, Tn)
+               ? run_sddmm_w4<false, SD_NM>(D, ldd, X, ldx, R, Kc, Tn, meta, out, nullptr, 0, 0, s)
                : run_sddmm_dma<256, 256, 4, 2, 2, false>(D, ldd, X, ldx, R, Kc, Tn, meta, out, nullptr, 0, s);
   if (dt == DT_BF16 && !force && Tn % 8 == 0 && ldd % 8 == 0 && ldx % 8 == 0 && (uintptr_t)D % 16 == 0 &&
       (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0)
@@ -774,8 +774,8 @@ hipError_t launch_sddmm_nm_dt(int dt, const void* D, int64_t ldd, const void* X,
   if (dt == DT_BF16 && !force_generic() && !env_is_one("NMSPARSE_SPMM_TIER") && Tn % TK == 0 && ldd % 8 == 0 &&
       ldx % 8 == 0 && (uintptr_t)D % 16 == 0 && (uintptr_t)X % 16 == 0 && (uintptr_t)out % 8 == 0 &&
       (uintptr_t)Dt % 16 == 0 && lddt % 8 == 0)
-    return sd_reg_ok(R, ldd, Kc, ldx, Tn)
-               ? run_sddmm_reg<true, SD_NM>(D, ldd, X, ldx, R, Kc, Tn, meta, out, Dt, lddt, 0, s)
+    return sd_w4_ok(R, ldd, Kc, ldx, Tn)
+               ? run_sddmm_w4<true, SD_NM>(D, ldd, X, ldx, R, Kc, Tn, meta, out, Dt, lddt, 0, s)
                : run_sddmm_dma<256, 256, 4, 2, 2, true>(D, ldd, X, ldx, R, Kc, Tn, meta, out, Dt, lddt, s);
   const hipError_t e = launch_sddmm_nm(dt, D, ldd, X, ldx, R, Kc, Tn, meta, out, s);
   if (e != hipSuccess) return e;
@@ -812,8 +812,8 @@ bool dense_nt_fast_ok(const void* A, int64_t lda, const void* B, int64_t ldb, co
 
 hipError_t launch_dense_nt(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t R, int64_t Kc, int64_t Tn,
                            float* out, int64_t ldo, hipStream_t s) {
-  if (sd_reg_ok(R, lda, Kc, ldb, Tn))
-    return run_sddmm_reg<false, SD_DENSE>(A, lda, B, ldb, R, Kc, Tn, nullptr, out, nullptr, 0, ldo, s);
+  if (sd_w4_ok(R, lda, Kc, ldb, Tn))
+    return run_sddmm_w4<false, SD_DENSE>(A, lda, B, ldb, R, Kc, Tn, nullptr, out, nullptr, 0, ldo, s);
   return run_sddmm_dma<256, 256, 4, 2, 2, false, SD_DENSE>(A, lda, B, ldb, R, Kc, Tn, nullptr, out, nullptr, 0, s,
                                                            nullptr, 1, 4, nullptr, 0, ldo);
 }
