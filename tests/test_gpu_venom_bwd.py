@@ -38,6 +38,9 @@ def _dz_bound(dY, Wd, hm, hc, T, F, V, M, dtype):
 SDDMM_VENOM_CASES = [
     # (T, F, Nc, V, M): V % 128 == 0 and Nc % 64 == 0 take the matrix-core kernel
     (256, 512, 128, 128, 8),      # one 512-wide gathered tile, only 256 columns of it in range
+    (384, 2048, 256, 128, 8),     # three V-blocks, two column tiles, four stages
+    (256, 1024, 384, 256, 16),    # M = 16, six stages
+    (256, 256, 256, 128, 4),      # M = 4, four stages
     (384, 2048, 192, 128, 8),     # three V-blocks, two column tiles, three 64-wide stages
     (256, 256, 64, 128, 4),       # M = 4: colsel 0..3
     (256, 1024, 128, 256, 16),    # M = 16, a 256-token V-block over two row tiles
