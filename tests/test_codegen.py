@@ -356,3 +356,20 @@ def test_checker_resolves_uniform_exec_branches():
     divergent = "v_cmp_gt_u32_e32 vcc, 8, v1\n    s_and_saveexec_b64 s[8:9], vcc\n" + loop
     bad = async_register_violations(divergent.splitlines())
     assert bad and "v2" in bad[0][1]
+
+
+def test_n8_sorting_network_sorts_every_input():
+    """The 8-input comparator network of the one-pass N:8 prune (csrc/prune.hip) sorts descending.
+    By the 0-1 principle a comparator network sorts every input iff it sorts all 2^8 inputs of
+    zeros and ones, so the 256 cases decide it."""
+    src = open(os.path.join(CSRC, "prune.hip")).read()
+    i = src.index("8-input sorting network of 19 comparators")
+    block = src[i:src.index("thr = srt[N - 1]", i)]
+    pairs = [(int(a), int(b)) for a, b in re.findall(r"cx\((\d+), (\d+)\)", block)]
+    assert len(pairs) == 19
+    for bits in range(256):
+        v = [(bits >> p) & 1 for p in range(8)]
+        for a, b in pairs:
+            hi, lo = max(v[a], v[b]), min(v[a], v[b])
+            v[a], v[b] = hi, lo
+        assert v == sorted(v, reverse=True), (bits, v)
