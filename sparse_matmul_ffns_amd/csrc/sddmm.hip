@@ -519,18 +519,82 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
 // the matrix instructions.
 //
 // Two LDS buffers of one 64-t stage (2 x 64 KB), filled by direct-to-LDS loads of whole 128-byte
-// rows (the swizzle and column placement of the kernel above: sd_swz, sd_xrow).  A stage is four
-// 16-t sub-steps of 16 v_mfma_f32_32x32x16_bf16 per wave; after every other matrix instruction
-// the wave reads one operand of the next sub-step from LDS, so no sub-step waits for its operands.
-// The barrier sits before the last sub-step: by then every wave has read all of the stage (the
-// last sub-step's operands are read during the one before), so the last sub-step reads the next
-// stage's first operands, and the buffer just left takes the loads of the stage after next: half
-// of them during that last sub-step, the other half during the next stage's first sub-step, one
-// after every other matrix instruction (issued faster, they queue in the vector-memory address
-// unit and hold the wave at the issue of the next).  One wave per SIMD: a wave's 256 fp32
-// accumulators sit in the accumulation registers.
+// rows (the swizzle of the kernel above, sd_swz; X rows placed so that every lane's fragments
+// hold the four columns of its 2:4 groups).  A stage is two 32-t sub-steps of 64
+// v_mfma_f32_16x16x32_bf16 per wave (8 x 8 fragments of 16 x 16); after every fourth matrix
+// instruction the wave reads one operand of the next sub-step from LDS, so no sub-step waits for
+// its operands.  The barrier sits between the two sub-steps: by then every wave has read all of
+// the stage, so the second sub-step reads the next stage's first operands, and the buffer just
+// left takes the loads of the stage after next: half of them during that sub-step, the other half
+// during the next stage's first, one after every fourth matrix instruction of the first 32 (issued
+// faster, they queue in the vector-memory address unit and hold the wave at the issue of the
+// next).  One wave per SIMD: a wave's 256 fp32 accumulators sit in the accumulation registers.
+// Under the chip's power limit the 16 x 16 x 32 instruction sustains ~10% more flops than the
+// 32 x 32 x 16 one (1784 against 1617 TFLOP/s in loops of nothing else on changing operands).
 // ---------------------------------------------------------------------------
 constexpr int W4_A = 256 * TK * 2, W4_STAGE = 2 * W4_A;   // D and X parts of a stage: 32 KB each
+
+// Epilogue of the four-wave kernel: 16 x 16 fragments (i, j) of a wave's 128 rows from r0w and 128
+// output columns from c0w; lane l holds rows 16 i + 4 (l / 16) + e (e < 4) and, in fragment j, column
+// c0w + 64 (j / 4) + 4 (l % 16) + j % 4, so lanes hold every column of 2:4 groups c0w/4 + 16 q +
+// l % 16 (q < 2).  SD_DENSE stores all four (16 bytes per row), SD_NM the two the nibble keeps.
+template <int MODE>
+__device__ __forceinline__ void sd_epilogue16(const f32x4 (&acc)[8][8], int64_t r0w, int64_t c0w, int l16, int aq,
+                                              int64_t R, int64_t Kc, const uint8_t* __restrict__ meta,
+                                              float* __restrict__ out, int64_t ldo) {
+  const int64_t G = Kc / 4, mrow = (Kc + 7) / 8;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t gq = c0w / 4 + 16 * q + l16;
+    if constexpr (MODE == SD_DENSE) {
+      const int64_t c0 = 4 * gq;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t row = r0w + 16 * i + 4 * aq + e;
+          if (row < R && c0 < Kc) {
+            float* dst = out + row * ldo + c0;
+            const float v[4] = {acc[i][4 * q][e], acc[i][4 * q + 1][e], acc[i][4 * q + 2][e], acc[i][4 * q + 3][e]};
+            if (c0 + 4 <= Kc) {
+              __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(dst));
+            } else {
+              for (int u = 0; u < 4 && c0 + u < Kc; ++u) dst[u] = v[u];
+            }
+          }
+        }
+    } else {
+      if (gq < G) {
+        uint32_t mb[8][4];   // the metadata byte of every output row of the lane, loaded up front
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            int64_t row = r0w + 16 * i + 4 * aq + e;
+            row = row < R ? row : R - 1;
+            mb[i][e] = meta[row * mrow + gq / 2];
+          }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t row = r0w + 16 * i + 4 * aq + e;
+            if (row < R) {
+              const uint32_t nib = (mb[i][e] >> (4 * (gq & 1))) & 0xF;
+              const float v0 = acc[i][4 * q][e], v1 = acc[i][4 * q + 1][e], v2 = acc[i][4 * q + 2][e],
+                          v3 = acc[i][4 * q + 3][e];
+              const uint32_t p0 = nib & 3, p1 = (nib >> 2) & 3;
+              typedef float f32x2 __attribute__((ext_vector_type(2)));
+              f32x2 o;
+              o[0] = p0 == 0 ? v0 : p0 == 1 ? v1 : p0 == 2 ? v2 : v3;
+              o[1] = p1 == 0 ? v0 : p1 == 1 ? v1 : p1 == 2 ? v2 : v3;
+              __builtin_nontemporal_store(o, reinterpret_cast<f32x2*>(out + row * (Kc / 2) + 2 * gq));
+            }
+          }
+      }
+    }
+  }
+}
 
 template <bool WRITE_DT, int MODE>
 __global__ __launch_bounds__(256) void sddmm_w4_kernel(const uint16_t* __restrict__ D, int64_t ldd,
@@ -539,7 +603,7 @@ __global__ __launch_bounds__(256) void sddmm_w4_kernel(const uint16_t* __restric
                                                         float* __restrict__ out, uint16_t* __restrict__ Dt,
                                                         int64_t lddt, int64_t ldo) {
   static_assert(MODE == SD_NM || MODE == SD_DENSE, "the gathered (V:N:M) mode keeps the eight-wave kernel");
-  constexpr int FM = 4;
+  constexpr int FM = 8, FN = 8;   // 16 x 16 fragments of the wave's 128 x 128
   extern __shared__ __align__(1024) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -569,7 +633,7 @@ __global__ __launch_bounds__(256) void sddmm_w4_kernel(const uint16_t* __restric
     int64_t row = m0 + r;
     row = row < R ? row : R - 1;
     off[t] = (uint32_t)(2 * (row * ldd + 8 * c));
-    const int n = (r & ~127) | ((r & 31) << 2) | ((r & 127) >> 5);   // inverse of sd_xrow
+    const int n = (r & ~63) | ((r & 15) << 2) | ((r >> 4) & 3);   // tile column of LDS row r
     int64_t col = n0 + n;
     col = col < Kc ? col : Kc - 1;
     off[8 + t] = (uint32_t)(2 * (col * ldx + 8 * c));
@@ -581,43 +645,44 @@ __global__ __launch_bounds__(256) void sddmm_w4_kernel(const uint16_t* __restric
     dma16s(off[t], base, uniform(lds_wave + buf * W4_STAGE + (t < 8 ? 0 : W4_A) + (t & 7) * 1024));
   };
 
-  f32x16 acc[FM][4];
+  f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
 
-  const int l32 = lane & 31, aa = lane >> 5;
-  // Fragment i's rows start at a multiple of 32, so every fragment's row l32 has the swizzle
-  // sd_swz(l32): one per-lane base per operand, fragments and buffers as constant offsets.
-  const int a_base = (wm * 128 + l32) * (TK * 2), b_base = W4_A + (wn * 128 + l32) * (TK * 2);
-  const int swz = sd_swz(l32);
-  // operand q of sub-step kk (q < 4: A fragment q, else B fragment q - 4)
-  auto read_op = [&](int buf, int kk, int q, bf16x8 (&a)[FM], bf16x8 (&b)[4]) {
-    const int co = buf * W4_STAGE + (((2 * kk + aa) ^ swz) << 4);
-    if (q < 4)
-      a[q] = *reinterpret_cast<const bf16x8*>(smem + a_base + co + q * 32 * (TK * 2));
+  const int l16 = lane & 15, aq = lane >> 4;
+  // Fragment i's rows start at a multiple of 16, so every fragment's row l16 has the swizzle
+  // sd_swz(l16): one per-lane base per operand, fragments and buffers as constant offsets.
+  const int a_base = (wm * 128 + l16) * (TK * 2), b_base = W4_A + (wn * 128 + l16) * (TK * 2);
+  const int swz = sd_swz(l16);
+  // operand q of sub-step kk (32 t; q < 8: A fragment q, else B fragment q - 8): lane l holds row
+  // (column) l % 16 of the fragment, t = 32 kk + 8 (l / 16) .. +7
+  auto read_op = [&](int buf, int kk, int q, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+    const int co = buf * W4_STAGE + (((4 * kk + aq) ^ swz) << 4);
+    if (q < 8)
+      a[q] = *reinterpret_cast<const bf16x8*>(smem + a_base + co + q * 16 * (TK * 2));
     else
-      b[q - 4] = *reinterpret_cast<const bf16x8*>(smem + b_base + co + (q - 4) * 32 * (TK * 2));
+      b[q - 8] = *reinterpret_cast<const bf16x8*>(smem + b_base + co + (q - 8) * 16 * (TK * 2));
   };
-  // One 16-t sub-step: 16 matrix instructions on (a, b); after the m-th, one LDS read of the next
-  // operands (m even: operand m/2 of sub-step kk_next of buffer rbuf, into an / bn; none when
-  // kk_next < 0) and other(m) (every m when EVERY == 1, odd m only when EVERY == 2): global loads
-  // or LDS writes of the stages in flight.  Scheduling barriers keep this order, so that each
-  // memory instruction issues while a matrix instruction runs.
-  auto substep = [&](auto every, const bf16x8 (&a)[FM], const bf16x8 (&b)[4], int rbuf, int kk_next,
-                     bf16x8 (&an)[FM], bf16x8 (&bn)[4], auto other) {
-    constexpr int EVERY = decltype(every)::value;
+  // One 32-t sub-step: 64 matrix instructions on (a, b), B fragment j outer; after every fourth,
+  // one LDS read of the next operands (operand m/4 of sub-step kk_next of buffer rbuf, into
+  // an / bn; the A fragments first, none when kk_next < 0), and after every fourth from the
+  // second on (the first 32 only) other(0 .. 7): loads of a stage in flight.  Scheduling barriers
+  // keep this order, so that each memory instruction issues while a matrix instruction runs.
+  auto substep = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN], int rbuf, int kk_next, bf16x8 (&an)[FM],
+                     bf16x8 (&bn)[FN], auto other) {
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int j = m >> 2, i = m & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int m = 0; m < 64; ++m) {
+      const int j = m >> 3, i = m & 7;
+      // the accumulator tied in and out of the instruction in the accumulation registers (as a
+      // builtin, the compiler moves the 64 small accumulators between registers every iteration)
+      asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(a[i]), "v"(b[j]));
       __builtin_amdgcn_sched_barrier(0);
-      if ((m & 1) == 0 && kk_next >= 0) read_op(rbuf, kk_next, m >> 1, an, bn);
-      if (EVERY == 1) other(m);
-      else if (m & 1) other(m >> 1);
+      if ((m & 3) == 0 && kk_next >= 0) read_op(rbuf, kk_next, m >> 2, an, bn);
+      if ((m & 3) == 2 && m < 32) other(m >> 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -655,14 +720,11 @@ __global__ __launch_bounds__(256) void sddmm_w4_kernel(const uint16_t* __restric
   // (a whole panel's wave issues exactly kDtStores; in a partial last panel every wait is for all).
   constexpr int kDtStores = 8;
   const bool whole_panel = m0 + 256 <= R;
-  auto stage = [&](int kt, bf16x8 (&a0)[FM], bf16x8 (&b0)[4]) {
+  auto stage = [&](int kt, bf16x8 (&a0)[FM], bf16x8 (&b0)[FN]) {
     const int buf = kt & 1;
-    bf16x8 a1[FM], b1[4];
-    auto none = [&](int) {};
+    bf16x8 a1[FM], b1[FN];
     const int kn = kt + 1 < KT ? kt + 1 : KT - 1;   // past the end: a repeat that is never read
-    substep(std::integral_constant<int, 2>(), a0, b0, buf, 1, a1, b1, [&](int t) { dma(8 + t, kn, buf ^ 1); });
-    substep(std::integral_constant<int, 2>(), a1, b1, buf, 2, a0, b0, none);
-    substep(std::integral_constant<int, 2>(), a0, b0, buf, 3, a1, b1, none);
+    substep(a0, b0, buf, 1, a1, b1, [&](int t) { dma(8 + t, kn, buf ^ 1); });
     bool wrote = false;
     if constexpr (WRITE_DT) {
       if (kt % ntn == tn) {
@@ -673,7 +735,7 @@ __global__ __launch_bounds__(256) void sddmm_w4_kernel(const uint16_t* __restric
     if (wrote) wait_vmcnt<kDtStores>(); else wait_vmcnt<0>();
     lds_barrier();   // stage kt+1 is in LDS for every wave; every wave has read all it needs of stage kt
     const int kl = kt + 2 < KT ? kt + 2 : KT - 1;   // past the end: a repeat that is never read
-    substep(std::integral_constant<int, 2>(), a1, b1, buf ^ 1, 0, a0, b0, [&](int t) { dma(t, kl, buf); });
+    substep(a1, b1, buf ^ 1, 0, a0, b0, [&](int t) { dma(t, kl, buf); });
   };
 
   // KT is even and at least 2 (the dispatch checks Tn % 128 == 0)
@@ -683,16 +745,19 @@ __global__ __launch_bounds__(256) void sddmm_w4_kernel(const uint16_t* __restric
   for (int t = 0; t < 8; ++t) dma(t, 1, 1);
   wait_vmcnt<8>();   // stage 0
   lds_barrier();
-  bf16x8 a0[FM], b0[4];
+  bf16x8 a0[FM], b0[FN];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) read_op(0, 0, q, a0, b0);
+  for (int q = 0; q < 16; ++q) read_op(0, 0, q, a0, b0);
   for (int kt = 0; kt < KT; kt += 2) {
     stage(kt, a0, b0);
     stage(kt + 1, a0, b0);
   }
   wait_vmcnt<0>();   // drain: no load may land in LDS after the workgroup ends
 
-  sd_epilogue<FM, MODE>(acc, m0 + wm * 128, n0 + wn * 128, l32, aa, R, Kc, meta, out, nullptr, 0, ldo);
+  // the last matrix instructions' results before any other instruction reads them (the compiler does
+  // not see the instructions inside the assembly statements)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  sd_epilogue16<MODE>(acc, m0 + wm * 128, n0 + wn * 128, l16, aq, R, Kc, meta, out, ldo);
 }
 
 template <bool WRITE_DT, int MODE>
