@@ -216,24 +216,20 @@ __global__ __launch_bounds__(256) void sddmm_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// pipelined path: direct-to-LDS loads, v_mfma_f32_32x32x16_bf16.
+// pipelined path: direct-to-LDS loads, v_mfma_f32_16x16x32_bf16.
 //
-// v_mfma_f32_32x32x16_bf16 on gfx950: lane l holds A row l%32 and B column
-// l%32, k = 8*(l/32)..+7; the result holds column l%32 and, in element e, row
-// 8*(e/4) + 4*(l/32) + e%4.  A wave owns 64 rows x 128 output columns; its
-// four B fragments j = 0..3 map lane c to output column 4c + j, so lane c holds
-// every column of 2:4 group c and selects two of them by the group's nibble.
-// Tiles are staged per 64 t (128-byte rows, whole cache lines) in two buffers,
-// loaded with direct-to-LDS dwordx4 loads; X rows are placed so that fragment
-// j's 32 rows are consecutive in LDS, and the 16-byte chunks of LDS row r are
-// XOR-swizzled by (r >> 1) & 7, which keeps the ds_read_b128 operand reads of
-// 16 consecutive rows free of bank conflicts.
+// A wave owns WM rows x 128 output columns as 16 x 16 fragments; fragment j
+// (of 8) maps lane c (= l % 16) to output column 64 (j / 4) + 4 c + j % 4, so
+// every lane holds all four columns of its 2:4 groups and selects two of them
+// by the group's nibble.  Tiles are staged per 64 t (128-byte rows, whole
+// cache lines) in two buffers, loaded with direct-to-LDS dwordx4 loads; X rows
+// are placed so that each fragment's 16 rows are consecutive in LDS, and the
+// 16-byte chunks of LDS row r are XOR-swizzled by (r >> 1) & 7, which keeps the
+// ds_read_b128 operand reads of 16 consecutive rows free of bank conflicts.
 // ---------------------------------------------------------------------------
 constexpr int TK = 64;   // t per stage
 
 __device__ __forceinline__ int sd_swz(int r) { return (r >> 1) & 7; }
-// LDS row of output column n (within a 128-column wave group): fragment j = n%4, lane c = n/4
-__device__ __forceinline__ int sd_xrow(int n) { return (n & ~127) | ((n & 3) << 5) | ((n & 127) >> 2); }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 struct SdCfg {
@@ -265,72 +261,74 @@ struct SdCfg {
 // SD_DENSE -- out[r][c] = (D X^T)[r][c] for every column, row stride ldo (a plain NT GEMM).
 enum { SD_NM = 0, SD_VNM = 1, SD_DENSE = 2 };
 
-// Epilogue of the pipelined SDDMM kernels: a wave's FM x 4 accumulator fragments cover rows
-// r0w .. r0w + 32 FM - 1 and output columns c0w .. c0w + 127 (fragment j, lane c: column
-// c0w + 4c + j), so lane l32 holds every column of 2:4 group c0w/4 + l32.  SD_DENSE stores all
-// four (16 bytes per row), the other modes the two the nibble keeps (8 bytes per row).
+// Epilogue of the pipelined SDDMM kernels: a wave's FM x 8 accumulator fragments of 16 x 16 cover
+// rows r0w .. r0w + 16 FM - 1 and 128 output columns from c0w; lane l holds rows 16 i + 4 (l / 16) + e
+// (e < 4) and, in fragment j, column c0w + 64 (j / 4) + 4 (l % 16) + j % 4, so lanes hold every column
+// of 2:4 groups c0w/4 + 16 q + l % 16 (q < 2).  SD_DENSE stores all four (16 bytes per row), the other
+// modes the two the nibble keeps (8 bytes per row).
 template <int FM, int MODE>
-__device__ __forceinline__ void sd_epilogue(const f32x16 (&acc)[FM][4], int64_t r0w, int64_t c0w, int l32, int aa,
-                                            int64_t R, int64_t Kc, const uint8_t* __restrict__ meta,
-                                            float* __restrict__ out, const uint16_t* __restrict__ hval, int relu,
-                                            int64_t ldo) {
+__device__ __forceinline__ void sd_epilogue16x(const f32x4 (&acc)[FM][8], int64_t r0w, int64_t c0w, int l16, int aq,
+                                               int64_t R, int64_t Kc, const uint8_t* __restrict__ meta,
+                                               float* __restrict__ out, const uint16_t* __restrict__ hval, int relu,
+                                               int64_t ldo) {
   const int64_t G = Kc / 4, mrow = (Kc + 7) / 8;
-  const int64_t gq = c0w / 4 + l32;
-  if constexpr (MODE == SD_DENSE) {
-    // every column: 16 contiguous bytes per lane and row (the 32 lanes of a row write 512 bytes)
-    const int64_t c0 = 4 * gq;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = r0w + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
-        if (row < R && c0 < Kc) {
-          float* dst = out + row * ldo + c0;
-          if (c0 + 4 <= Kc) {
-            __builtin_nontemporal_store(f32x4{acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]},
-                                        reinterpret_cast<f32x4*>(dst));
-          } else {
-            const float v[4] = {acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]};
-            for (int q = 0; q < 4 && c0 + q < Kc; ++q) dst[q] = v[q];
-          }
-        }
-      }
-    return;
-  }
   const int64_t mrow_v = MODE == SD_VNM ? (G + 1) / 2 : mrow;   // V:N:M nibbles: one per gathered group
-  if (gq < G) {
-    uint32_t mb[FM][16];   // the metadata byte of every output row of the lane, loaded up front
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+  for (int q = 0; q < 2; ++q) {
+    const int64_t gq = c0w / 4 + 16 * q + l16;
+    if constexpr (MODE == SD_DENSE) {
+      const int64_t c0 = 4 * gq;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        int64_t row = r0w + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
-        row = row < R ? row : R - 1;
-        mb[i][e] = meta[row * mrow_v + gq / 2];
-      }
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = r0w + 32 * i + 8 * (e >> 2) + 4 * aa + (e & 3);
-        if (row < R) {
-          const uint32_t nib = (mb[i][e] >> (4 * (gq & 1))) & 0xF;
-          const float v0 = acc[i][0][e], v1 = acc[i][1][e], v2 = acc[i][2][e], v3 = acc[i][3][e];
-          const uint32_t p0 = nib & 3, p1 = (nib >> 2) & 3;
-          typedef float f32x2 __attribute__((ext_vector_type(2)));
-          f32x2 o;
-          o[0] = p0 == 0 ? v0 : p0 == 1 ? v1 : p0 == 2 ? v2 : v3;
-          o[1] = p1 == 0 ? v0 : p1 == 1 ? v1 : p1 == 2 ? v2 : v3;
-          if constexpr (MODE == SD_VNM) {
-            if (relu) {
-              // ReLU's derivative at the kept activations: 1 where the bf16 value is > 0
-              const uint32_t hp = *reinterpret_cast<const uint32_t*>(hval + row * (2 * G) + 2 * gq);
-              o[0] = Elem<uint16_t>::positive((uint16_t)(hp & 0xFFFF)) ? o[0] : 0.f;
-              o[1] = Elem<uint16_t>::positive((uint16_t)(hp >> 16)) ? o[1] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const int64_t row = r0w + 16 * i + 4 * aq + e;
+          if (row < R && c0 < Kc) {
+            float* dst = out + row * ldo + c0;
+            const float v[4] = {acc[i][4 * q][e], acc[i][4 * q + 1][e], acc[i][4 * q + 2][e], acc[i][4 * q + 3][e]};
+            if (c0 + 4 <= Kc) {
+              __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(dst));
+            } else {
+              for (int u = 0; u < 4 && c0 + u < Kc; ++u) dst[u] = v[u];
             }
           }
-          __builtin_nontemporal_store(o, reinterpret_cast<f32x2*>(out + row * (Kc / 2) + 2 * gq));
         }
+    } else {
+      if (gq < G) {
+        uint32_t mb[FM][4];   // the metadata byte of every output row of the lane, loaded up front
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            int64_t row = r0w + 16 * i + 4 * aq + e;
+            row = row < R ? row : R - 1;
+            mb[i][e] = meta[row * mrow_v + gq / 2];
+          }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t row = r0w + 16 * i + 4 * aq + e;
+            if (row < R) {
+              const uint32_t nib = (mb[i][e] >> (4 * (gq & 1))) & 0xF;
+              const float v0 = acc[i][4 * q][e], v1 = acc[i][4 * q + 1][e], v2 = acc[i][4 * q + 2][e],
+                          v3 = acc[i][4 * q + 3][e];
+              const uint32_t p0 = nib & 3, p1 = (nib >> 2) & 3;
+              typedef float f32x2 __attribute__((ext_vector_type(2)));
+              f32x2 o;
+              o[0] = p0 == 0 ? v0 : p0 == 1 ? v1 : p0 == 2 ? v2 : v3;
+              o[1] = p1 == 0 ? v0 : p1 == 1 ? v1 : p1 == 2 ? v2 : v3;
+              if constexpr (MODE == SD_VNM) {
+                if (relu) {
+                  // ReLU's derivative at the kept activations: 1 where the bf16 value is > 0
+                  const uint32_t hp = *reinterpret_cast<const uint32_t*>(hval + row * (2 * G) + 2 * gq);
+                  o[0] = Elem<uint16_t>::positive((uint16_t)(hp & 0xFFFF)) ? o[0] : 0.f;
+                  o[1] = Elem<uint16_t>::positive((uint16_t)(hp >> 16)) ? o[1] : 0.f;
+                }
+              }
+              __builtin_nontemporal_store(o, reinterpret_cast<f32x2*>(out + row * (Kc / 2) + 2 * gq));
+            }
+          }
       }
     }
   }
@@ -344,7 +342,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   using Cfg = SdCfg<BM, BN, WAVES_M, WAVES_N, STAGES>;
   static_assert(!WRITE_DT || BM % 64 == 0, "transposing waves cover 64 rows each");
   static_assert(!WRITE_DT || BM / 64 <= WAVES_M * WAVES_N, "enough waves to transpose a stage");
-  constexpr int FM = Cfg::FM;
+  constexpr int FM = Cfg::WM / 16, FN = 8;   // 16 x 16 fragments of the wave's WM x 128
   extern __shared__ __align__(1024) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -379,7 +377,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   for (int t = 0; t < Cfg::B_INSTR; ++t) {
     const int r = 8 * (wave * Cfg::B_INSTR + t) + (lane >> 3);      // LDS row
     const int c = (lane & 7) ^ sd_swz(r);
-    const int n = (r & ~127) | ((r & 31) << 2) | ((r & 127) >> 5);   // inverse of sd_xrow
+    const int n = (r & ~63) | ((r & 15) << 2) | ((r >> 4) & 3);   // tile column of LDS row r
     int64_t col = n0 + n;
     col = col < Kc ? col : Kc - 1;
     if constexpr (MODE == SD_VNM) {
@@ -399,59 +397,47 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
       dma16(b_src[t] + t0, uniform(st + Cfg::A_BYTES + (wave * Cfg::B_INSTR + t) * 1024));
   };
 
-  f32x16 acc[FM][4];
+  f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
 
-  const int l32 = lane & 31, aa = lane >> 5;
-  int a_row[FM], b_row[4];
+  const int l16 = lane & 15, aq = lane >> 4;
+  // fragments' rows start at multiples of 16: one per-lane base and swizzle per operand
+  const int a_base = (wm * Cfg::WM + l16) * (TK * 2), b_base = Cfg::A_BYTES + (wn * 128 + l16) * (TK * 2);
+  const int swz = sd_swz(l16);
+  // A stage is two 32-t sub-steps of 8 x FM v_mfma_f32_16x16x32_bf16 (lane l: row (column) l % 16 of
+  // a fragment, t = 32 kk + 8 (l / 16) .. +7).  One register set of operands (two waves per SIMD hide
+  // each other's LDS latency; a second set would not fit beside the transposes' registers).  The
+  // accumulators are tied through the instruction in assembly (as builtins, the compiler moves the
+  // small accumulators between registers every stage).
+  auto read_ops = [&](const unsigned char* st, int kk, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+    const int co = (((4 * kk + aq) ^ swz) << 4);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) a_row[i] = wm * Cfg::WM + 32 * i + l32;
+    for (int jj = 0; jj < FN; ++jj)
+      b[jj] = *reinterpret_cast<const bf16x8*>(st + b_base + co + jj * 16 * (TK * 2));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b_row[j] = wn * 128 + 32 * j + l32;   // = sd_xrow(wn*128 + 4*l32 + j)
-
-  // A stage is four 16-k sub-steps of 4 x FM matrix instructions.  The operands of sub-step kk+1
-  // (FM A and 4 B fragments) are read into the second of two register sets while sub-step kk's
-  // instructions run, so the LDS latency is exposed once per stage (after the barrier) instead of
-  // before every group of instructions.
-  auto read_ops = [&](const unsigned char* st, int kk, bf16x8 (&a)[FM], bf16x8 (&b)[4]) {
-    const int c = 2 * kk + aa;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(st + Cfg::A_BYTES + b_row[j] * (TK * 2) + ((c ^ sd_swz(b_row[j])) << 4));
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(st + a_row[i] * (TK * 2) + ((c ^ sd_swz(a_row[i])) << 4));
+    for (int ii = 0; ii < FM; ++ii)
+      a[ii] = *reinterpret_cast<const bf16x8*>(st + a_base + co + ii * 16 * (TK * 2));
   };
-  auto mma = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[4]) {
+  auto mma = [&](const bf16x8 (&a)[FM], const bf16x8 (&b)[FN]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int jj = 0; jj < FN; ++jj)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int ii = 0; ii < FM; ++ii)
+        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[ii][jj]) : "v"(a[ii]), "v"(b[jj]));
   };
   auto compute = [&](int kt) {
     const unsigned char* st = smem + (kt % STAGES) * Cfg::STAGE;
-    bf16x8 a0[FM], b0[4], a1[FM], b1[4];
-    // the scheduling barriers keep each group of reads ahead of the instructions before it
-    // (the scheduler would otherwise sink every read next to its first use)
+    bf16x8 a0[FM], b0[FN];
     read_ops(st, 0, a0, b0);
-    read_ops(st, 1, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
     mma(a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    read_ops(st, 2, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_ops(st, 3, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
+    read_ops(st, 1, a0, b0);
     mma(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1);
   };
 
   // Dt: stage kt of this row panel is written by the workgroup whose column tile is kt % ntn
@@ -511,7 +497,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
   }
   if (WRITE_DT) wait_vmcnt<0>();
 
-  sd_epilogue<FM, MODE>(acc, m0 + wm * Cfg::WM, n0 + wn * 128, l32, aa, R, Kc, meta, out, hval, relu, ldo);
+  // the last instructions' results before any other instruction reads them (the compiler does not
+  // see the instructions inside the assembly statements)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  sd_epilogue16x<FM, MODE>(acc, m0 + wm * Cfg::WM, n0 + wn * 128, l16, aq, R, Kc, meta, out, hval, relu, ldo);
 }
 
 // ---------------------------------------------------------------------------
@@ -533,68 +522,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void sddmm_dma_kernel(
 // 32 x 32 x 16 one (1784 against 1617 TFLOP/s in loops of nothing else on changing operands).
 // ---------------------------------------------------------------------------
 constexpr int W4_A = 256 * TK * 2, W4_STAGE = 2 * W4_A;   // D and X parts of a stage: 32 KB each
-
-// Epilogue of the four-wave kernel: 16 x 16 fragments (i, j) of a wave's 128 rows from r0w and 128
-// output columns from c0w; lane l holds rows 16 i + 4 (l / 16) + e (e < 4) and, in fragment j, column
-// c0w + 64 (j / 4) + 4 (l % 16) + j % 4, so lanes hold every column of 2:4 groups c0w/4 + 16 q +
-// l % 16 (q < 2).  SD_DENSE stores all four (16 bytes per row), SD_NM the two the nibble keeps.
-template <int MODE>
-__device__ __forceinline__ void sd_epilogue16(const f32x4 (&acc)[8][8], int64_t r0w, int64_t c0w, int l16, int aq,
-                                              int64_t R, int64_t Kc, const uint8_t* __restrict__ meta,
-                                              float* __restrict__ out, int64_t ldo) {
-  const int64_t G = Kc / 4, mrow = (Kc + 7) / 8;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int64_t gq = c0w / 4 + 16 * q + l16;
-    if constexpr (MODE == SD_DENSE) {
-      const int64_t c0 = 4 * gq;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t row = r0w + 16 * i + 4 * aq + e;
-          if (row < R && c0 < Kc) {
-            float* dst = out + row * ldo + c0;
-            const float v[4] = {acc[i][4 * q][e], acc[i][4 * q + 1][e], acc[i][4 * q + 2][e], acc[i][4 * q + 3][e]};
-            if (c0 + 4 <= Kc) {
-              __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(dst));
-            } else {
-              for (int u = 0; u < 4 && c0 + u < Kc; ++u) dst[u] = v[u];
-            }
-          }
-        }
-    } else {
-      if (gq < G) {
-        uint32_t mb[8][4];   // the metadata byte of every output row of the lane, loaded up front
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            int64_t row = r0w + 16 * i + 4 * aq + e;
-            row = row < R ? row : R - 1;
-            mb[i][e] = meta[row * mrow + gq / 2];
-          }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t row = r0w + 16 * i + 4 * aq + e;
-            if (row < R) {
-              const uint32_t nib = (mb[i][e] >> (4 * (gq & 1))) & 0xF;
-              const float v0 = acc[i][4 * q][e], v1 = acc[i][4 * q + 1][e], v2 = acc[i][4 * q + 2][e],
-                          v3 = acc[i][4 * q + 3][e];
-              const uint32_t p0 = nib & 3, p1 = (nib >> 2) & 3;
-              typedef float f32x2 __attribute__((ext_vector_type(2)));
-              f32x2 o;
-              o[0] = p0 == 0 ? v0 : p0 == 1 ? v1 : p0 == 2 ? v2 : v3;
-              o[1] = p1 == 0 ? v0 : p1 == 1 ? v1 : p1 == 2 ? v2 : v3;
-              __builtin_nontemporal_store(o, reinterpret_cast<f32x2*>(out + row * (Kc / 2) + 2 * gq));
-            }
-          }
-      }
-    }
-  }
-}
 
 template <bool WRITE_DT, int MODE>
 __global__ __launch_bounds__(256) void sddmm_w4_kernel(const uint16_t* __restrict__ D, int64_t ldd,
@@ -757,7 +684,7 @@ __global__ __launch_bounds__(256) void sddmm_w4_kernel(const uint16_t* __restric
   // the last matrix instructions' results before any other instruction reads them (the compiler does
   // not see the instructions inside the assembly statements)
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  sd_epilogue16<MODE>(acc, m0 + wm * 128, n0 + wn * 128, l16, aq, R, Kc, meta, out, ldo);
+  sd_epilogue16x<8, MODE>(acc, m0 + wm * 128, n0 + wn * 128, l16, aq, R, Kc, meta, out, nullptr, 0, ldo);
 }
 
 template <bool WRITE_DT, int MODE>
