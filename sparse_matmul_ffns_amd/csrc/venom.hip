@@ -285,10 +285,167 @@ __global__ __launch_bounds__(256) void venom_prune_kernel(const T* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------------------
+// The tiled path for bf16 with V in {64, 128, 256} and K a multiple of CW = 16384 / V: one
+// workgroup per 32 KB tile (V rows x CW columns) and nothing carried from tile to tile, so four
+// workgroups share a CU and each ends as soon as its stores are issued.  The streaming kernel above
+// keeps at most two workgroups per CU (its registers hold the next 64 KB tile) and, walking
+// several tiles, waits for each tile's stores before the next one's loads are used; with small
+// independent tiles the CU's resident workgroups sit in different phases (loads, column sums,
+// selection) and HBM stays busy.  Same rule, same order of the fp64 additions, same outputs.
+// Tiles are dealt so that the consecutive column tiles of a V-row block share an XCD, whose L2
+// then merges the partial lines of the values and metadata rows they write.
+// ---------------------------------------------------------------------------
+template <int V, int M, bool RELU>
+__global__ __launch_bounds__(256) void venom_prune_tile_kernel(const uint16_t* __restrict__ Z, int64_t ldz,
+                                                               int64_t K, uint16_t* __restrict__ values,
+                                                               uint8_t* __restrict__ meta,
+                                                               uint8_t* __restrict__ colsel, int ntx) {
+  constexpr int CW = 16384 / V;          // columns of a tile
+  constexpr int NG = CW / M, NQ = NG / 4;  // groups, quads of groups per tile row
+  constexpr int PITCH = CW + 8;          // LDS row pitch in elements (16 bytes of padding)
+  constexpr int CPR = CW / 8;            // 16-byte chunks per tile row
+  constexpr int NU = V * CPR / 256;      // chunks per thread
+  static_assert(NQ >= 1 && (V * CPR) % 256 == 0 && 256 % NQ == 0 && CW <= 256, "tile shape");
+  __shared__ __align__(16) uint16_t tile[V * PITCH];
+  __shared__ double l1[CW];
+  __shared__ uint32_t csel[NG];
+
+  const int tid = threadIdx.x;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t blk = t / ntx, c0 = (int64_t)(t - blk * ntx) * CW;
+  const int64_t G = K / M;
+
+  // 1. the tile, ReLU applied, into LDS (16-byte loads, a row's chunks on consecutive lanes)
+  u32x4 x[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int i = tid + 256 * u, r = i / CPR, c = (i % CPR) * 8;
+    x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Z + (blk * V + r) * ldz + c0 + c));
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int i = tid + 256 * u, r = i / CPR, c = (i % CPR) * 8;
+    u32x4 v = x[u];
+    if constexpr (RELU) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = v[w] & 0xFFFFu, hi = v[w] >> 16;
+        v[w] = (Elem<uint16_t>::positive((uint16_t)lo) ? lo : 0u) | ((Elem<uint16_t>::positive((uint16_t)hi) ? hi : 0u) << 16);
+      }
+    }
+    *reinterpret_cast<u32x4*>(tile + r * PITCH + c) = v;
+  }
+  __syncthreads();
+
+  // 2. column L1 norms in fp64, rows in ascending order (one lane per column)
+  if (tid < CW) {
+    double a = 0.0;
+#pragma unroll 8
+    for (int r = 0; r < V; ++r) a += (double)__uint_as_float((uint32_t)(tile[r * PITCH + tid] & 0x7FFFu) << 16);
+    l1[tid] = a;
+  }
+  __syncthreads();
+
+  // 3. per group the 4 columns of largest L1 (lower column on ties): one lane per (group, column),
+  //    the group's kept positions packed in ascending order from the wave's ballot
+  if (tid < CW) {
+    const int g = tid / M, p = tid % M;
+    const double kp = l1[tid];
+    int rk = 0;
+#pragma unroll
+    for (int q = 0; q < M; ++q) {
+      const double kq = l1[g * M + q];
+      rk += (kq > kp || (q < p && kq == kp)) ? 1 : 0;
+    }
+    const uint64_t kept = __ballot(rk < 4);
+    if (p == 0) {
+      uint32_t rest = (uint32_t)(kept >> ((tid & 63) & ~(M - 1))) & ((1u << M) - 1u), packed = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        packed |= (uint32_t)__builtin_ctz(rest) << (8 * j);
+        rest &= rest - 1u;
+      }
+      csel[g] = packed;
+      *reinterpret_cast<uint32_t*>(colsel + (blk * G + c0 / M + g) * 4) = packed;
+    }
+  }
+  __syncthreads();
+
+  // 4. per (row, quad of groups): 2 of each group's 4 chosen columns by magnitude (lower on ties);
+  //    16 bytes of values and 2 bytes of nibbles
+  const int q = tid % NQ;
+  int ofs[4][4];
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    const uint32_t cs = csel[4 * q + gi];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ofs[gi][j] = (4 * q + gi) * M + (int)((cs >> (8 * j)) & 0xFF);
+  }
+  const int64_t gq = c0 / M + 4 * q;   // the quad's first group, even
+  const int64_t meta_row = (G + 1) / 2;
+#pragma unroll
+  for (int r = tid / NQ; r < V; r += 256 / NQ) {
+    const uint16_t* trow = tile + r * PITCH;
+    uint32_t out[4], nibs = 0;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      uint32_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = trow[ofs[gi][j]];
+      const uint32_t nib = select24_bf16(v[0], v[1], v[2], v[3]);
+      const uint32_t d01 = v[0] | (v[1] << 16), d23 = v[2] | (v[3] << 16);
+      const uint32_t j0 = nib & 3, j1 = nib >> 2;
+      out[gi] = __builtin_amdgcn_perm(d23, d01, (j0 * 0x202u + 0x100u) | ((j1 * 0x202u + 0x100u) << 16));
+      nibs |= nib << (4 * gi);
+    }
+    const int64_t row = blk * V + r;
+    *reinterpret_cast<u32x4*>(values + row * (G * 2) + gq * 2) = u32x4{out[0], out[1], out[2], out[3]};
+    *reinterpret_cast<uint16_t*>(meta + row * meta_row + gq / 2) = (uint16_t)nibs;
+  }
+}
+
+// Conditions of the tiled path (the caller has checked R % V == 0 and K % M == 0).
+static bool venom_tile_ok(const void* Z, int64_t ldz, int64_t K, int V, const void* values, const uint8_t* meta,
+                          const uint8_t* colsel, const uint8_t* mask) {
+  if (mask || (V != 64 && V != 128 && V != 256) || env_is_one("NMSPARSE_VENOM_STREAM")) return false;
+  const int CW = 16384 / V;
+  return K % CW == 0 && (uintptr_t)Z % 16 == 0 && ldz % 8 == 0 && (uintptr_t)values % 16 == 0 &&
+         (uintptr_t)meta % 2 == 0 && (uintptr_t)colsel % 4 == 0;
+}
+
+template <int V, int M>
+static hipError_t venom_tile_launch(const void* Z, int64_t ldz, int64_t R, int64_t K, int relu, void* values,
+                                    uint8_t* meta, uint8_t* colsel, hipStream_t s) {
+  const int64_t ntx = K / (16384 / V), ntiles = (R / V) * ntx;
+  if (ntiles > INT32_MAX || ntx > INT32_MAX) return hipErrorInvalidValue;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(256), 0, s, (const uint16_t*)Z, ldz, K, (uint16_t*)values,
+                       meta, colsel, (int)ntx);
+    return hipGetLastError();
+  };
+  return relu ? go(venom_prune_tile_kernel<V, M, true>) : go(venom_prune_tile_kernel<V, M, false>);
+}
+
+template <int V>
+static hipError_t venom_tile_dispatch(int M, const void* Z, int64_t ldz, int64_t R, int64_t K, int relu, void* values,
+                                      uint8_t* meta, uint8_t* colsel, hipStream_t s) {
+  switch (M) {
+    case 4: return venom_tile_launch<V, 4>(Z, ldz, R, K, relu, values, meta, colsel, s);
+    case 8: return venom_tile_launch<V, 8>(Z, ldz, R, K, relu, values, meta, colsel, s);
+    default: return venom_tile_launch<V, 16>(Z, ldz, R, K, relu, values, meta, colsel, s);
+  }
+}
+
 template <typename T>
 static hipError_t venom_dispatch(const void* Z, int64_t ldz, int64_t R, int64_t K, int V, int M, int relu,
                                  void* values, uint8_t* meta, uint8_t* colsel, uint8_t* mask, int64_t ldmask,
                                  hipStream_t s) {
+  if (sizeof(T) == 2 && venom_tile_ok(Z, ldz, K, V, values, meta, colsel, mask)) {
+    return V == 64    ? venom_tile_dispatch<64>(M, Z, ldz, R, K, relu, values, meta, colsel, s)
+           : V == 128 ? venom_tile_dispatch<128>(M, Z, ldz, R, K, relu, values, meta, colsel, s)
+                      : venom_tile_dispatch<256>(M, Z, ldz, R, K, relu, values, meta, colsel, s);
+  }
   const int esz = sizeof(T);
   int CW = (int)(65536 / ((int64_t)V * esz));
   CW = (CW / 64) * 64;
