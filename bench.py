@@ -10,11 +10,11 @@ A step is one pass of the hot path over the workload's synthetic inputs
       bf16 2:4 weight [8192 x 2048] ~ N(0, 0.02)
       with activations [2048 x 4096] ~ N(0, 1);
   ffn_down_vnm64_2_8_2048x8192x4096: prune_act_venom (V=64, M=8) -> spmm_venom;
-  train_step_nm24_dmodel4096_dff16384_tok8192: nm_reprune_t_transpose (the
-      weight's 2:4 transpose re-pruned and X transposed, in one launch) ->
-      spmm_nm_t (Y) -> sddmm_nm_dt (dW, and dY^T written from the
-      SDDMM's LDS tiles) -> spmm_nm_t (dX) (the weight's own prune and
-      compress run once before timing);
+  train_step_nm24_dmodel4096_dff16384_tok8192: nm_reprune_t_transpose_panels
+      (the weight's 2:4 transpose re-pruned, in the panel layout, and X
+      transposed, in one launch) -> spmm_nm_t (Y) -> sddmm_nm_dt (dW, and
+      dY^T written from the SDDMM's LDS tiles) -> spmm_nm_t_panels (dX) (the
+      weight's own prune and compress run once before timing);
   relu_act_vnm128_2_8_8192x16384x4096: prune_act_venom (ReLU, V=128, M=8) ->
       spmm_venom;
   nm24_fp32_256x512x128: the small fp32 case.
@@ -304,18 +304,20 @@ def _w_train(w):
     Xt = torch.empty((T, dm), dtype=X.dtype, device="cuda")
     dYt = torch.empty((T, dff), dtype=dY.dtype, device="cuda")
     # dW comes before dX: the SDDMM stages every tile of dY through LDS and writes dY^T from there
-    # (sddmm_nm_dt), which the dX product then reads K-contiguous
+    # (sddmm_nm_dt), which the dX product then reads K-contiguous.  The re-pruned transpose is
+    # written in the panel layout, which the dX product (K = d_ff: 256 steps per tile) reads with
+    # four waves two steps ahead
     steps = [
-        ("nm_reprune_t_transpose", lambda: nm.nm_reprune_t_transpose(vals, meta, dff, dm, X, values_t=vt, meta_t=mt,
-                                                                     Xt=Xt)),
+        ("nm_reprune_t_transpose_panels",
+         lambda: nm.nm_reprune_t_transpose_panels(vals, meta, dff, dm, X, values_t=vt, meta_t=mt, Xt=Xt)),
         ("spmm_nm_t_fwd", lambda: nm.spmm_nm_t(vals, meta, dm, Xt, out=Y)),
         ("sddmm_nm_dt", lambda: nm.sddmm_nm(dY, X, meta, out=dW, Dt=dYt)),
-        ("spmm_nm_t_dx", lambda: nm.spmm_nm_t(vt, mt, dff, dYt, out=dX)),
+        ("spmm_nm_t_panels_dx", lambda: nm.spmm_nm_t_panels(vt, mt, dm, dff, dYt, out=dX)),
     ]
     g = 2.0 * dff * dm * T
-    flops = {"spmm_nm_t_fwd": g, "spmm_nm_t_dx": g, "sddmm_nm_dt": g}
-    algo = {"spmm_nm_t_fwd": ("mfma", g / 2), "spmm_nm_t_dx": ("mfma", g / 2), "sddmm_nm_dt": ("mfma", g),
-            "nm_reprune_t_transpose": ("hbm", 2 * (dff * dm // 2 * 2 + dff * dm // 8) + 2 * dm * T * 2)}
+    flops = {"spmm_nm_t_fwd": g, "spmm_nm_t_panels_dx": g, "sddmm_nm_dt": g}
+    algo = {"spmm_nm_t_fwd": ("mfma", g / 2), "spmm_nm_t_panels_dx": ("mfma", g / 2), "sddmm_nm_dt": ("mfma", g),
+            "nm_reprune_t_transpose_panels": ("hbm", 2 * (dff * dm // 2 * 2 + dff * dm // 8) + 2 * dm * T * 2)}
     return steps, flops, algo, "sddmm_nm_dt"
 
 
@@ -477,6 +479,8 @@ KERNEL_SOURCES = {
     "prune_act_venom": ["venom.hip"],
     "nm_reprune_t": ["reprune.hip"],
     "nm_reprune_t_transpose": ["reprune.hip"],
+    "nm_reprune_t_transpose_panels": ["reprune.hip"],
+    "spmm_nm_t_panels_dx": ["spmm_w4.hip"],
 }
 SHARED_SOURCES = ["api.cpp", "common.hpp", "dma.hpp", "launch.hpp", "prep_bodies.hpp"]
 

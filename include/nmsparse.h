@@ -436,6 +436,56 @@ nm_status nm_reprune_t_transpose(nm_dtype dt, const void* values, const uint8_t*
                                  nm_stream stream);
 
 /*
+ * The panel layout of a bf16 2:4 form (R rows, K dense columns, R % 4 == 0,
+ * K % 256 == 0): the same values and nibbles as the row-major form
+ * (values [R][K/2], meta [R][K/8]), in another order, with the same total sizes:
+ *   values: the 64 bytes of row r for the 64-column step s (its 32 kept values,
+ *           in column order) at byte ((r / 2) * (K / 64) + s) * 128 + (r % 2) * 64;
+ *   meta:   the 32 bytes of row r for the 256-column chunk c (its 64 nibbles,
+ *           group 0 in bits 0..3) at byte ((r / 4) * (K / 256) + c) * 128 + (r % 4) * 32.
+ * Every 64-column step of a 256-row tile is then whole 128-byte lines of each
+ * operand, which the four-wave SpMM below needs to load two steps ahead.
+ */
+
+/*
+ * nm_to_panels -- the panel layout of a bf16 2:4 form given row-major.
+ *   values [R][K/2], meta [R][K/8] in; values_p, meta_p (same sizes) out.
+ * R % 4 == 0 and K % 256 == 0 (NM_ERR_SHAPE), all four pointers 16-byte aligned
+ * (NM_ERR_ALIGN), bf16 only (NM_ERR_UNSUPPORTED).  No output may overlap an input.
+ */
+nm_status nm_to_panels(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                       void* values_p, uint8_t* meta_p, nm_stream stream);
+
+/*
+ * nm_reprune_t_transpose_panels -- nm_reprune_t_transpose with the re-pruned
+ * transposed weight written in the panel layout (a K x R form compressed along
+ * R): the double-pruned backward's operand (NSF PAR award 2340011, SLOPE
+ * abstract) for spmm_nm_t_panels.  Xt as for nm_reprune_t_transpose.
+ * bf16 only; R % 256 == 0 and K % 128 == 0 (NM_ERR_SHAPE); values and values_t
+ * 16-byte, meta and meta_t 2-byte aligned (NM_ERR_ALIGN).  Outputs equal
+ * nm_to_panels of nm_reprune_t's, byte for byte.
+ */
+nm_status nm_reprune_t_transpose_panels(nm_dtype dt, const void* values, const uint8_t* meta,
+                                        int64_t R, int64_t K, void* values_t, uint8_t* meta_t,
+                                        const void* X, int64_t ldx, int64_t RX, int64_t CX,
+                                        void* Xt, int64_t ldxt, nm_stream stream);
+
+/*
+ * spmm_nm_t_panels -- spmm_nm_t of a weight given in the panel layout
+ * ("Success story: ESPLAG", Research Topic: the SpMM of a 2:4 layer; the
+ * backward's product with the re-pruned transposed weight, SLOPE abstract):
+ * C[r][n] = sum_k decompress(values, meta)[r][k] * Bt[n][k].
+ *   values, meta: panel layout of the R x K form; Bt [Nc][ldbt]; C [R][ldc] fp32.
+ * bf16 only; R % 256 == 0, K % 256 == 0, ldbt >= K, ldbt % 8 == 0, ldc >= Nc
+ * (NM_ERR_SHAPE); values, meta and Bt 16-byte, C 4-byte aligned (NM_ERR_ALIGN);
+ * NM_ERR_TOO_LARGE when values or Bt reach 4 GiB.  The products are added in the
+ * order of spmm_nm_t's pipelined kernel, so C equals spmm_nm_t's bit for bit.
+ */
+nm_status spmm_nm_t_panels(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R,
+                           int64_t K, const void* Bt, int64_t ldbt, int64_t Nc, float* C,
+                           int64_t ldc, nm_stream stream);
+
+/*
  * sddmm_nm -- the weight gradient of a 2:4 layer, sampled at the weight's
  * survivors ("Success story: ESPLAG", Research Topic: kernels for the full
  * sparse training step):

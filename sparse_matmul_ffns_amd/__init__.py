@@ -16,6 +16,8 @@ from .nmsparse import (  # noqa: F401
     nm_prune_compress,
     nm_prune_compress_transpose,
     nm_reprune_t_transpose,
+    nm_reprune_t_transpose_panels,
+    nm_to_panels,
     nm_reprune_t,
     prune_act_venom,
     sddmm_nm,
@@ -29,6 +31,7 @@ from .nmsparse import (  # noqa: F401
     spmm_venom_tn,
     venom_tn_work_bytes,
     spmm_nm_t,
+    spmm_nm_t_panels,
     spmm_nm_t_lowrank,
     spmm_nm_t_relu_venom,
     spmm_venom,

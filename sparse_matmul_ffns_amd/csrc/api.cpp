@@ -267,6 +267,42 @@ nm_status nm_reprune_t_transpose(nm_dtype dt, const void* values, const uint8_t*
                                                        ldxt, hs(stream)));
 }
 
+nm_status nm_to_panels(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, void* values_p,
+                       uint8_t* meta_p, nm_stream stream) {
+  if (!values || !meta || !values_p || !meta_p) return NM_ERR_NULL;
+  if (dt != NM_BF16) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || R % 4 != 0 || K % 256 != 0) return NM_ERR_SHAPE;
+  if (!aligned(values, 16) || !aligned(meta, 16) || !aligned(values_p, 16) || !aligned(meta_p, 16)) return NM_ERR_ALIGN;
+  return hip_status(nms::launch_nm_to_panels(values, meta, R, K, values_p, meta_p, hs(stream)));
+}
+
+nm_status nm_reprune_t_transpose_panels(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                                        void* values_t, uint8_t* meta_t, const void* X, int64_t ldx, int64_t RX,
+                                        int64_t CX, void* Xt, int64_t ldxt, nm_stream stream) {
+  if (!values || !meta || !values_t || !meta_t || !X || !Xt) return NM_ERR_NULL;
+  if (dt != NM_BF16) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || R % 256 != 0 || K % 128 != 0) return NM_ERR_SHAPE;
+  if (RX <= 0 || CX <= 0 || ldx < CX || ldxt < RX) return NM_ERR_SHAPE;
+  if (!aligned(values, 16) || !aligned(meta, 2) || !aligned(values_t, 16) || !aligned(meta_t, 2) ||
+      !aligned(X, esize(dt)) || !aligned(Xt, esize(dt)))
+    return NM_ERR_ALIGN;
+  return hip_status(nms::launch_nm_reprune_t_transpose_panels(values, meta, R, K, values_t, meta_t, X, ldx, RX, CX, Xt,
+                                                              ldxt, hs(stream)));
+}
+
+nm_status spmm_nm_t_panels(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
+                           int64_t ldbt, int64_t Nc, float* C, int64_t ldc, nm_stream stream) {
+  if (!values || !meta || !Bt || !C) return NM_ERR_NULL;
+  if (dt != NM_BF16) return NM_ERR_UNSUPPORTED;
+  if (R <= 0 || K <= 0 || Nc <= 0 || R % 256 != 0 || K % 256 != 0 || ldbt < K || ldbt % 8 != 0 || ldc < Nc)
+    return NM_ERR_SHAPE;
+  if (!aligned(values, 16) || !aligned(meta, 16) || !aligned(Bt, 16) || !aligned(C, 4)) return NM_ERR_ALIGN;
+  if (R * K >= (int64_t(1) << 32) || Nc * ldbt * 2 >= (int64_t(1) << 32)) return NM_ERR_TOO_LARGE;
+  const hipError_t e = nms::launch_spmm_nm_t_panels(values, meta, R, K, Bt, ldbt, Nc, C, ldc, hs(stream));
+  if (e == hipErrorNotSupported) return NM_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
 nm_status sddmm_nm(nm_dtype dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
                    int64_t T, const uint8_t* meta, float* values_out, nm_stream stream) {
   if (!D || !X || !meta || !values_out) return NM_ERR_NULL;

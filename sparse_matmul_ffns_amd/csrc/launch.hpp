@@ -83,6 +83,15 @@ hipError_t launch_spmm_nm_general(int dt, const void* values, const uint8_t* met
                                   int64_t work_bytes, hipStream_t s);
 hipError_t launch_nm_transpose(int dt, const void* src, int64_t lds, int64_t R, int64_t Cn, void* dst, int64_t ldd,
                                hipStream_t s);
+bool spmm_panels_ok(const void* values, const uint8_t* meta, const void* Bt, int64_t ldbt, int64_t R, int64_t K,
+                    int64_t Nc);
+hipError_t launch_spmm_nm_t_panels(const void* values, const uint8_t* meta, int64_t R, int64_t K, const void* Bt,
+                                   int64_t ldbt, int64_t Nc, float* C, int64_t ldc, hipStream_t s);
+hipError_t launch_nm_reprune_t_transpose_panels(const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                                                void* values_t, uint8_t* meta_t, const void* X, int64_t ldx,
+                                                int64_t RX, int64_t CX, void* Xt, int64_t ldxt, hipStream_t s);
+hipError_t launch_nm_to_panels(const void* values, const uint8_t* meta, int64_t R, int64_t K, void* values_p,
+                               uint8_t* meta_p, hipStream_t s);
 hipError_t launch_sddmm_nm_dt(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
                               int64_t Tn, const uint8_t* meta, float* out, void* Dt, int64_t lddt, hipStream_t s);
 bool sddmm_venom_fast_ok(const void* dY, int64_t lddy, const void* Wd, int64_t ldw, int64_t Tn, int64_t F, int64_t Nc,

@@ -137,7 +137,10 @@ __global__ __launch_bounds__(256) void reprune_t_kernel(const T* __restrict__ va
 constexpr int RB_TILE = 128;
 
 // Tiles t = first, first + stride, ... of the re-prune (the kernel below runs one per workgroup;
-// the fused launch with a transpose passes its own numbering).
+// the fused launch with a transpose passes its own numbering).  PANELS: the output in the panel
+// layout of spmm_nm_t_panels (R a multiple of 256; the same values and nibbles, each 16-byte
+// values piece and 2-byte metadata piece at its panel address).
+template <bool PANELS = false>
 __device__ __forceinline__ void reprune_t_bf16_body(uint32_t first, uint32_t stride, uint32_t* __restrict__ tile,
                                                     const uint16_t* __restrict__ values,
                                                     const uint8_t* __restrict__ meta, int64_t R, int64_t K,
@@ -224,10 +227,19 @@ __device__ __forceinline__ void reprune_t_bf16_body(uint32_t first, uint32_t str
           out[h] = __builtin_amdgcn_perm(d23, d01, (q0 * 0x202u + 0x100u) | ((q1 * 0x202u + 0x100u) << 16));
           nibs |= nib << (4 * h);
         }
-        const int64_t orow = k0 + 2 * j + half;
-        *reinterpret_cast<u32x4*>(values_t + orow * (R / 2) + (r0 + 16 * ch) / 2) =
-            u32x4{out[0], out[1], out[2], out[3]};
-        *reinterpret_cast<uint16_t*>(meta_t + orow * (R / 8) + (r0 + 16 * ch) / 8) = (uint16_t)nibs;
+        const int64_t orow = k0 + 2 * j + half, oc = r0 + 16 * ch;   // output row, its dense column
+        uint16_t* vd;
+        uint8_t* md;
+        if constexpr (PANELS) {
+          vd = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(values_t) +
+                                           ((orow >> 1) * (R / 64) + oc / 64) * 128 + (orow & 1) * 64 + oc % 64);
+          md = meta_t + ((orow >> 2) * (R / 256) + oc / 256) * 128 + (orow & 3) * 32 + (oc % 256) / 8;
+        } else {
+          vd = values_t + orow * (R / 2) + oc / 2;
+          md = meta_t + orow * (R / 8) + oc / 8;
+        }
+        *reinterpret_cast<u32x4*>(vd) = u32x4{out[0], out[1], out[2], out[3]};
+        *reinterpret_cast<uint16_t*>(md) = (uint16_t)nibs;
       }
     }
     __syncthreads();   // every lane is done with the tile before the next one is written
@@ -249,6 +261,7 @@ __global__ __launch_bounds__(256) void reprune_t_bf16_kernel(const uint16_t* __r
 // X^T is the freshest data in the last-level cache when the forward product reads it; with the
 // transpose first, the step's later products measured ~5 us slower at d_model 4096, d_ff 16384,
 // 8192 tokens.
+template <bool PANELS>
 __global__ __launch_bounds__(256) void reprune_transpose_kernel(const uint16_t* __restrict__ values,
                                                                 const uint8_t* __restrict__ meta, int64_t R,
                                                                 int64_t K, uint16_t* __restrict__ values_t,
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(256) void reprune_transpose_kernel(const uint16_t* 
   __shared__ uint32_t tile[RB_TILE * 64];
   const int b = blockIdx.x;
   if (b < (int)n_reprune)
-    reprune_t_bf16_body((uint32_t)b, n_reprune, tile, values, meta, R, K, values_t, meta_t);
+    reprune_t_bf16_body<PANELS>((uint32_t)b, n_reprune, tile, values, meta, R, K, values_t, meta_t);
   else
     transpose_bf16_body(b - (int)n_reprune, X, ldx, RX, CX, Xt, ldxt);
 }
@@ -307,9 +320,60 @@ hipError_t launch_nm_reprune_t_transpose(int dt, const void* values, const uint8
     if (e != hipSuccess) return e;
     return launch_nm_transpose(dt, X, ldx, RX, CX, Xt, ldxt, s);
   }
-  hipLaunchKernelGGL(reprune_transpose_kernel, dim3((unsigned)(n_reprune + n_transpose)), dim3(256), 0, s,
+  hipLaunchKernelGGL(reprune_transpose_kernel<false>, dim3((unsigned)(n_reprune + n_transpose)), dim3(256), 0, s,
                      (const uint16_t*)values, meta, R, K, (uint16_t*)values_t, meta_t, (const uint16_t*)X, ldx, RX, CX,
                      (uint16_t*)Xt, ldxt, (uint32_t)n_reprune);
+  return hipGetLastError();
+}
+
+// The same launch with the re-pruned transpose in the panel layout: bf16, R a multiple of 256 and
+// K of 128, the aligned layout of the tiled re-prune; no fallback.
+hipError_t launch_nm_reprune_t_transpose_panels(const void* values, const uint8_t* meta, int64_t R, int64_t K,
+                                                void* values_t, uint8_t* meta_t, const void* X, int64_t ldx,
+                                                int64_t RX, int64_t CX, void* Xt, int64_t ldxt, hipStream_t s) {
+  if (R % 256 != 0 || K % RB_TILE != 0 || (uintptr_t)values % 16 != 0 || (uintptr_t)meta % 2 != 0 ||
+      (uintptr_t)values_t % 16 != 0 || (uintptr_t)meta_t % 2 != 0)
+    return hipErrorNotSupported;
+  const int64_t n_reprune = (R / RB_TILE) * (K / RB_TILE);
+  const int64_t tiles = ((RX + 63) / 64) * ((CX + 63) / 64);
+  const int64_t n_transpose = (tiles + 3) / 4;
+  if (n_reprune + n_transpose > (int64_t)INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(reprune_transpose_kernel<true>, dim3((unsigned)(n_reprune + n_transpose)), dim3(256), 0, s,
+                     (const uint16_t*)values, meta, R, K, (uint16_t*)values_t, meta_t, (const uint16_t*)X, ldx, RX, CX,
+                     (uint16_t*)Xt, ldxt, (uint32_t)n_reprune);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Row-major 2:4 form -> panel layout (spmm_nm_t_panels): one thread per 16-byte piece of the
+// output, values first, then metadata; R a multiple of 4, K of 256.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void nm_to_panels_kernel(const uint8_t* __restrict__ values,
+                                                           const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+                                                           uint8_t* __restrict__ values_p, uint8_t* __restrict__ meta_p) {
+  const int64_t nv = R * K / 16, nm = R * K / 128;   // 16-byte pieces of values (R x K bytes) and metadata
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < nv) {
+    const int64_t KT = K / 64, L = i / 8, w = (i % 8) * 16;   // line (row pair, step), byte in the line
+    const int64_t r = 2 * (L / KT) + w / 64, st = L % KT;
+    *reinterpret_cast<u32x4*>(values_p + 16 * i) =
+        *reinterpret_cast<const u32x4*>(values + r * K + st * 64 + w % 64);
+  } else if (i < nv + nm) {
+    const int64_t j = i - nv, KC = K / 256, L = j / 8, w = (j % 8) * 16;   // line (4 rows, chunk)
+    const int64_t r = 4 * (L / KC) + w / 32, c = L % KC;
+    *reinterpret_cast<u32x4*>(meta_p + 16 * j) = *reinterpret_cast<const u32x4*>(meta + r * (K / 8) + c * 32 + w % 32);
+  }
+}
+
+hipError_t launch_nm_to_panels(const void* values, const uint8_t* meta, int64_t R, int64_t K, void* values_p,
+                               uint8_t* meta_p, hipStream_t s) {
+  if (R % 4 != 0 || K % 256 != 0 || (uintptr_t)values % 16 != 0 || (uintptr_t)meta % 16 != 0 ||
+      (uintptr_t)values_p % 16 != 0 || (uintptr_t)meta_p % 16 != 0)
+    return hipErrorNotSupported;
+  const int64_t n = R * K / 16 + R * K / 128;
+  if ((n + 255) / 256 > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(nm_to_panels_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const uint8_t*)values,
+                     meta, R, K, (uint8_t*)values_p, meta_p);
   return hipGetLastError();
 }
 

@@ -37,6 +37,9 @@ _SIGNATURES = {
     "nm_decompress": [_int, _vp, _vp, _i64, _i64, _int, _int, _vp, _i64, _vp],
     "spmm_nm": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
+    "nm_to_panels": [_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp],
+    "nm_reprune_t_transpose_panels": [_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
+    "spmm_nm_t_panels": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t_out_bf16": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t_lowrank": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
                           _vp],
@@ -529,6 +532,53 @@ def nm_reprune_t_transpose(values: torch.Tensor, meta: torch.Tensor, R: int, K: 
                                         _rows(X, "X"), RX, CX, _p(Xt), _rows(Xt, "Xt"), _stream()),
            "nm_reprune_t_transpose")
     return values_t, meta_t, Xt
+
+
+def nm_to_panels(values: torch.Tensor, meta: torch.Tensor, R: int, K: int, values_p=None, meta_p=None):
+    """The panel layout (for spmm_nm_t_panels) of a bf16 2:4 form given row-major; returns
+    (values_p, meta_p), flat buffers of the row-major sizes."""
+    _dev(values, meta, values_p, meta_p)
+    _flat(values, "values"), _flat(meta, "meta")
+    if values_p is None:
+        values_p = torch.empty((R * K // 2,), dtype=values.dtype, device=values.device)
+    if meta_p is None:
+        meta_p = torch.empty((R * K // 8,), dtype=torch.uint8, device=values.device)
+    _check(lib().nm_to_panels(_dt(values), _p(values), _p(meta), R, K, _p(values_p), _p(meta_p), _stream()),
+           "nm_to_panels")
+    return values_p, meta_p
+
+
+def nm_reprune_t_transpose_panels(values: torch.Tensor, meta: torch.Tensor, R: int, K: int, X: torch.Tensor,
+                                  values_t=None, meta_t=None, Xt=None):
+    """nm_reprune_t_transpose with the re-pruned transpose (K x R, compressed along R) in the panel
+    layout; returns (values_t, meta_t, Xt), values_t and meta_t flat."""
+    _dev(values, meta, values_t, meta_t, X, Xt)
+    _flat(values, "values"), _flat(meta, "meta")
+    if values_t is None:
+        values_t = torch.empty((K * R // 2,), dtype=values.dtype, device=values.device)
+    if meta_t is None:
+        meta_t = torch.empty((K * R // 8,), dtype=torch.uint8, device=values.device)
+    RX, CX = X.shape
+    if Xt is None:
+        Xt = torch.empty((CX, RX), dtype=X.dtype, device=X.device)
+    if Xt.shape != (CX, RX) or Xt.dtype != X.dtype:
+        raise ValueError("Xt must be [CX, RX] with X's dtype")
+    _check(lib().nm_reprune_t_transpose_panels(_dt(values), _p(values), _p(meta), R, K, _p(values_t), _p(meta_t),
+                                               _p(X), _rows(X, "X"), RX, CX, _p(Xt), _rows(Xt, "Xt"), _stream()),
+           "nm_reprune_t_transpose_panels")
+    return values_t, meta_t, Xt
+
+
+def spmm_nm_t_panels(values: torch.Tensor, meta: torch.Tensor, R: int, K: int, Bt: torch.Tensor, out=None):
+    """spmm_nm_t of an R x K bf16 2:4 weight in the panel layout: C [R, Nc] fp32."""
+    _dev(values, meta, Bt, out)
+    _flat(values, "values"), _flat(meta, "meta")
+    Nc = Bt.shape[0]
+    if out is None:
+        out = torch.empty((R, Nc), dtype=torch.float32, device=Bt.device)
+    _check(lib().spmm_nm_t_panels(_dt(Bt), _p(values), _p(meta), R, K, _p(Bt), _rows(Bt, "Bt"), Nc, _p(out),
+                                  _rows(out, "out"), _stream()), "spmm_nm_t_panels")
+    return out
 
 
 def sddmm_nm(D: torch.Tensor, X: torch.Tensor, meta: torch.Tensor, out=None, Dt=None):

@@ -249,7 +249,7 @@ def test_pipelined_spmm_never_touches_in_flight_registers(tmp_path, src, prefix,
 
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
-@pytest.mark.parametrize("src", ["spmm_dma.hip", "spmm_vnm.hip", "spmm_nt.hip", "sddmm.hip", "lowrank.hip"])
+@pytest.mark.parametrize("src", ["spmm_dma.hip", "spmm_vnm.hip", "spmm_nt.hip", "spmm_w4.hip", "sddmm.hip", "lowrank.hip"])
 def test_m0_written_only_by_the_direct_load_helpers(tmp_path, src):
     kernels = _kernels(_compile(tmp_path, src), "_ZN3nms")
     assert kernels
