@@ -118,6 +118,60 @@ __global__ __launch_bounds__(256) void venom_expand_t_kernel(const uint16_t* __r
   }
 }
 
+// The same with whole-vector loads: a thread takes one token and four consecutive groups, reading
+// their kept pairs (16 bytes), nibbles (2 bytes) and column choices (16 bytes) with one load each
+// instead of a load per byte.  Tiles of 64 tokens x 128 rows, so a tile's tokens lie in one
+// V-block (V % 64 == 0); the LDS row pitch of 72 elements keeps the 16-byte reads of the
+// write-out aligned, and the 8-token chunks of row r sit at chunk ^ ((r >> 4) & 7), so the rows a
+// wave writes at once (16, 32 or 64 apart) fall on different banks.
+template <int M>
+__global__ __launch_bounds__(256) void venom_expand_t_vec_kernel(const uint16_t* __restrict__ hv,
+                                                                 const uint8_t* __restrict__ hm,
+                                                                 const uint8_t* __restrict__ hc, int64_t F, int V,
+                                                                 uint16_t* __restrict__ Ht, int64_t ldh) {
+  constexpr int NG = XT_F / M, NQ = NG / 4;   // groups and quads of groups of a tile row
+  static_assert(NQ >= 1 && 256 % NQ == 0, "tile");
+  __shared__ __align__(16) uint16_t tile[XT_F][XT_T + 8];
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * XT_T, k0 = (int64_t)blockIdx.y * XT_F;
+  const int64_t G = F / M;
+  for (int i = tid; i < XT_F * (XT_T + 8) / 8; i += 256)
+    reinterpret_cast<u32x4*>(&tile[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  for (int u = tid; u < XT_T * NQ; u += 256) {
+    const int tl = u / NQ, q = u % NQ;
+    const int64_t t = t0 + tl, g0 = k0 / M + 4 * q;
+    const u32x4 pairs = *reinterpret_cast<const u32x4*>(hv + t * 2 * G + 2 * g0);
+    const uint32_t nibs = *reinterpret_cast<const uint16_t*>(hm + t * (G / 2) + g0 / 2);
+    const u32x4 cs = *reinterpret_cast<const u32x4*>(hc + ((t / V) * G + g0) * 4);
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const uint32_t nib = (nibs >> (4 * gi)) & 0xFu;
+      const int row = (4 * q + gi) * M;
+      const int c0 = (int)((cs[gi] >> (8 * (nib & 3u))) & (uint32_t)(M - 1));
+      const int c1 = (int)((cs[gi] >> (8 * (nib >> 2))) & (uint32_t)(M - 1));
+      const int r0 = row + c0, r1 = row + c1;
+      tile[r0][(((tl >> 3) ^ (r0 >> 4)) & 7) * 8 + (tl & 7)] = (uint16_t)(pairs[gi] & 0xFFFFu);
+      tile[r1][(((tl >> 3) ^ (r1 >> 4)) & 7) * 8 + (tl & 7)] = (uint16_t)(pairs[gi] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < XT_F * 8; i += 256) {
+    const int r = i >> 3, piece = i & 7;
+    *reinterpret_cast<u32x4*>(Ht + (k0 + r) * ldh + t0 + 8 * piece) =
+        *reinterpret_cast<const u32x4*>(&tile[r][8 * ((piece ^ (r >> 4)) & 7)]);
+  }
+}
+
+// Conditions of the vector kernel: whole tiles, a tile's tokens in one V-block, 16-byte rows of
+// values and column choices, 2-byte nibble pieces.
+static bool expand_vec_ok(const void* hv, const uint8_t* hm, const uint8_t* hc, int64_t Tn, int64_t F, int V, int M,
+                          const void* Ht, int64_t ldh) {
+  return !env_is_one("NMSPARSE_EXPAND_SCATTER") && Tn % XT_T == 0 && F % XT_F == 0 && V % XT_T == 0 &&
+         ldh % 8 == 0 && (uintptr_t)hv % 16 == 0 && (uintptr_t)hm % 2 == 0 && (uintptr_t)hc % 16 == 0 &&
+         (uintptr_t)Ht % 16 == 0 && (M == 4 || M == 8 || M == 16);
+}
+
 int64_t venom_tn_work_bytes(int esz, int64_t Tn, int64_t F) { return esz == 2 ? F * Tn * 2 : 0; }
 
 hipError_t launch_sddmm_venom(int dt, const void* dY, int64_t lddy, const void* Wd, int64_t ldw, int64_t Tn,
@@ -145,8 +199,17 @@ hipError_t launch_spmm_venom_tn(int dt, const void* hv, const uint8_t* hm, const
   if (dt == DT_BF16 && !force_generic() && need > 0 && work && work_bytes >= need && (uintptr_t)work % 16 == 0 &&
       dense_nt_fast_ok(work, Tn, dYt, lddyt, dW, lddw, Tn)) {
     const dim3 grid((unsigned)((Tn + XT_T - 1) / XT_T), (unsigned)((F + XT_F - 1) / XT_F));
-    hipLaunchKernelGGL(venom_expand_t_kernel, grid, dim3(256), 0, s, (const uint16_t*)hv, hm, hc, Tn, F, V, M,
-                       (uint16_t*)work, Tn);
+    if (expand_vec_ok(hv, hm, hc, Tn, F, V, M, work, Tn)) {
+      auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const uint16_t*)hv, hm, hc, F, V, (uint16_t*)work, Tn);
+      };
+      if (M == 4) go(venom_expand_t_vec_kernel<4>);
+      else if (M == 8) go(venom_expand_t_vec_kernel<8>);
+      else go(venom_expand_t_vec_kernel<16>);
+    } else {
+      hipLaunchKernelGGL(venom_expand_t_kernel, grid, dim3(256), 0, s, (const uint16_t*)hv, hm, hc, Tn, F, V, M,
+                         (uint16_t*)work, Tn);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_dense_nt(work, Tn, dYt, lddyt, F, Nc, Tn, dW, lddw, s);

@@ -139,3 +139,17 @@ def test_venom_backward_rejects():
         nm.sddmm_venom(z(100, 64), z(64, 64), z(100, 16), u8(100, 4), u8(1, 8, 4), 128, 8)
     with pytest.raises(nm.NmError):   # M = 5
         nm.spmm_venom_tn(z(128, 16), u8(128, 4), u8(1, 8, 4), 40, 128, 5, z(8, 128))
+
+
+@pytest.mark.parametrize("T,F,Nc,V,M", [(256, 512, 256, 128, 8), (192, 256, 72, 64, 4), (128, 1024, 64, 64, 16),
+                                        (512, 384, 136, 256, 8)])
+def test_spmm_venom_tn_expansions_agree(T, F, Nc, V, M, monkeypatch):
+    """The vector expansion of h_s^T and the scattering one (NMSPARSE_EXPAND_SCATTER=1) give the same
+    dW_down bit for bit, for every M; both against the oracle on small integers (exact)."""
+    hv, hm, hc, dY, _ = _case(T, F, Nc, V, M, 5 * T + F, "ints")
+    args = (dev(hv, "bf16"), dev(hm, "u8"), dev(hc, "u8"), F, V, M, dev(np.ascontiguousarray(dY.T), "bf16"))
+    a = nm.spmm_venom_tn(*args, work="auto")
+    monkeypatch.setenv("NMSPARSE_EXPAND_SCATTER", "1")
+    b = nm.spmm_venom_tn(*args, work="auto")
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert np.array_equal(host(a), O.spmm_venom_tn(hv, hm, hc, T, F, V, M, dY, "bf16"))
