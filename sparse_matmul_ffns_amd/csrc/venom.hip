@@ -286,9 +286,10 @@ __global__ __launch_bounds__(256) void venom_prune_kernel(const T* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// The tiled path for bf16 with V in {64, 128, 256} and K a multiple of CW = 16384 / V: one
-// workgroup per 32 KB tile (V rows x CW columns) and nothing carried from tile to tile, so four
-// workgroups share a CU and each ends as soon as its stores are issued.  The streaming kernel above
+// The tiled path for bf16 with V in {64, 128, 256} and K a multiple of CW = 256, 256, 64 columns:
+// one workgroup per tile (V rows x CW columns, 32 KB, or 64 KB for V = 128) and nothing carried
+// from tile to tile, so two to four workgroups share a CU and each ends as soon as its stores are
+// issued.  The streaming kernel above
 // keeps at most two workgroups per CU (its registers hold the next 64 KB tile) and, walking
 // several tiles, waits for each tile's stores before the next one's loads are used; with small
 // independent tiles the CU's resident workgroups sit in different phases (loads, column sums,
@@ -296,12 +297,16 @@ __global__ __launch_bounds__(256) void venom_prune_kernel(const T* __restrict__ 
 // Tiles are dealt so that the consecutive column tiles of a V-row block share an XCD, whose L2
 // then merges the partial lines of the values and metadata rows they write.
 // ---------------------------------------------------------------------------
+// Columns of a tile: 256 for V = 128 (a row's 64 values fill a 128-byte line; 66.6 against 69.9 us
+// with 128 columns at 8192 x 16384), 16384 / V otherwise.
+constexpr int tile_cols(int V) { return V == 128 ? 256 : 16384 / V; }
+
 template <int V, int M, bool RELU>
 __global__ __launch_bounds__(256) void venom_prune_tile_kernel(const uint16_t* __restrict__ Z, int64_t ldz,
                                                                int64_t K, uint16_t* __restrict__ values,
                                                                uint8_t* __restrict__ meta,
                                                                uint8_t* __restrict__ colsel, int ntx) {
-  constexpr int CW = 16384 / V;          // columns of a tile
+  constexpr int CW = tile_cols(V);       // columns of a tile
   constexpr int NG = CW / M, NQ = NG / 4;  // groups, quads of groups per tile row
   constexpr int PITCH = CW + 8;          // LDS row pitch in elements (16 bytes of padding)
   constexpr int CPR = CW / 8;            // 16-byte chunks per tile row
@@ -409,7 +414,7 @@ __global__ __launch_bounds__(256) void venom_prune_tile_kernel(const uint16_t* _
 static bool venom_tile_ok(const void* Z, int64_t ldz, int64_t K, int V, const void* values, const uint8_t* meta,
                           const uint8_t* colsel, const uint8_t* mask) {
   if (mask || (V != 64 && V != 128 && V != 256) || env_is_one("NMSPARSE_VENOM_STREAM")) return false;
-  const int CW = 16384 / V;
+  const int CW = tile_cols(V);
   return K % CW == 0 && (uintptr_t)Z % 16 == 0 && ldz % 8 == 0 && (uintptr_t)values % 16 == 0 &&
          (uintptr_t)meta % 2 == 0 && (uintptr_t)colsel % 4 == 0;
 }
@@ -417,7 +422,7 @@ static bool venom_tile_ok(const void* Z, int64_t ldz, int64_t K, int V, const vo
 template <int V, int M>
 static hipError_t venom_tile_launch(const void* Z, int64_t ldz, int64_t R, int64_t K, int relu, void* values,
                                     uint8_t* meta, uint8_t* colsel, hipStream_t s) {
-  const int64_t ntx = K / (16384 / V), ntiles = (R / V) * ntx;
+  const int64_t ntx = K / tile_cols(V), ntiles = (R / V) * ntx;
   if (ntiles > INT32_MAX || ntx > INT32_MAX) return hipErrorInvalidValue;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(256), 0, s, (const uint16_t*)Z, ldz, K, (uint16_t*)values,
