@@ -30,6 +30,11 @@ small fp32 case, the V:N:M down-projection, the double-pruned training step,
 the ReLU V:N:M step and that step's backward (dZ at the kept activations and
 dW_down).
 
+A default run also measures the bf16 matrix rate the chip sustains under its
+power limit (`sustained_mfma`: a chip-wide loop of independent matrix
+instructions, no memory traffic) and reports every bf16 step against it
+(`pct_of_sustained_bf16_dense`) beside the nominal peak.
+
 Warm-up: the W untimed steps are repeated until at least one second of them
 has run, so that the timed steps see settled GPU clocks.  `cold` reports, beside
 `value`, the median of five single steps each run after 512 MiB have been
@@ -87,6 +92,37 @@ def copy_calibration(steps):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_per_launch": n, "launches": steps}))
+
+
+def sustained_mfma():
+    """The bf16 matrix rate the chip sustains under its power limit, measured live: the library's
+    probe (a chip-wide loop of independent matrix instructions on register operands that change
+    every iteration, two waves per SIMD, no memory traffic), timed with HIP events on the stream it runs on, after a second of
+    warm-up.  Dense v_mfma_f32_32x32x16_bf16 and 2:4 v_smfmac_f32_32x32x32_bf16 (dense-equivalent
+    flops)."""
+    import torch
+    import sparse_matmul_ffns_amd as nm
+    sink = torch.empty(512 * 256, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    iters = 4096
+    res = {}
+    for kind, key in ((0, "dense_bf16_tflops"), (1, "smfmac_2to4_dense_equivalent_tflops")):
+        t0 = time.time()
+        while time.time() - t0 < 1.0:
+            nm.mfma_rate_probe(kind, iters, sink)
+            torch.cuda.synchronize()
+        best = 0.0
+        for _ in range(5):
+            e0.record()
+            flops = nm.mfma_rate_probe(kind, iters, sink)
+            e1.record()
+            e1.synchronize()
+            best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        res[key] = round(best, 1)
+    res["how"] = ("chip-wide loop of independent bf16 matrix instructions on register operands that change every "
+                  "iteration (random signs and significands; nm_mfma_rate_probe), 2 waves per SIMD, no memory traffic, "
+                  "best of 5 launches after 1 s of warm-up")
+    return res
 
 
 def _dev(raw):
@@ -670,6 +706,15 @@ def main():
             r = measure(name, args.steps, args.warmup, not args.no_cpu)
             r.pop("workload")
             out["configs"][name] = r
+        # the same figures against the matrix rate the chip sustains (measured last, so that its
+        # full-power loop does not warm the chip for the workloads)
+        sus = sustained_mfma()
+        out["sustained_mfma"] = sus
+        dense = sus["dense_bf16_tflops"]
+        out["config"]["pct_of_sustained_bf16_dense"] = round(100.0 * out["value"] / dense, 2)
+        for r in out["configs"].values():
+            if r.get("dtype") == "bf16":
+                r["pct_of_sustained_bf16_dense"] = round(100.0 * r["value"] / dense, 2)
     print(json.dumps(out))
 
 

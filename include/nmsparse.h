@@ -436,6 +436,22 @@ nm_status nm_reprune_t_transpose(nm_dtype dt, const void* values, const uint8_t*
                                  nm_stream stream);
 
 /*
+ * nm_mfma_rate_probe -- a measurement aid, not a step of the sparse path: a
+ * chip-wide loop of independent bf16 matrix instructions on register operands
+ * (kind 0: v_mfma_f32_32x32x16_bf16; kind 1: v_smfmac_f32_32x32x32_bf16, 2:4),
+ * eight accumulators per wave, two waves per SIMD on 256 CUs, no memory traffic.
+ * Timed by the caller (events around it on `stream`), it gives the matrix rate
+ * the chip sustains under its power limit, the reference the benchmark reports
+ * next to the nominal peak.
+ *   iters  loop count per wave (1 .. 2^24)
+ *   sink   device fp32 [512 * 256]: one value per thread, written so that
+ *          nothing is optimised away (its contents mean nothing)
+ *   flops  host output: the dense-equivalent flops one launch performs
+ * NM_ERR_UNSUPPORTED for another kind, NM_ERR_SHAPE for iters out of range.
+ */
+nm_status nm_mfma_rate_probe(int kind, int64_t iters, float* sink, int64_t* flops, nm_stream stream);
+
+/*
  * The panel layout of a bf16 2:4 form (R rows, K dense columns, R % 4 == 0,
  * K % 256 == 0): the same values and nibbles as the row-major form
  * (values [R][K/2], meta [R][K/8]), in another order, with the same total sizes:

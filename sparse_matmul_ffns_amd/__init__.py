@@ -10,6 +10,7 @@ from .nmsparse import (  # noqa: F401
     NM_ERR_TOO_LARGE,
     NmError,
     lib,
+    mfma_rate_probe,
     nm_compress,
     nm_decompress,
     nm_prune,

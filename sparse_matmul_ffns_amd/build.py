@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "nmsparse")
 LIB = os.path.join(PKG, "libnmsparse.so")
 
-SOURCES = ["api.cpp", "prune.hip", "venom.hip", "reprune.hip", "spmm.hip", "spmm_dma.hip", "spmm_vnm.hip", "spmm_nt.hip", "spmm_w4.hip", "sddmm.hip", "prep.hip", "lowrank.hip", "general.hip", "venom_bwd.hip"]
+SOURCES = ["api.cpp", "prune.hip", "venom.hip", "reprune.hip", "spmm.hip", "spmm_dma.hip", "spmm_vnm.hip", "spmm_nt.hip", "spmm_w4.hip", "sddmm.hip", "prep.hip", "lowrank.hip", "general.hip", "venom_bwd.hip", "probe.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

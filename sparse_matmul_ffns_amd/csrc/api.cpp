@@ -267,6 +267,15 @@ nm_status nm_reprune_t_transpose(nm_dtype dt, const void* values, const uint8_t*
                                                        ldxt, hs(stream)));
 }
 
+nm_status nm_mfma_rate_probe(int kind, int64_t iters, float* sink, int64_t* flops, nm_stream stream) {
+  if (!sink || !flops) return NM_ERR_NULL;
+  if (kind != 0 && kind != 1) return NM_ERR_UNSUPPORTED;
+  if (iters <= 0 || iters > (int64_t(1) << 24)) return NM_ERR_SHAPE;
+  if (!aligned(sink, 4)) return NM_ERR_ALIGN;
+  *flops = nms::mfma_probe_flops(kind, iters);
+  return hip_status(nms::launch_mfma_rate_probe(kind, iters, sink, hs(stream)));
+}
+
 nm_status nm_to_panels(nm_dtype dt, const void* values, const uint8_t* meta, int64_t R, int64_t K, void* values_p,
                        uint8_t* meta_p, nm_stream stream) {
   if (!values || !meta || !values_p || !meta_p) return NM_ERR_NULL;

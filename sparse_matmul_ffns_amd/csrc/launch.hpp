@@ -92,6 +92,8 @@ hipError_t launch_nm_reprune_t_transpose_panels(const void* values, const uint8_
                                                 int64_t RX, int64_t CX, void* Xt, int64_t ldxt, hipStream_t s);
 hipError_t launch_nm_to_panels(const void* values, const uint8_t* meta, int64_t R, int64_t K, void* values_p,
                                uint8_t* meta_p, hipStream_t s);
+int64_t mfma_probe_flops(int kind, int64_t iters);
+hipError_t launch_mfma_rate_probe(int kind, int64_t iters, float* sink, hipStream_t s);
 hipError_t launch_sddmm_nm_dt(int dt, const void* D, int64_t ldd, const void* X, int64_t ldx, int64_t R, int64_t Kc,
                               int64_t Tn, const uint8_t* meta, float* out, void* Dt, int64_t lddt, hipStream_t s);
 bool sddmm_venom_fast_ok(const void* dY, int64_t lddy, const void* Wd, int64_t ldw, int64_t Tn, int64_t F, int64_t Nc,

@@ -38,6 +38,7 @@ _SIGNATURES = {
     "spmm_nm": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "nm_to_panels": [_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp],
+    "nm_mfma_rate_probe": [_int, _i64, _vp, ctypes.POINTER(_i64), _vp],
     "nm_reprune_t_transpose_panels": [_int, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t_panels": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
     "spmm_nm_t_out_bf16": [_int, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp],
@@ -532,6 +533,19 @@ def nm_reprune_t_transpose(values: torch.Tensor, meta: torch.Tensor, R: int, K: 
                                         _rows(X, "X"), RX, CX, _p(Xt), _rows(Xt, "Xt"), _stream()),
            "nm_reprune_t_transpose")
     return values_t, meta_t, Xt
+
+
+def mfma_rate_probe(kind: int, iters: int, sink: torch.Tensor) -> int:
+    """Launch the matrix-rate probe (kind 0 dense bf16 MFMA, 1 2:4 SMFMAC) on the current stream;
+    returns the dense-equivalent flops of the launch.  `sink` is an fp32 CUDA tensor of at least
+    512 * 256 elements."""
+    _dev(sink)
+    if sink.dtype != torch.float32 or sink.numel() < 512 * 256:
+        raise ValueError("sink must be an fp32 tensor of at least 131072 elements")
+    flops = _i64(0)
+    _check(lib().nm_mfma_rate_probe(int(kind), int(iters), _p(sink), ctypes.byref(flops), _stream()),
+           "nm_mfma_rate_probe")
+    return flops.value
 
 
 def nm_to_panels(values: torch.Tensor, meta: torch.Tensor, R: int, K: int, values_p=None, meta_p=None):

@@ -208,3 +208,13 @@ def test_gmp_schedule_hand_worked(L, params, table):
     assert L.nm_gmp_n_at(8, 8, 0, 4, 1, -1, 0, None) == -1          # n_final must be < M
     assert L.nm_gmp_n_at(8, 2, 5, 4, 1, -1, 0, None) == -1          # t_end < t_begin
     assert L.nm_gmp_n_at(6, 2, 0, 4, 1, -1, 0, None) == -1          # M
+
+
+def test_mfma_rate_probe_errors(L):
+    flops = ctypes.c_int64(0)
+    assert L.nm_mfma_rate_probe(0, 16, None, ctypes.byref(flops), None) == nm.NM_ERR_NULL
+    assert L.nm_mfma_rate_probe(0, 16, FAKE, None, None) == nm.NM_ERR_NULL
+    assert L.nm_mfma_rate_probe(2, 16, FAKE, ctypes.byref(flops), None) == nm.NM_ERR_UNSUPPORTED
+    assert L.nm_mfma_rate_probe(1, 0, FAKE, ctypes.byref(flops), None) == nm.NM_ERR_SHAPE
+    assert L.nm_mfma_rate_probe(1, 1 << 25, FAKE, ctypes.byref(flops), None) == nm.NM_ERR_SHAPE
+    assert L.nm_mfma_rate_probe(0, 16, FAKE + 2, ctypes.byref(flops), None) == nm.NM_ERR_ALIGN
