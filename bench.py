@@ -19,9 +19,12 @@ A step is one pass of the hot path over the workload's synthetic inputs
       spmm_venom;
   nm24_fp32_256x512x128: the small fp32 case.
 `value` is dense-equivalent TFLOP/s of the whole step (2 R K Nc per product,
-pruned zeros counted as if dense).  The JSON line also carries the roofline
-of the step's dominant kernel, timed with HIP events on the stream it runs on,
-and the fp64 CPU oracle timed on the host (rank 0, N = 1 only).
+pruned zeros counted as if dense).  `products` gives the same flops over the
+event-timed durations of the step's matrix products alone (without the prune,
+compress and transpose launches), beside `value`, never in its place.  The JSON
+line also carries the roofline of the step's dominant kernel, timed with HIP
+events on the stream it runs on, and the fp64 CPU oracle timed on the host
+(rank 0, N = 1 only).
 
 Without --workload the headline is the 2:4 up-projection, and `configs` adds
 the same measurement (step time, dense-equivalent TFLOP/s, share of the bf16
@@ -627,6 +630,10 @@ def measure(workload, steps_n, warmup_n, with_cpu):
     ms_per_step = elapsed * 1e3 / steps_n
     total_flops = sum(flops.values())
     value = total_flops / (ms_per_step * 1e-3) / 1e12
+    # the step's matrix products alone (their event-timed durations, without the prune, compress
+    # and transpose launches around them): beside `value`, never in its place
+    prod_ms = sum(per_kernel_ms[n] for n in flops)
+    prod_tflops = total_flops / (prod_ms * 1e-3) / 1e12
 
     from sparse_matmul_ffns_amd import synth
     w = synth.WORKLOADS[workload]
@@ -647,6 +654,9 @@ def measure(workload, steps_n, warmup_n, with_cpu):
         "kernels": names,
         "pct_of_bf16_peak_dense_equivalent": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "per_kernel_us": {n: round(v * 1e3, 2) for n, v in per_kernel_ms.items()},
+        "products": {"kernels": list(flops), "us": round(prod_ms * 1e3, 2),
+                     "dense_equiv_tflops": round(prod_tflops, 2),
+                     "pct_of_bf16_peak": round(100 * prod_tflops / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": recorded_counter(workload, dominant, "hbm_bytes_per_launch"),
@@ -695,6 +705,7 @@ def main():
         "config": {"workload": workload, "kernels": head["kernels"],
                    "pct_of_bf16_peak_dense_equivalent": head["pct_of_bf16_peak_dense_equivalent"]},
         "per_kernel_us": head["per_kernel_us"],
+        "products": head["products"],
         "roofline": head["roofline"],
         "cold": head["cold"],
     }
