@@ -49,7 +49,9 @@
  *     GPU (see there).
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Every call
  *     is asynchronous on that stream; argument errors are returned before
- *     anything is launched.
+ *     anything is launched.  No call allocates, clears memory with a memset or
+ *     synchronises, so a sequence of calls on one stream can be captured into a
+ *     HIP graph and replayed.
  *   - Floating point: products accumulate in fp32 and are written as fp32,
  *     except where a call states a bf16 result (rounded to nearest even).
  *   - Errors: NM_ERR_NULL for a NULL required pointer, NM_ERR_SHAPE for
