@@ -67,6 +67,55 @@ def small_ints(shape, seed: int, lo: int = -8, hi: int = 8, dtype: str = "bf16")
     return f32_to_bf16_bits(x) if dtype == "bf16" else x
 
 
+# Counter-based integers for operands too large to draw on the host: entry (i, j) depends on i, j and
+# the seed only, so a device fills the whole matrix and the host regenerates any rows or columns it
+# samples.  h = (i * 0x9E3779B1 + j * 0x85EBCA77 + seed * 0xC2B2AE3D) mod 2^32, then the
+# lowbias32 finalizer (h ^= h >> 16; h *= 0x7FEB352D; h ^= h >> 15; h *= 0x846CA68B; h ^= h >> 16,
+# all mod 2^32), and the entry is h mod (2 span + 1) - span.
+_HASH_I, _HASH_J, _HASH_S = 0x9E3779B1, 0x85EBCA77, 0xC2B2AE3D
+_MASK32 = 0xFFFFFFFF
+
+
+def hashed_ints(rows, cols, seed: int, span: int = 3) -> np.ndarray:
+    """Entries (i, j) for i in `rows`, j in `cols` (1-D index arrays): integers in [-span, span] as
+    bf16 bit patterns, shape [len(rows), len(cols)]."""
+    i = np.asarray(rows, dtype=np.uint64).reshape(-1, 1)
+    j = np.asarray(cols, dtype=np.uint64).reshape(1, -1)
+    m = np.uint64(_MASK32)
+    h = (i * np.uint64(_HASH_I) + j * np.uint64(_HASH_J) + np.uint64((seed * _HASH_S) & _MASK32)) & m
+    h ^= h >> np.uint64(16)
+    h = (h * np.uint64(0x7FEB352D)) & m
+    h ^= h >> np.uint64(15)
+    h = (h * np.uint64(0x846CA68B)) & m
+    h ^= h >> np.uint64(16)
+    v = (h % np.uint64(2 * span + 1)).astype(np.int64) - span
+    return f32_to_bf16_bits(v.astype(np.float32))
+
+
+def hashed_ints_torch(rows, cols, seed: int, span: int = 3, block: int = 1 << 24):
+    """hashed_ints on the device of `rows` (1-D int64 torch tensors): a torch.bfloat16 matrix
+    [len(rows), len(cols)], built in pieces of about `block` entries.  The arithmetic is int64 with
+    the low 32 bits kept after every step (a product that wraps past 2^63 keeps its low bits), so
+    the values equal the numpy form's."""
+    import torch
+    nr, nc = rows.numel(), cols.numel()
+    out = torch.empty((nr, nc), dtype=torch.bfloat16, device=rows.device)
+    cb = min(nc, block)
+    rb = max(1, block // cb)
+    for r0 in range(0, nr, rb):
+        i = rows[r0:r0 + rb].to(torch.int64).reshape(-1, 1)
+        for c0 in range(0, nc, cb):
+            j = cols[c0:c0 + cb].to(torch.int64).reshape(1, -1)
+            h = (i * _HASH_I + j * _HASH_J + ((seed * _HASH_S) & _MASK32)) & _MASK32
+            h ^= h >> 16
+            h = (h * 0x7FEB352D) & _MASK32
+            h ^= h >> 15
+            h = (h * 0x846CA68B) & _MASK32
+            h ^= h >> 16
+            out[r0:r0 + rb, c0:c0 + cb] = (torch.remainder(h, 2 * span + 1) - span).to(torch.bfloat16)
+    return out
+
+
 def tie_rich(shape, seed: int, dtype: str = "bf16") -> np.ndarray:
     """Values from {-2, -1, -0.0, +0.0, 1, 2, 3}: many equal magnitudes and signed zeros."""
     rng = np.random.Generator(np.random.PCG64(seed))
